@@ -1,0 +1,262 @@
+/*
+ * CPU oracle for the MoE layer forward pass.  TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  The HIP library never links, includes or calls it, and
+ * this file includes nothing from the HIP library: the two share no code.
+ *
+ * It is written to be read against the pages it follows, not to be fast:
+ * plain per-token loops, fp32 storage, fp64 accumulation, no blocking, no
+ * fusion, no reordering beyond what each definition states.
+ *
+ * Pages cited (titles translated; original titles are given in the design
+ * notes):
+ *   [P1] "Optimising MoE with Triton: topk_gating operator fusion in practice"
+ *   [P2] "SpMM in MoE: accelerating sparse experts with Triton kernels"
+ *   [P4] "MoE architecture optimisation and SonicMoE practice"
+ *   [P5] "Triton GPU kernel programming in practice"
+ *
+ * Pins (checked by the CPU tests, against things other than this file):
+ *   softmax      - rows sum to 1; E=2 logistic closed form; equal row = 1/E
+ *   top-K        - an independent full sort on tiny inputs, constructed ties
+ *   weights      - sum to 1; K=1 gives 1; E=K=2 closed form; ratio property
+ *   counts       - brute recount; sum = T*K; offsets = library cumulative sum
+ *   permutation  - round trip, segment purity, ascending tokens in segments
+ *   gather       - library fancy indexing
+ *   expert FFN / combine / layer - E=1,K=1 equals a dense SwiGLU MLP built
+ *                  from library matmuls; identical experts reduce to that MLP
+ *                  for any routing; zero row; exact scaling by 2
+ * Every function here is pinned; none is "parity unpinned".
+ *
+ * Errors: every entry point returns 0 on success and a negative value on a
+ * bad argument (null pointer, out-of-range size, non-finite logit).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* Widen one stored element to double.  bf16 is the upper half of an IEEE
+ * binary32, so widening is exact: shift the 16 stored bits up by 16. */
+static double load_elem(const void* base, int dtype, size_t i) {
+    if (dtype == ORACLE_BF16) {
+        uint32_t bits = ((uint32_t)((const uint16_t*)base)[i]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float*)base)[i];
+}
+
+/* [P1] §1 and [P5] §4: softmax over the E expert scores of one token, with the
+ * maximum subtracted first for numerical stability ([P1] §4.1).  fp64. */
+int oracle_softmax(const float* logits, int T, int E, double* probs) {
+    if (!logits || !probs || T < 0 || E < 1) return -1;
+    for (int t = 0; t < T; ++t) {
+        const float* l = logits + (size_t)t * E;
+        double m = -INFINITY;
+        for (int e = 0; e < E; ++e) {
+            if (!isfinite(l[e])) return -2;
+            if ((double)l[e] > m) m = (double)l[e];
+        }
+        double s = 0.0;
+        for (int e = 0; e < E; ++e) s += exp((double)l[e] - m);
+        for (int e = 0; e < E; ++e) probs[(size_t)t * E + e] = exp((double)l[e] - m) / s;
+    }
+    return 0;
+}
+
+/* [P1] §1 (softmax then top-k over the expert axis), [P4] §1 (each token keeps
+ * the K experts with the highest scores).  Selection is on the logits, which
+ * orders experts exactly as their softmax probabilities do.  Slot 0 holds the
+ * best expert; equal logits go to the lower expert index (float equality, so
+ * -0.0 and +0.0 are equal).  Weights: the softmax probabilities of the chosen
+ * experts, renormalised to sum to 1 over the K slots (fp64, rounded once).
+ * Counts: [P4] §3.1, one count per (token, slot) added to its expert.
+ * Offsets: exclusive prefix sum of the counts, with offsets[E] = T*K. */
+int oracle_route(const float* logits, int T, int E, int K, int32_t* idx, float* w,
+                 int32_t* counts, int32_t* offsets) {
+    if (!logits || !idx || !w || !counts || !offsets) return -1;
+    if (T < 0 || E < 1 || K < 1 || K > E) return -1;
+    double* p = (double*)malloc(sizeof(double) * (size_t)E);
+    char* taken = (char*)malloc((size_t)E);
+    if (!p || !taken) { free(p); free(taken); return -3; }
+    int rc = 0;
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int t = 0; t < T && rc == 0; ++t) {
+        const float* l = logits + (size_t)t * E;
+        rc = oracle_softmax(l, 1, E, p);
+        if (rc) break;
+        memset(taken, 0, (size_t)E);
+        for (int k = 0; k < K; ++k) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || l[e] > l[best]) best = e; /* strict: ties keep the lower e */
+            }
+            taken[best] = 1;
+            idx[(size_t)t * K + k] = best;
+        }
+        double s = 0.0;
+        for (int k = 0; k < K; ++k) s += p[idx[(size_t)t * K + k]];
+        for (int k = 0; k < K; ++k) w[(size_t)t * K + k] = (float)(p[idx[(size_t)t * K + k]] / s);
+        for (int k = 0; k < K; ++k) counts[idx[(size_t)t * K + k]] += 1;
+    }
+    free(p);
+    free(taken);
+    if (rc) return rc;
+    int32_t run = 0;
+    for (int e = 0; e < E; ++e) { offsets[e] = run; run += counts[e]; }
+    offsets[E] = run;
+    return 0;
+}
+
+/* [P2] §6 (each token row is duplicated once per selected expert) and [P4]
+ * §2.2 (intermediates stored grouped by expert).  The expert-contiguous order
+ * is a stable counting sort of the row-major (token, slot) list: walk experts
+ * in ascending order, and inside an expert walk tokens in ascending order.
+ * sorted_pair[p] = t*K + k, inv[t*K + k] = p. */
+int oracle_permute(const int32_t* idx, int T, int E, int K, int32_t* sorted_pair, int32_t* inv) {
+    if (!idx || !sorted_pair || !inv || T < 0 || E < 1 || K < 1) return -1;
+    for (size_t q = 0; q < (size_t)T * K; ++q)
+        if (idx[q] < 0 || idx[q] >= E) return -1;
+    int32_t p = 0;
+    for (int e = 0; e < E; ++e)
+        for (int t = 0; t < T; ++t)
+            for (int k = 0; k < K; ++k)
+                if (idx[(size_t)t * K + k] == e) {
+                    sorted_pair[p] = t * K + k;
+                    inv[(size_t)t * K + k] = p;
+                    ++p;
+                }
+    return 0;
+}
+
+/* Gather step of [P4] §1: row p of the expert-ordered input is the token row
+ * that (token, slot) pair sorted_pair[p] came from.  A pure byte copy. */
+int oracle_gather_rows(const void* X, int elem_bytes, int T, int d, int K,
+                       const int32_t* sorted_pair, void* Xp) {
+    if (!X || !sorted_pair || !Xp || elem_bytes < 1 || T < 0 || d < 0 || K < 1) return -1;
+    size_t row = (size_t)d * elem_bytes;
+    for (size_t p = 0; p < (size_t)T * K; ++p) {
+        int32_t q = sorted_pair[p];
+        if (q < 0 || q >= T * K) return -1;
+        memcpy((char*)Xp + p * row, (const char*)X + (size_t)(q / K) * row, row);
+    }
+    return 0;
+}
+
+/* One expert's two-layer MLP with SwiGLU on one input row ([P4] §1: the first
+ * layer's output passes through SiLU, H = SiLU(W1 X); [P4] §2.2: the SwiGLU
+ * activation is applied to that product, gated by the W3 branch).
+ *   h1[j] = sum_i x[i] W1[i,j],  h3[j] = sum_i x[i] W3[i,j]          (fp64)
+ *   a[j]  = SiLU(h1[j]) * h3[j],  SiLU(z) = z / (1 + exp(-z))     (stored fp32)
+ *   y[c]  = sum_j a[j] W2[j,c]                            (fp64, stored fp32)
+ * W1, W3 are [d, n] and W2 is [n, d] for this expert, row-major. */
+static void expert_row(const void* x, size_t xoff, int dtype, const void* W1, const void* W3,
+                       const void* W2, size_t woff13, size_t woff2, int d, int n, double* h1,
+                       double* h3, float* a, float* y) {
+    for (int j = 0; j < n; ++j) { h1[j] = 0.0; h3[j] = 0.0; }
+    for (int i = 0; i < d; ++i) {
+        double xi = load_elem(x, dtype, xoff + (size_t)i);
+        for (int j = 0; j < n; ++j) {
+            h1[j] += xi * load_elem(W1, dtype, woff13 + (size_t)i * n + j);
+            h3[j] += xi * load_elem(W3, dtype, woff13 + (size_t)i * n + j);
+        }
+    }
+    for (int j = 0; j < n; ++j) a[j] = (float)(h1[j] / (1.0 + exp(-h1[j])) * h3[j]);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+    for (int c = 0; c < d; ++c) acc[c] = 0.0;
+    for (int j = 0; j < n; ++j) {
+        double aj = (double)a[j];
+        for (int c = 0; c < d; ++c) acc[c] += aj * load_elem(W2, dtype, woff2 + (size_t)j * d + c);
+    }
+    for (int c = 0; c < d; ++c) y[c] = (float)acc[c];
+    free(acc);
+}
+
+/* Grouped expert MLP over expert-ordered rows ([P4] §1 GEMM step).  Row r of
+ * Xp belongs to expert row_expert[r]; only the rows listed in `rows` (or all
+ * `nrows` rows when rows == NULL) are computed.  act is [nsel, n], y is
+ * [nsel, d], in the order of `rows`. */
+int oracle_expert_ffn(const void* Xp, int dtype, int nrows, const int32_t* row_expert,
+                      const int32_t* rows, int nsel, const void* W1, const void* W3,
+                      const void* W2, int E, int d, int n, float* act, float* y) {
+    if (!Xp || !row_expert || !W1 || !W3 || !W2 || !act || !y) return -1;
+    if (nrows < 0 || nsel < 0 || E < 1 || d < 1 || n < 1) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int s = 0; s < nsel; ++s) {
+        int r = rows ? rows[s] : s;
+        if (r < 0 || r >= nrows || row_expert[r] < 0 || row_expert[r] >= E) { bad |= 1; continue; }
+        int e = row_expert[r];
+        double* h1 = (double*)malloc(sizeof(double) * (size_t)n);
+        double* h3 = (double*)malloc(sizeof(double) * (size_t)n);
+        expert_row(Xp, (size_t)r * d, dtype, W1, W3, W2, (size_t)e * d * n, (size_t)e * n * d, d, n,
+                   h1, h3, act + (size_t)s * n, y + (size_t)s * d);
+        free(h1);
+        free(h3);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Scatter / aggregation step ([P4] §1; [P2] §1 and §6: the outputs of the
+ * selected experts are combined as a gate-weighted average).  With the
+ * renormalised weights summing to 1 this is a weighted sum:
+ *   out[t,c] = sum_k w[t,k] * Y[inv[t*K+k], c],  summed over k in order in fp64. */
+int oracle_combine(const float* Y, const float* w, const int32_t* inv, int T, int d, int K,
+                   float* out) {
+    if (!Y || !w || !inv || !out || T < 0 || d < 0 || K < 1) return -1;
+    for (int t = 0; t < T; ++t)
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k)
+                acc += (double)w[(size_t)t * K + k] * (double)Y[(size_t)inv[(size_t)t * K + k] * d + c];
+            out[(size_t)t * d + c] = (float)acc;
+        }
+    return 0;
+}
+
+/* The whole layer for a subset of tokens, as a per-token loop over the
+ * selected experts: route the token, run each selected expert's MLP on the
+ * token row, accumulate the gate-weighted outputs ([P4] §1 Router -> Experts
+ * -> Aggregator).  It does not use the permutation at all.  tokens == NULL
+ * means all T tokens; out is [ntok, d] in the order of `tokens`. */
+int oracle_layer(const void* X, int dtype, const float* logits, const void* W1, const void* W3,
+                 const void* W2, int T, int d, int E, int K, int n, const int32_t* tokens,
+                 int ntok, float* out) {
+    if (!X || !logits || !W1 || !W3 || !W2 || !out) return -1;
+    if (T < 0 || d < 1 || E < 1 || K < 1 || K > E || n < 1 || ntok < 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int s = 0; s < ntok; ++s) {
+        int t = tokens ? tokens[s] : s;
+        if (t < 0 || t >= T) { bad |= 1; continue; }
+        int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
+        float* w = (float*)malloc(sizeof(float) * (size_t)K);
+        int32_t* cnt = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+        int32_t* off = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+        double* h1 = (double*)malloc(sizeof(double) * (size_t)n);
+        double* h3 = (double*)malloc(sizeof(double) * (size_t)n);
+        float* a = (float*)malloc(sizeof(float) * (size_t)n);
+        float* y = (float*)malloc(sizeof(float) * (size_t)d);
+        double* acc = (double*)calloc((size_t)d, sizeof(double));
+        if (oracle_route(logits + (size_t)t * E, 1, E, K, idx, w, cnt, off) != 0) bad |= 1;
+        else
+            for (int k = 0; k < K; ++k) {
+                int e = idx[k];
+                expert_row(X, (size_t)t * d, dtype, W1, W3, W2, (size_t)e * d * n,
+                           (size_t)e * n * d, d, n, h1, h3, a, y);
+                for (int c = 0; c < d; ++c) acc[c] += (double)w[k] * (double)y[c];
+            }
+        for (int c = 0; c < d; ++c) out[(size_t)s * d + c] = (float)acc[c];
+        free(idx); free(w); free(cnt); free(off); free(h1); free(h3); free(a); free(y); free(acc);
+    }
+    return bad ? -1 : 0;
+}
