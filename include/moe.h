@@ -1,0 +1,170 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer forward library, libmoe.so.
+ *
+ * The layer follows the problem statement of [P4] section 1: tokens
+ * X in R^{T x d}, E expert scores per token, the K best experts kept per
+ * token, and each expert a two-layer MLP whose first layer goes through SiLU
+ * (SwiGLU: W1 and W3 are [d, n], W2 is [n, d]).  The forward pass is
+ * gate -> histogram/offsets -> permute (gather) -> grouped expert MLP ->
+ * combine (scatter), as in [P4] section 1 and [P2] section 6.
+ *
+ * Pages cited (titles translated):
+ *   [P1] "Optimising MoE with Triton: topk_gating operator fusion in practice"
+ *   [P2] "SpMM in MoE: accelerating sparse experts with Triton kernels"
+ *   [P3] "Triton optimisation speeds up matrix computation for Mixture-of-Experts models"
+ *   [P4] "MoE architecture optimisation and SonicMoE practice"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless stated; the caller owns every buffer.
+ *    The library never allocates or frees memory and keeps no state between
+ *    calls except a per-device cache of the compute-unit count.
+ *  - Tensors are dense and row-major.  Expert weights are stacked expert-major:
+ *    W1[e] starts at element e*d*n.  No biases.
+ *  - `dtype` (moe_dtype) is the storage type of X, W1, W3, W2, Xp, Act, Y and
+ *    out.  Router logits and gate weights are always fp32; indices int32.
+ *    Arithmetic: fp32 accumulation; bf16 results are rounded to nearest-even.
+ *  - Every device pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it: no host<->device synchronisation, no copies.
+ *  - Errors: a call returns a moe_status.  Arguments are validated before any
+ *    launch; on a validation error nothing is launched and no output is
+ *    touched.  MOE_ERR_HIP reports a failed launch.  Faults inside a kernel
+ *    surface at the caller's next synchronisation.  moe_last_error() gives a
+ *    human-readable reason for the last failure on the calling thread.
+ *  - Router logits must be finite; non-finite logits give unspecified routing.
+ *  - Supported sizes: 1 <= E <= 256, 1 <= K <= min(E, 8), T >= 1,
+ *    T*K < 2^31; for the layer calls d and n are multiples of 128 (bf16) or
+ *    of 64 (fp32), and T*K*max(d,n) < 2^40.  Outside these: MOE_ERR_UNSUPPORTED
+ *    (or MOE_ERR_INVALID_ARG for values that are meaningless, such as K > E).
+ *  - Calls that write the same buffers race if they overlap on different
+ *    streams; calls on one stream are ordered.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,  /* null pointer, misalignment, meaningless size */
+    MOE_ERR_UNSUPPORTED = 2,  /* valid but outside the supported sizes above */
+    MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+    MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Static string naming a status code ("ok", "invalid argument", ...). */
+const char* moe_status_string(int status);
+
+/* Reason for the most recent non-OK status returned on this thread. */
+const char* moe_last_error(void);
+
+/* Workspace sizes in bytes (device memory, 256-byte aligned start) for the
+ * calls that need one.  Return 0 for invalid sizes. */
+size_t moe_route_workspace_bytes(int T, int E, int K);
+size_t moe_permute_workspace_bytes(int T, int E, int K);
+size_t moe_forward_workspace_bytes(int T, int d, int E, int K, int n, int dtype);
+
+/*
+ * moe_route -- steps 1 and 2: fused softmax top-K gate, per-expert histogram
+ * and exclusive prefix offsets.
+ *   [P1] section 1: softmax over the expert axis, then top-k, then a per-expert
+ *   accumulation, fused into one pass ([P1] section 2.1); [P4] section 1: the
+ *   K best of E scores per token; [P4] section 3.1: per-expert token counts.
+ * Semantics (per token t):
+ *   topk_idx[t,0..K-1]: the K experts with the largest logits, best first;
+ *     equal logits go to the lower expert index (-0.0 equals +0.0).
+ *   topk_w[t,k] = softmax(logits[t])[idx] renormalised over the K slots,
+ *     i.e. exp(l_k - l_0) / sum_j exp(l_j - l_0).
+ *   counts[e] = number of (t,k) with topk_idx[t,k] == e.
+ *   offsets[e] = sum_{e' < e} counts[e'], offsets[E] = T*K  (E+1 entries).
+ * In:  logits [T,E] fp32.
+ * Out: topk_idx [T,K] int32, topk_w [T,K] fp32, counts [E] int32,
+ *      offsets [E+1] int32.
+ * Workspace: moe_route_workspace_bytes(T,E,K) bytes (per-chunk counts).
+ * Deterministic: integer histogram, no floating-point atomics.
+ */
+int moe_route(const float* logits, int T, int E, int K, int32_t* topk_idx, float* topk_w,
+              int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_permute -- step 3: token rows into expert-contiguous order.
+ *   [P2] section 6: each token row is repeated once per selected expert;
+ *   [P4] section 1 (gather) and section 2.2 (intermediates grouped by expert).
+ * Order: a stable counting sort of the row-major (t,k) list by expert: rows of
+ * expert e occupy [offsets[e], offsets[e+1]) in ascending token order, where
+ * offsets is the exclusive scan of the expert histogram of topk_idx (exactly
+ * what moe_route returns).  The placement is derived from topk_idx itself, so
+ * no offsets argument is taken and no stale offsets can misplace a row.
+ * In:  X [T,d] (dtype; d*sizeof(dtype) a multiple of 16 bytes),
+ *      topk_idx [T,K] int32 with entries in [0,E) and the K entries of a
+ *      token distinct (as moe_route produces).  Entries outside [0,E) are
+ *      skipped: their rows are not placed and their inv entries not written.
+ * Out: sorted_pair [T*K] int32 (= t*K + k at each expert-ordered position p),
+ *      inv [T*K] int32 (inv[t*K+k] = p), Xp [T*K, d] (dtype), Xp[p] = X[t].
+ * Workspace: moe_permute_workspace_bytes(T,E,K) bytes.
+ */
+int moe_permute(const void* X, int dtype, int T, int d, int E, int K, const int32_t* topk_idx,
+                int32_t* sorted_pair, int32_t* inv, void* Xp, void* ws, size_t ws_bytes,
+                void* stream);
+
+/*
+ * moe_grouped_ffn -- step 4: grouped GEMM over all experts in one launch per
+ * layer ([P3] technical innovations: many independent GEMMs in one kernel;
+ * persistent design: as many workgroups as the GPU holds, pulling tiles),
+ * with the SwiGLU activation fused into the first GEMM's epilogue ([P4]
+ * section 2.2).
+ *   For expert e, rows r in [offsets[e], offsets[e] + counts[e]) of Xp:
+ *     Act[r] = SiLU(Xp[r] W1[e]) * (Xp[r] W3[e]),  SiLU(z) = z / (1 + e^-z)
+ *     Y[r]   = Act[r] W2[e]
+ *   fp32 accumulation; Act and Y stored in dtype.
+ * In:  Xp [T*K,d], W1 [E,d,n], W3 [E,d,n], W2 [E,n,d], counts [E],
+ *      offsets [E+1].
+ * Out: Act [T*K,n], Y [T*K,d].  No workspace: the ragged tile schedule is
+ *      derived from counts on the device.
+ */
+int moe_grouped_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
+                    int T, int d, int E, int K, int n, const int32_t* counts,
+                    const int32_t* offsets, void* Act, void* Y, void* stream);
+
+/*
+ * moe_combine -- step 5: gate-weighted combine back to token order ([P4]
+ * section 1 scatter; [P2] sections 1 and 6: the selected experts' outputs are
+ * averaged with the gate weights).  A gather-sum by token, no atomics:
+ *   out[t] = sum_{k=0}^{K-1} topk_w[t,k] * Y[inv[t*K+k]]
+ * summed in k order in fp32 and rounded once to dtype.
+ * In:  Y [T*K,d] (dtype), topk_w [T,K] fp32, inv [T*K] int32.
+ * Out: out [T,d] (dtype).
+ */
+int moe_combine(const void* Y, const float* topk_w, const int32_t* inv, int dtype, int T, int d,
+                int K, void* out, void* stream);
+
+/*
+ * moe_forward -- the whole layer: moe_route, moe_permute, moe_grouped_ffn and
+ * moe_combine on one stream, with the permutation's per-chunk counts reused
+ * from the gate.  Results equal those of the four calls made in sequence.
+ * In:  X [T,d], logits [T,E], W1, W3 [E,d,n], W2 [E,n,d].
+ * Out: out [T,d].
+ * Optional outputs (may be NULL, then they live in the workspace):
+ *      topk_idx [T,K], topk_w [T,K], counts [E], offsets [E+1],
+ *      sorted_pair [T*K], inv [T*K].
+ * Workspace: moe_forward_workspace_bytes(T,d,E,K,n,dtype) bytes; it also holds
+ *      Xp [T*K,d], Act [T*K,n] and Y [T*K,d].
+ */
+int moe_forward(const void* X, const float* logits, const void* W1, const void* W3,
+                const void* W2, int dtype, int T, int d, int E, int K, int n, void* out,
+                int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                int32_t* sorted_pair, int32_t* inv, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,205 @@
+"""Python binding of libmoe, the gfx950 MoE layer forward library.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libmoe.so`` (built in-tree by ``_build.build()``).  PyTorch provides device
+memory and the current stream.  There is no CPU fallback: if the library is
+missing, or a tensor is not on the GPU, the call raises.
+
+The functions carry the names of the C entry points declared in
+``include/moe.h``; each allocates its outputs and workspace with torch and
+enqueues the library call on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe.h")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+
+_lib = None
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        super().__init__(f"{func}: status {status}: {detail}")
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmoe.so and declare its C signatures (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "moe_status_string": ([I], ctypes.c_char_p),
+        "moe_last_error": ([], ctypes.c_char_p),
+        "moe_route_workspace_bytes": ([I, I, I], Z),
+        "moe_permute_workspace_bytes": ([I, I, I], Z),
+        "moe_forward_workspace_bytes": ([I, I, I, I, I, I], Z),
+        "moe_route": ([P, I, I, I, P, P, P, P, P, Z, P], I),
+        "moe_permute": ([P, I, I, I, I, I, P, P, P, P, P, Z, P], I),
+        "moe_grouped_ffn": ([P, P, P, P, I, I, I, I, I, I, P, P, P, P, P], I),
+        "moe_combine": ([P, P, P, I, I, I, I, P, P], I),
+        "moe_forward": ([P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P], I),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/moe.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def _check(status: int, func: str):
+    if status != MOE_OK:
+        lib = load_library()
+        raise MoEError(status, func, lib.moe_last_error().decode())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return MOE_F32
+    if dt == torch.bfloat16:
+        return MOE_BF16
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def moe_route(logits: torch.Tensor, K: int):
+    """Steps 1-2.  logits [T,E] fp32 -> (topk_idx [T,K] i32, topk_w [T,K] f32, counts [E] i32, offsets [E+1] i32)."""
+    lib = load_library()
+    T, E = logits.shape
+    dev = logits.device
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    nws = lib.moe_route_workspace_bytes(T, E, K)
+    ws = _workspace(nws, dev)
+    _check(lib.moe_route(_dev(logits, "logits", torch.float32), T, E, K, idx.data_ptr(), w.data_ptr(),
+                         counts.data_ptr(), offsets.data_ptr(), ws.data_ptr(), nws, _stream(dev)), "moe_route")
+    return idx, w, counts, offsets
+
+
+def moe_permute(X: torch.Tensor, topk_idx: torch.Tensor, E: int):
+    """Step 3.  X [T,d], topk_idx [T,K] -> (sorted_pair [T*K] i32, inv [T*K] i32, Xp [T*K,d])."""
+    lib = load_library()
+    T, d = X.shape
+    K = topk_idx.shape[1]
+    dev = X.device
+    sp = torch.empty(T * K, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * K, dtype=torch.int32, device=dev)
+    Xp = torch.empty((T * K, d), dtype=X.dtype, device=dev)
+    nws = lib.moe_permute_workspace_bytes(T, E, K)
+    ws = _workspace(nws, dev)
+    _check(lib.moe_permute(_dev(X, "X"), dtype_code(X.dtype), T, d, E, K, _dev(topk_idx, "topk_idx", torch.int32),
+                           sp.data_ptr(), inv.data_ptr(), Xp.data_ptr(), ws.data_ptr(), nws, _stream(dev)),
+           "moe_permute")
+    return sp, inv, Xp
+
+
+def moe_grouped_ffn(Xp: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, W2: torch.Tensor,
+                    counts: torch.Tensor, offsets: torch.Tensor, K: int):
+    """Step 4.  Xp [T*K,d], W1/W3 [E,d,n], W2 [E,n,d] -> (Act [T*K,n], Y [T*K,d])."""
+    lib = load_library()
+    A, d = Xp.shape
+    E, _, n = W1.shape
+    T = A // K
+    dev = Xp.device
+    Act = torch.empty((A, n), dtype=Xp.dtype, device=dev)
+    Y = torch.empty((A, d), dtype=Xp.dtype, device=dev)
+    _check(lib.moe_grouped_ffn(_dev(Xp, "Xp"), _dev(W1, "W1", Xp.dtype), _dev(W3, "W3", Xp.dtype),
+                               _dev(W2, "W2", Xp.dtype), dtype_code(Xp.dtype), T, d, E, K, n,
+                               _dev(counts, "counts", torch.int32), _dev(offsets, "offsets", torch.int32),
+                               Act.data_ptr(), Y.data_ptr(), _stream(dev)), "moe_grouped_ffn")
+    return Act, Y
+
+
+def moe_combine(Y: torch.Tensor, topk_w: torch.Tensor, inv: torch.Tensor):
+    """Step 5.  Y [T*K,d], topk_w [T,K] f32, inv [T*K] i32 -> out [T,d]."""
+    lib = load_library()
+    T, K = topk_w.shape
+    d = Y.shape[1]
+    dev = Y.device
+    out = torch.empty((T, d), dtype=Y.dtype, device=dev)
+    _check(lib.moe_combine(_dev(Y, "Y"), _dev(topk_w, "topk_w", torch.float32), _dev(inv, "inv", torch.int32),
+                           dtype_code(Y.dtype), T, d, K, out.data_ptr(), _stream(dev)), "moe_combine")
+    return out
+
+
+class ForwardPlan:
+    """Preallocated outputs and workspace for repeated moe_forward calls on one shape."""
+
+    def __init__(self, T: int, d: int, E: int, K: int, n: int, dtype: torch.dtype, device):
+        lib = load_library()
+        self.T, self.d, self.E, self.K, self.n, self.dtype = T, d, E, K, n, dtype
+        self.device = torch.device(device)
+        self.ws_bytes = lib.moe_forward_workspace_bytes(T, d, E, K, n, dtype_code(dtype))
+        if self.ws_bytes == 0:
+            raise MoEError(MOE_ERR_UNSUPPORTED, "moe_forward_workspace_bytes", lib.moe_last_error().decode())
+        dev = self.device
+        self.ws = _workspace(self.ws_bytes, dev)
+        self.out = torch.empty((T, d), dtype=dtype, device=dev)
+        self.topk_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.sorted_pair = torch.empty(T * K, dtype=torch.int32, device=dev)
+        self.inv = torch.empty(T * K, dtype=torch.int32, device=dev)
+
+    def __call__(self, X, logits, W1, W3, W2):
+        lib = load_library()
+        dt = self.dtype
+        _check(lib.moe_forward(_dev(X, "X", dt), _dev(logits, "logits", torch.float32), _dev(W1, "W1", dt),
+                               _dev(W3, "W3", dt), _dev(W2, "W2", dt), dtype_code(dt), self.T, self.d, self.E,
+                               self.K, self.n, self.out.data_ptr(), self.topk_idx.data_ptr(),
+                               self.topk_w.data_ptr(), self.counts.data_ptr(), self.offsets.data_ptr(),
+                               self.sorted_pair.data_ptr(), self.inv.data_ptr(), self.ws.data_ptr(),
+                               self.ws_bytes, _stream(self.device)), "moe_forward")
+        return self.out
+
+
+def moe_forward(X: torch.Tensor, logits: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, W2: torch.Tensor,
+                K: int):
+    """Whole layer.  Returns (out [T,d], plan) -- the plan also holds the routing outputs."""
+    T, d = X.shape
+    E, _, n = W1.shape
+    plan = ForwardPlan(T, d, E, K, n, X.dtype, X.device)
+    plan(X, logits, W1, W3, W2)
+    return plan.out, plan

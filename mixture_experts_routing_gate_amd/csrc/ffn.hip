@@ -1,0 +1,293 @@
+// Step 4 of the MoE layer forward: the grouped expert MLP.
+//
+// Page [P4] "MoE architecture optimisation and SonicMoE practice" section 1
+// (each expert is a two-layer MLP, first layer through SiLU) and section 2.2
+// (the SwiGLU activation fused into the GEMM epilogue); page [P3] "Triton
+// optimisation speeds up matrix computation for Mixture-of-Experts models"
+// (all experts' GEMMs in one launch; a persistent grid sized to the machine
+// that walks a tile list).  The tile list is derived on the device from the
+// per-expert counts: expert e owns ceil(count_e / BM) row tiles times N/BN
+// column tiles, so empty experts cost nothing and no host sync is needed.
+//
+//   FFN1: Act[r] = SiLU(Xp[r] W1[e]) * (Xp[r] W3[e])   (both products in one tile)
+//   FFN2: Y[r]   = Act[r] W2[e]
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Builds s_start[0..E] = exclusive prefix over experts of (row tiles * NT) in
+// LDS.  Must be called by all threads of the block.
+template <int BM>
+__device__ void build_schedule(const int32_t* __restrict__ counts, int E, int NT, int rows,
+                               int* s_start, int* s_tmp) {
+    const int tid = threadIdx.x;
+    int v = 0;
+    if (tid < E) v = ((min(max(counts[tid], 0), rows) + BM - 1) / BM) * NT;
+    s_tmp[tid] = v;
+    __syncthreads();
+    for (int sh = 1; sh < 256; sh <<= 1) {  // inclusive scan over 256 slots
+        const int x = (tid >= sh) ? s_tmp[tid - sh] : 0;
+        __syncthreads();
+        s_tmp[tid] += x;
+        __syncthreads();
+    }
+    if (tid < E) s_start[tid + 1] = s_tmp[tid];
+    if (tid == 0) s_start[0] = 0;
+    __syncthreads();
+}
+
+// Expert owning global tile `tile`: the last e with s_start[e] <= tile.
+__device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) {
+    int lo = 0, hi = E;  // answer in [lo, hi)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_start[mid] <= tile) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+MOE_DEV float silu_mul(float h1, float h3) { return h1 / (1.0f + __expf(-h1)) * h3; }
+
+// bf16 MFMA tile kernel.  Block tile 128 x 128 x 64, four waves in 2 x 2, each
+// wave 64 x 64 as 2 x 2 v_mfma_f32_32x32x16_bf16 tiles (x2 for the W1/W3 pair).
+// A [rows, Kd] is K-contiguous; B [Kd, N] is N-contiguous and is transposed
+// into LDS so that both MFMA operands read 8 consecutive k per lane.
+template <bool DUAL>
+__global__ __launch_bounds__(kThreads, 2) void ffn_bf16_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
+    uint16_t* __restrict__ C, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    int E, int Kd, int N, int rows) {
+    constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
+    constexpr int NB = DUAL ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][BN * LDK];
+    __shared__ int s_start[257];
+    __shared__ int s_tmp[256];
+
+    const int NT = N / BN;
+    build_schedule<BM>(counts, E, NT, rows, s_start, s_tmp);
+    const int total = s_start[E];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, lh = lane >> 5;
+
+    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+        const int e = find_expert(s_start, E, tile);
+        const int cnt = min(max(counts[e], 0), rows);
+        const int mt = (cnt + BM - 1) / BM;
+        const int local = tile - s_start[e];
+        const int m_tile = local % mt;
+        const int n_tile = local / mt;
+        const int r0 = offsets[e] + m_tile * BM;
+        // rows of this tile that exist; never past the end of A/C whatever counts/offsets hold
+        const int rows_valid = (r0 < 0 || r0 >= rows) ? 0 : min(min(BM, cnt - m_tile * BM), rows - r0);
+        const size_t row0 = (size_t)max(r0, 0);
+        const int n0 = n_tile * BN;
+        const uint16_t* Bp[2] = {B0 + (size_t)e * Kd * N, DUAL ? B1 + (size_t)e * Kd * N : nullptr};
+
+        f32x16 acc[NB][2][2];
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[m][mi][ni][i] = 0.0f;
+
+        for (int k0 = 0; k0 < Kd; k0 += BK) {
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = tid + kThreads * i;
+                const int r = c >> 3;
+                const int kc = (c & 7) << 3;
+                u32x4 val = {0u, 0u, 0u, 0u};
+                if (r < rows_valid) val = *reinterpret_cast<const u32x4*>(A + (row0 + r) * Kd + k0 + kc);
+                *reinterpret_cast<u32x4*>(As + r * LDK + kc) = val;
+            }
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = tid + kThreads * i;
+                    const int kr = c >> 4;
+                    const int nc = (c & 15) << 3;
+                    const u32x4 val =
+                        *reinterpret_cast<const u32x4*>(Bp[m] + (size_t)(k0 + kr) * N + n0 + nc);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        Bs[m][(nc + j) * LDK + kr] = (uint16_t)(val[j >> 1] >> (16 * (j & 1)));
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                bf16x8 a[2], b[NB][2];
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+                    a[mi] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + mi * 32 + l32) * LDK + ks * 16 + lh * 8);
+#pragma unroll
+                for (int m = 0; m < NB; ++m)
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+                        b[m][ni] = *reinterpret_cast<const bf16x8*>(Bs[m] + (wn * 64 + ni * 32 + l32) * LDK + ks * 16 + lh * 8);
+#pragma unroll
+                for (int m = 0; m < NB; ++m)
+#pragma unroll
+                    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                        for (int ni = 0; ni < 2; ++ni)
+                            acc[m][mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[m][ni], acc[m][mi][ni], 0, 0, 0);
+            }
+        }
+        // 32x32 accumulator layout: element i of lane l is row (i/4)*8 + (l/32)*4 + i%4, column l%32.
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int row = wm * 64 + mi * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+                    const int col = n0 + wn * 64 + ni * 32 + l32;
+                    if (row < rows_valid) {
+                        float v = acc[0][mi][ni][i];
+                        if (DUAL) v = silu_mul(v, acc[NB - 1][mi][ni][i]);
+                        C[(row0 + row) * N + col] = f32_to_bf16(v);
+                    }
+                }
+    }
+}
+
+// fp32 tile kernel (plain FMA): block tile 64 x 64 x 16, each thread 4 x 4 outputs.
+template <bool DUAL>
+__global__ __launch_bounds__(kThreads) void ffn_f32_kernel(const float* __restrict__ A,
+                                                           const float* __restrict__ B0,
+                                                           const float* __restrict__ B1,
+                                                           float* __restrict__ C,
+                                                           const int32_t* __restrict__ counts,
+                                                           const int32_t* __restrict__ offsets, int E,
+                                                           int Kd, int N, int rows) {
+    constexpr int BM = 64, BN = 64, BK = 16;
+    constexpr int NB = DUAL ? 2 : 1;
+    __shared__ float As[BK][BM + 4];
+    __shared__ float Bs[NB][BK][BN + 4];
+    __shared__ int s_start[257];
+    __shared__ int s_tmp[256];
+    const int NT = N / BN;
+    build_schedule<BM>(counts, E, NT, rows, s_start, s_tmp);
+    const int total = s_start[E];
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+
+    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+        const int e = find_expert(s_start, E, tile);
+        const int cnt = min(max(counts[e], 0), rows);
+        const int mt = (cnt + BM - 1) / BM;
+        const int local = tile - s_start[e];
+        const int m_tile = local % mt;
+        const int n_tile = local / mt;
+        const int r0 = offsets[e] + m_tile * BM;
+        // rows of this tile that exist; never past the end of A/C whatever counts/offsets hold
+        const int rows_valid = (r0 < 0 || r0 >= rows) ? 0 : min(min(BM, cnt - m_tile * BM), rows - r0);
+        const size_t row0 = (size_t)max(r0, 0);
+        const int n0 = n_tile * BN;
+        const float* Bp[2] = {B0 + (size_t)e * Kd * N, DUAL ? B1 + (size_t)e * Kd * N : nullptr};
+        float acc[NB][4][4];
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[m][i][j] = 0.0f;
+        for (int k0 = 0; k0 < Kd; k0 += BK) {
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = tid + kThreads * i;
+                const int r = c >> 4, kk = c & 15;
+                As[kk][r] = (r < rows_valid) ? A[(row0 + r) * Kd + k0 + kk] : 0.0f;
+            }
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = tid + kThreads * i;
+                    const int kk = c >> 6, nn = c & 63;
+                    Bs[m][kk][nn] = Bp[m][(size_t)(k0 + kk) * N + n0 + nn];
+                }
+            __syncthreads();
+#pragma unroll
+            for (int kk = 0; kk < BK; ++kk) {
+                float a[4], b[NB][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+                for (int m = 0; m < NB; ++m)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) b[m][j] = Bs[m][kk][tx + 16 * j];
+#pragma unroll
+                for (int m = 0; m < NB; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[m][i][j] = fmaf(a[i], b[m][j], acc[m][i][j]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = ty + 16 * i;
+                if (row < rows_valid) {
+                    float v = acc[0][i][j];
+                    if (DUAL) {
+                        const float h3 = acc[NB - 1][i][j];
+                        v = v / (1.0f + expf(-v)) * h3;
+                    }
+                    C[(row0 + row) * N + n0 + tx + 16 * j] = v;
+                }
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
+                      int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
+                      void* Act, void* Y, hipStream_t s) {
+    const int grid = device_cu_count() * 2;
+    if (dtype == 1) {
+        hipLaunchKernelGGL(ffn_bf16_kernel<true>, dim3(grid), dim3(kThreads), 0, s,
+                           static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
+                           static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(Act), counts,
+                           offsets, E, d, n, rows);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(ffn_bf16_kernel<false>, dim3(grid), dim3(kThreads), 0, s,
+                           static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
+                           static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(Y), counts,
+                           offsets, E, n, d, rows);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(ffn_f32_kernel<true>, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const float*>(Xp), static_cast<const float*>(W1),
+                       static_cast<const float*>(W3), static_cast<float*>(Act), counts, offsets, E, d,
+                       n, rows);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(ffn_f32_kernel<false>, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const float*>(Act), static_cast<const float*>(W2),
+                       static_cast<const float*>(nullptr), static_cast<float*>(Y), counts, offsets, E,
+                       n, d, rows);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,41 @@
+// Host-side launchers of the libmoe kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tokens per chunk: the gate writes one expert histogram per chunk and the
+// permutation places each chunk's rows at that chunk's base, so the stable
+// order needs no cross-chunk communication beyond one scan.
+inline int chunk_tokens(int T) { return T <= 65536 ? 256 : 1024; }
+inline int num_chunks(int T) { return (T + chunk_tokens(T) - 1) / chunk_tokens(T); }
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// Steps 1-2.
+hipError_t launch_gate(const float* logits, int T, int E, int K, int32_t* idx, float* w,
+                       int32_t* blk, hipStream_t s);
+hipError_t launch_scan(const int32_t* blk, int B, int E, int32_t* counts, int32_t* offsets,
+                       int32_t* blkbase, hipStream_t s);
+
+// Step 3.
+hipError_t launch_chunk_hist(const int32_t* idx, int T, int E, int K, int32_t* blk, hipStream_t s);
+hipError_t launch_rank(const int32_t* idx, int T, int E, int K, const int32_t* blkbase,
+                       int32_t* sorted_pair, int32_t* inv, hipStream_t s);
+hipError_t launch_copy_rows(const void* X, size_t row_bytes, int T, int K, const int32_t* inv,
+                            void* Xp, hipStream_t s);
+
+// Step 4.  dtype: 0 = fp32, 1 = bf16.
+hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
+                      int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
+                      void* Act, void* Y, hipStream_t s);
+
+// Step 5.
+hipError_t launch_combine(const void* Y, const float* w, const int32_t* inv, int dtype, int T, int d,
+                          int K, void* out, hipStream_t s);
+
+}  // namespace moe

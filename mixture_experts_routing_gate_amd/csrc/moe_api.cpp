@@ -1,0 +1,321 @@
+// C ABI of libmoe: argument validation, workspace carving and kernel
+// orchestration for the MoE layer forward.  The entry points are declared
+// (with their semantics and the passages they follow) in include/moe.h.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 8;
+
+// Shared checks of (T, E, K).  Returns MOE_OK or an error status.
+int check_tek(int T, int E, int K) {
+    if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1 (got %d)", T);
+    if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1 (got %d)", E);
+    if (K < 1 || K > E) return fail(MOE_ERR_INVALID_ARG, "K must be in [1, E] (got K=%d, E=%d)", K, E);
+    if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E=%d exceeds the supported maximum %d", E, kMaxE);
+    if (K > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "K=%d exceeds the supported maximum %d", K, kMaxK);
+    if ((long long)T * K >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*K must be < 2^31");
+    return MOE_OK;
+}
+
+int check_dtype(int dtype) {
+    if (dtype != MOE_F32 && dtype != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    return MOE_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+// Feature dimensions handled by the tile kernels: multiples of the tile edge.
+int check_dim(const char* name, int v, int dtype) {
+    const int q = dtype == MOE_BF16 ? 128 : 64;
+    if (v < 1) return fail(MOE_ERR_INVALID_ARG, "%s must be >= 1 (got %d)", name, v);
+    if (v % q != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "%s=%d must be a multiple of %d for this dtype", name, v, q);
+    return MOE_OK;
+}
+
+// Row-copy dims: 16-byte rows suffice.
+int check_row(int d, int dtype) {
+    if (d < 1) return fail(MOE_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+    if (((size_t)d * elem_bytes(dtype)) % 16 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "rows of d=%d elements must be a multiple of 16 bytes", d);
+    return MOE_OK;
+}
+
+#define CHECK(expr)                     \
+    do {                                \
+        const int _s = (expr);          \
+        if (_s != MOE_OK) return _s;    \
+    } while (0)
+
+#define NONNULL(p)                                                                          \
+    do {                                                                                    \
+        if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s must not be NULL", #p);     \
+        if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s must be 16-byte aligned", #p); \
+    } while (0)
+
+#define HIPCHECK(expr)                                                                       \
+    do {                                                                                     \
+        const hipError_t _e = (expr);                                                        \
+        if (_e != hipSuccess)                                                                \
+            return fail(MOE_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(_e));         \
+    } while (0)
+
+// Workspace carving: a bump allocator over the caller's buffer.
+struct Carver {
+    char* base;
+    size_t used = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <typename T>
+    T* take(size_t count) {
+        T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+        used += align_up(count * sizeof(T));
+        return p;
+    }
+};
+
+size_t route_ws(int T, int E) { return align_up((size_t)num_chunks(T) * E * sizeof(int32_t)); }
+
+size_t permute_ws(int T, int E) {
+    return 2 * align_up((size_t)num_chunks(T) * E * sizeof(int32_t)) + align_up(E * sizeof(int32_t)) +
+           align_up((E + 1) * sizeof(int32_t));
+}
+
+size_t forward_ws(int T, int d, int E, int K, int n, int dtype) {
+    const size_t A = (size_t)T * K;
+    const size_t s = elem_bytes(dtype);
+    size_t b = 0;
+    b += 2 * align_up((size_t)num_chunks(T) * E * 4);  // blk, blkbase
+    b += align_up(A * 4) * 2;                          // topk_idx, topk_w
+    b += align_up(E * 4) + align_up((E + 1) * 4);      // counts, offsets
+    b += align_up(A * 4) * 2;                          // sorted_pair, inv
+    b += align_up(A * d * s) * 2 + align_up(A * n * s);  // Xp, Y, Act
+    return b;
+}
+
+std::atomic<int> g_cu_count[64];
+
+}  // namespace
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+        cu = 256;
+    if (dev < 64) g_cu_count[dev].store(cu, std::memory_order_relaxed);
+    return cu;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported size or dtype";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+size_t moe_route_workspace_bytes(int T, int E, int K) {
+    if (check_tek(T, E, K) != MOE_OK) return 0;
+    return route_ws(T, E);
+}
+
+size_t moe_permute_workspace_bytes(int T, int E, int K) {
+    if (check_tek(T, E, K) != MOE_OK) return 0;
+    return permute_ws(T, E);
+}
+
+size_t moe_forward_workspace_bytes(int T, int d, int E, int K, int n, int dtype) {
+    if (check_tek(T, E, K) != MOE_OK || check_dtype(dtype) != MOE_OK || check_dim("d", d, dtype) != MOE_OK ||
+        check_dim("n", n, dtype) != MOE_OK)
+        return 0;
+    return forward_ws(T, d, E, K, n, dtype);
+}
+
+int moe_route(const float* logits, int T, int E, int K, int32_t* topk_idx, float* topk_w,
+              int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes, void* stream) {
+    CHECK(check_tek(T, E, K));
+    NONNULL(logits);
+    NONNULL(topk_idx);
+    NONNULL(topk_w);
+    NONNULL(counts);
+    NONNULL(offsets);
+    const size_t need = route_ws(T, E);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "moe_route needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Carver c(ws);
+    int32_t* blk = c.take<int32_t>((size_t)num_chunks(T) * E);
+    HIPCHECK(launch_gate(logits, T, E, K, topk_idx, topk_w, blk, s));
+    HIPCHECK(launch_scan(blk, num_chunks(T), E, counts, offsets, nullptr, s));
+    return MOE_OK;
+}
+
+int moe_permute(const void* X, int dtype, int T, int d, int E, int K, const int32_t* topk_idx,
+                int32_t* sorted_pair, int32_t* inv, void* Xp, void* ws, size_t ws_bytes, void* stream) {
+    CHECK(check_tek(T, E, K));
+    CHECK(check_dtype(dtype));
+    CHECK(check_row(d, dtype));
+    NONNULL(X);
+    NONNULL(topk_idx);
+    NONNULL(sorted_pair);
+    NONNULL(inv);
+    NONNULL(Xp);
+    const size_t need = permute_ws(T, E);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "moe_permute needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int B = num_chunks(T);
+    Carver c(ws);
+    int32_t* blk = c.take<int32_t>((size_t)B * E);
+    int32_t* blkbase = c.take<int32_t>((size_t)B * E);
+    int32_t* cnt = c.take<int32_t>(E);
+    int32_t* off = c.take<int32_t>(E + 1);
+    HIPCHECK(launch_chunk_hist(topk_idx, T, E, K, blk, s));
+    HIPCHECK(launch_scan(blk, B, E, cnt, off, blkbase, s));
+    HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s));
+    HIPCHECK(launch_copy_rows(X, (size_t)d * elem_bytes(dtype), T, K, inv, Xp, s));
+    return MOE_OK;
+}
+
+int moe_grouped_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype, int T,
+                    int d, int E, int K, int n, const int32_t* counts, const int32_t* offsets, void* Act,
+                    void* Y, void* stream) {
+    CHECK(check_tek(T, E, K));
+    CHECK(check_dtype(dtype));
+    CHECK(check_dim("d", d, dtype));
+    CHECK(check_dim("n", n, dtype));
+    NONNULL(Xp);
+    NONNULL(W1);
+    NONNULL(W3);
+    NONNULL(W2);
+    NONNULL(counts);
+    NONNULL(offsets);
+    NONNULL(Act);
+    NONNULL(Y);
+    if ((long long)T * K * (long long)(d > n ? d : n) >= (1LL << 40))
+        return fail(MOE_ERR_UNSUPPORTED, "T*K*max(d,n) must be < 2^40");
+    HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, T * K, d, E, n, counts, offsets, Act, Y,
+                        static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_combine(const void* Y, const float* topk_w, const int32_t* inv, int dtype, int T, int d, int K,
+                void* out, void* stream) {
+    if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1 (got %d)", T);
+    if (K < 1) return fail(MOE_ERR_INVALID_ARG, "K must be >= 1 (got %d)", K);
+    if (K > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "K=%d exceeds the supported maximum %d", K, kMaxK);
+    if ((long long)T * K >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*K must be < 2^31");
+    CHECK(check_dtype(dtype));
+    CHECK(check_row(d, dtype));
+    NONNULL(Y);
+    NONNULL(topk_w);
+    NONNULL(inv);
+    NONNULL(out);
+    HIPCHECK(launch_combine(Y, topk_w, inv, dtype, T, d, K, out, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_forward(const void* X, const float* logits, const void* W1, const void* W3, const void* W2,
+                int dtype, int T, int d, int E, int K, int n, void* out, int32_t* topk_idx,
+                float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* inv,
+                void* ws, size_t ws_bytes, void* stream) {
+    CHECK(check_tek(T, E, K));
+    CHECK(check_dtype(dtype));
+    CHECK(check_dim("d", d, dtype));
+    CHECK(check_dim("n", n, dtype));
+    NONNULL(X);
+    NONNULL(logits);
+    NONNULL(W1);
+    NONNULL(W3);
+    NONNULL(W2);
+    NONNULL(out);
+    for (const void* p : {(const void*)topk_idx, (const void*)topk_w, (const void*)counts,
+                          (const void*)offsets, (const void*)sorted_pair, (const void*)inv})
+        if (p != nullptr && !aligned16(p))
+            return fail(MOE_ERR_INVALID_ARG, "optional outputs must be 16-byte aligned");
+    if ((long long)T * K * (long long)(d > n ? d : n) >= (1LL << 40))
+        return fail(MOE_ERR_UNSUPPORTED, "T*K*max(d,n) must be < 2^40");
+    const size_t need = forward_ws(T, d, E, K, n, dtype);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "moe_forward needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t A = (size_t)T * K;
+    const size_t sz = elem_bytes(dtype);
+    const int B = num_chunks(T);
+    Carver c(ws);
+    int32_t* blk = c.take<int32_t>((size_t)B * E);
+    int32_t* blkbase = c.take<int32_t>((size_t)B * E);
+    int32_t* ws_idx = c.take<int32_t>(A);
+    float* ws_w = c.take<float>(A);
+    int32_t* ws_cnt = c.take<int32_t>(E);
+    int32_t* ws_off = c.take<int32_t>(E + 1);
+    int32_t* ws_sp = c.take<int32_t>(A);
+    int32_t* ws_inv = c.take<int32_t>(A);
+    void* Xp = c.take<char>(A * d * sz);
+    void* Yb = c.take<char>(A * d * sz);
+    void* Act = c.take<char>(A * n * sz);
+    if (!topk_idx) topk_idx = ws_idx;
+    if (!topk_w) topk_w = ws_w;
+    if (!counts) counts = ws_cnt;
+    if (!offsets) offsets = ws_off;
+    if (!sorted_pair) sorted_pair = ws_sp;
+    if (!inv) inv = ws_inv;
+
+    HIPCHECK(launch_gate(logits, T, E, K, topk_idx, topk_w, blk, s));
+    HIPCHECK(launch_scan(blk, B, E, counts, offsets, blkbase, s));
+    HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s));
+    HIPCHECK(launch_copy_rows(X, (size_t)d * sz, T, K, inv, Xp, s));
+    HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, (int)A, d, E, n, counts, offsets, Act, Yb, s));
+    HIPCHECK(launch_combine(Yb, topk_w, inv, dtype, T, d, K, out, s));
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+"""GPU parity of moe_permute, moe_grouped_ffn and moe_combine, each fed the
+oracle's exact upstream outputs so that every step is tested on its own."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_routing_gate_amd as moe
+import oracle
+import synth
+from parity_util import check_close, check_equal, cuda, from_np, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def routed(cfg: synth.MoEConfig, seed=0):
+    """Host inputs of a small config plus the oracle's routing of them."""
+    inp = synth.make_inputs(cfg, "cpu", seed)
+    lg = to_np(inp["logits"])
+    idx, w, counts, offsets = oracle.route(lg, cfg.K)
+    sp, inv = oracle.permute(idx, cfg.E)
+    return inp, lg, idx, w, counts, offsets, sp, inv
+
+
+def forced_counts_idx(counts, K=1):
+    """topk_idx [T,1] whose histogram is exactly `counts` (tokens dealt round-robin)."""
+    E = len(counts)
+    rem = list(counts)
+    out = []
+    e = 0
+    while sum(rem):
+        if rem[e]:
+            out.append(e)
+            rem[e] -= 1
+        e = (e + 1) % E
+    return np.array(out, np.int32).reshape(-1, K)
+
+
+PERMUTE_CASES = [
+    synth.MoEConfig("p1", T=1, d=128, E=4, K=1, n=128),
+    synth.MoEConfig("p2", T=300, d=256, E=8, K=2, n=128),
+    synth.MoEConfig("p3", T=1000, d=384, E=64, K=4, n=128, logits="bias", bias_var=2.0),
+    synth.MoEConfig("p4", T=513, d=128, E=256, K=8, n=128, dtype="f32"),
+    synth.MoEConfig("p5", T=70001, d=128, E=16, K=2, n=128),
+]
+
+
+@pytest.mark.parametrize("cfg", PERMUTE_CASES, ids=lambda c: c.name)
+def test_permute_matches_oracle(cfg):
+    rng = np.random.default_rng(cfg.T)
+    lg = (rng.normal(size=(cfg.T, cfg.E)) + rng.normal(0, 2, cfg.E)).astype(np.float32)
+    idx, _, _, _ = oracle.route(lg, cfg.K)
+    X = synth._normal((cfg.T, cfg.d), 1.0, cfg.torch_dtype, torch.device("cpu"), synth._gen("cpu", 1, "X"))
+    sp, inv, Xp = moe.moe_permute(cuda(X), cuda(torch.from_numpy(idx)), cfg.E)
+    torch.cuda.synchronize()
+    rsp, rinv = oracle.permute(idx, cfg.E)
+    check_equal(sp, rsp, "sorted_pair")
+    check_equal(inv, rinv, "inv")
+    check_equal(Xp, oracle.gather_rows(to_np(X), rsp, cfg.K), "Xp")
+
+
+FFN_CASES = [
+    synth.CONFIGS["tiny"],
+    synth.MoEConfig("ffn_bf16", T=512, d=256, E=8, K=2, n=384),
+    synth.MoEConfig("ffn_ragged", T=300, d=128, E=16, K=4, n=256, logits="bias", bias_var=2.0),
+    synth.MoEConfig("ffn_sparse", T=1000, d=256, E=64, K=4, n=128, logits="bias", bias_var=4.0),
+    synth.MoEConfig("ffn_t1", T=1, d=128, E=4, K=1, n=128),
+    synth.MoEConfig("ffn_dense", T=200, d=256, E=1, K=1, n=256),
+    synth.MoEConfig("ffn_f32_ragged", T=333, d=192, E=8, K=3, n=128, dtype="f32", logits="bias", bias_var=2.0),
+]
+
+
+def _ffn_check(cfg, Xp_np, row_expert, counts, offsets, W):
+    Act, Y = moe.moe_grouped_ffn(cuda(from_np(Xp_np)), cuda(W["W1"]), cuda(W["W3"]), cuda(W["W2"]),
+                                 cuda(torch.from_numpy(counts)), cuda(torch.from_numpy(offsets)), cfg.K)
+    torch.cuda.synchronize()
+    ract, ry = oracle.expert_ffn(Xp_np, row_expert, to_np(W["W1"]), to_np(W["W3"]), to_np(W["W2"]))
+    check_close(Act, ract, cfg.dtype, "Act")
+    check_close(Y, ry, cfg.dtype, "Y")
+
+
+@pytest.mark.parametrize("cfg", FFN_CASES, ids=lambda c: c.name)
+def test_grouped_ffn_matches_oracle(cfg):
+    inp, lg, idx, w, counts, offsets, sp, inv = routed(cfg)
+    Xp = oracle.gather_rows(to_np(inp["X"]), sp, cfg.K)
+    _ffn_check(cfg, Xp, idx.ravel()[sp], counts, offsets, inp)
+
+
+@pytest.mark.parametrize("counts", [[1, 127, 128, 129], [0, 0, 255, 1], [128, 0, 0, 0], [0, 0, 0, 300]])
+def test_grouped_ffn_ragged_tails(counts):
+    cfg = synth.MoEConfig("tails", T=sum(counts), d=128, E=4, K=1, n=256)
+    idx = forced_counts_idx(counts)
+    c = np.bincount(idx.ravel(), minlength=4).astype(np.int32)
+    assert list(c) == counts
+    off = np.concatenate([[0], np.cumsum(c)]).astype(np.int32)
+    sp, inv = oracle.permute(idx, 4)
+    inp = synth.make_inputs(cfg, "cpu", 2)
+    Xp = oracle.gather_rows(to_np(inp["X"]), sp, 1)
+    _ffn_check(cfg, Xp, idx.ravel()[sp], c, off, inp)
+
+
+COMBINE_CASES = [
+    synth.CONFIGS["tiny"],
+    synth.MoEConfig("cmb_bf16", T=700, d=384, E=16, K=4, n=128, logits="bias", bias_var=2.0),
+    synth.MoEConfig("cmb_k8", T=129, d=7168 // 4, E=32, K=8, n=128),
+    synth.MoEConfig("cmb_k1", T=50, d=128, E=4, K=1, n=128),
+]
+
+
+@pytest.mark.parametrize("cfg", COMBINE_CASES, ids=lambda c: c.name)
+def test_combine_matches_oracle(cfg):
+    rng = np.random.default_rng(cfg.T)
+    lg = (rng.normal(size=(cfg.T, cfg.E)) + rng.normal(0, 2, cfg.E)).astype(np.float32)
+    idx, w, counts, offsets = oracle.route(lg, cfg.K)
+    sp, inv = oracle.permute(idx, cfg.E)
+    Y = torch.from_numpy(rng.normal(size=(cfg.T * cfg.K, cfg.d)).astype(np.float32)).to(cfg.torch_dtype)
+    out = moe.moe_combine(cuda(Y), cuda(torch.from_numpy(w)), cuda(torch.from_numpy(inv)))
+    torch.cuda.synchronize()
+    ref = oracle.combine(Y.float().numpy(), w, inv)
+    check_close(out, ref, cfg.dtype, "out")
