@@ -364,6 +364,236 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_wide_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel with a 4-stage LDS pipeline (used when d % 256 == 0 and
+// n % 128 == 0).  Same tiles as above (256 x 256 per CU, 4 waves of 128 x 128)
+// but K advances 32 at a time through four 32 KB LDS stages:
+//  * DMA is buffer_load ... lds: one scalar buffer resource per matrix, a
+//    fixed 32-bit per-lane offset per tile and a scalar offset per K-step, so
+//    issuing a load costs no vector ALU work.  The load for K-step kt+3 is
+//    issued during K-step kt, about 2.5 K-steps (~2.5k MFMA cycles) ahead of use.
+//  * Each 32-row B stage is stored as two 128-column halves so that every DMA
+//    instruction reads a single matrix (W1 or W3 for the SwiGLU GEMM).
+//  * Fragment reads use precomputed per-lane LDS addresses with immediate
+//    offsets; the next sub-step's fragments are read while the current
+//    sub-step's 16 MFMAs run; one barrier per K-step.
+// ---------------------------------------------------------------------------
+constexpr int kP4BK = 32, kP4Stage = 32768, kP4Lds = 4 * kP4Stage;
+
+// Raw buffer resource (4 scalar dwords): 48-bit base, stride 0, num_records,
+// and the gfx9 dword-3 format word.
+typedef int32_t rsrc_t __attribute__((ext_vector_type(4)));
+
+MOE_DEV rsrc_t make_rsrc(const void* base) {
+    const uint64_t a = (uint64_t)base;
+    rsrc_t r;
+    r[0] = uniform((int)(uint32_t)a);
+    r[1] = uniform((int)(uint32_t)(a >> 32) & 0xffff);
+    r[2] = 0x7fffffff;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from global memory straight into LDS at M0 + 16*lane.
+// Issued through inline assembly on purpose: the compiler cannot tell which
+// LDS bytes an LDS-DMA writes, so for the builtin it waits for every
+// outstanding load before the next LDS read -- which would drain the whole
+// prefetch pipeline each K-step.  The kernel orders the DMA itself with
+// explicit vmcnt waits and barriers.
+MOE_DEV void dma16(const rsrc_t& r, char* lds, uint32_t voff, uint32_t soff) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds;
+    __asm__ volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(uniform((int)m0)), "v"(voff), "s"(r), "s"(uniform((int)soff))
+        : "memory", "m0");
+}
+
+template <bool DUAL>
+__global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
+    uint16_t* __restrict__ C, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    int E, int Kd, int N, int rows) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    __shared__ int s_start[257];
+    __shared__ int s_tmp[256];
+
+    constexpr int OUTW = DUAL ? 128 : 256;
+    const int NT = N / OUTW;
+    build_schedule<kWideBM>(counts, E, NT, rows, s_start, s_tmp);
+    const int total = s_start[E];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = uniform(tid / kWave);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int g16 = lane >> 4, s16 = lane & 15;
+
+    // LDS fragment addresses (byte offsets into a stage; stages 2-3 use +64 KB).
+    // A row r, k-chunk c of 8 elements sits at r*64 + ((c ^ ((r/4)%4)) * 16).
+    const int arow = wm * 128 + l32;
+    int a_rd[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) a_rd[ks] = arow * 64 + (((ks * 2 + lh) ^ ((arow >> 2) & 3)) << 4);
+    // B k-row k, column n of half h sits at 16K + h*8K + k*256 + (((n/8) ^ 4*(k%4)) * 16) + (n%8)*2.
+    const int b_x = (s16 >> 2) << 2;
+    const int b_c = (g16 & 1) * 2 + ((s16 & 3) >> 1);
+    const int b_lane = 16384 + ((g16 >> 1) * 8 + (s16 >> 2)) * 256 + (s16 & 1) * 8;
+    int b_rd[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        const int half = DUAL ? (ni >> 1) : wn;
+        const int nn = DUAL ? (wn * 64 + (ni & 1) * 32) : ni * 32;
+        b_rd[ni] = b_lane + half * 8192 + ((((nn >> 3) ^ b_x) + b_c) << 4);
+    }
+
+    const int G = gridDim.x;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per_xcd = G >> 3;
+    for (int round = 0;; ++round) {
+        const int tile = round * G + xcd * per_xcd + slot;
+        if (tile >= total) break;
+        const int e = uniform(find_expert(s_start, E, tile));
+        const int cnt = min(max(counts[e], 0), rows);
+        const int mt = (cnt + kWideBM - 1) / kWideBM;
+        const int local = tile - s_start[e];
+        const int m_tile = local % mt;
+        const int n_tile = local / mt;
+        const int r0 = offsets[e] + m_tile * kWideBM;
+        const int rows_valid = (r0 < 0 || r0 >= rows) ? 0 : min(min(kWideBM, cnt - m_tile * kWideBM), rows - r0);
+        if (rows_valid <= 0) continue;
+        const int n0 = n_tile * OUTW;
+
+        // DMA sources.  A: 16 rows of 64 bytes per KB; rows past the segment are
+        // clamped to its last row.  B: 4 k-rows of one 128-column half per KB.
+        const rsrc_t ra = make_rsrc(A + (size_t)r0 * Kd);
+        const int half = wave >> 1;
+        const uint16_t* bmat = (DUAL && half) ? B1 : B0;
+        const rsrc_t rb = make_rsrc(bmat + (size_t)e * Kd * N);
+        uint32_t a_vo[4], b_vo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (wave * 4 + i) * 16 + (lane >> 2);
+            const int ch = (lane & 3) ^ ((r >> 2) & 3);
+            a_vo[i] = ((uint32_t)min(r, rows_valid - 1) * (uint32_t)Kd + ch * 8) * 2u;
+            const int kr = (wave & 1) * 16 + i * 4 + (lane >> 4);
+            const int bc = (lane & 15) ^ ((kr & 3) << 2);
+            const int col = (DUAL ? n0 : n0 + half * 128) + bc * 8;
+            b_vo[i] = ((uint32_t)kr * (uint32_t)N + col) * 2u;
+        }
+        const uint32_t b_step = (uint32_t)kP4BK * (uint32_t)N * 2u;
+        const int KT = Kd / kP4BK;
+        auto issue = [&](int kt, int stage) {
+            char* sa = smem + stage * kP4Stage + (wave * 4) * 1024;
+            char* sb = smem + stage * kP4Stage + 16384 + (wave * 4) * 1024;
+            const uint32_t sa_off = (uint32_t)kt * (kP4BK * 2);
+            const uint32_t sb_off = (uint32_t)kt * b_step;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dma16(ra, sa + i * 1024, a_vo[i], sa_off);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dma16(rb, sb + i * 1024, b_vo[i], sb_off);
+        };
+
+        f32x16 acc[4][4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+
+        bf16x8 af[2][4], bfr[2][4];
+        auto load_frags = [&](int stage, int ks, int buf) {
+            const char* sa = smem + stage * kP4Stage + a_rd[ks];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * 64);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const char* pb = smem + stage * kP4Stage + b_rd[ni] + ks * 16 * 256;
+                const bf16x4 h0 = lds_read_tr(pb);
+                const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
+                bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        };
+        auto mfma = [&](int buf, int lo, int hi) {
+#pragma unroll
+            for (int q = lo; q < hi; ++q) {
+                const int mi = q >> 2, ni = q & 3;
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
+            }
+        };
+
+        // Prologue: K-steps 0..2 in flight, wait for step 0.
+        issue(0, 0);
+        if (KT > 1) issue(1, 1);
+        if (KT > 2) issue(2, 2);
+        if (KT > 2) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (KT > 1) __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        load_frags(0, 0, 0);
+
+        for (int kt0 = 0; kt0 < KT; kt0 += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int kt = kt0 + u;
+                // sub-step 0: fragments of ks=1 stream in behind the 16 MFMAs of ks=0
+                load_frags(u, 1, 1);
+                mfma(0, 0, 16);
+#pragma unroll
+                for (int i = 0; i < 12; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                // sub-step 1: half the MFMAs, then wait for step kt+1 and sync,
+                // refill the stage of step kt-1 with step kt+3, read step kt+1's ks=0.
+                mfma(1, 0, 8);
+                if (kt + 2 < KT) __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+                if (kt + 3 < KT) issue(kt + 3, (u + 3) & 3);
+                if (kt + 1 < KT) load_frags((u + 1) & 3, 0, 0);
+                mfma(1, 8, 16);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+            }
+        }
+
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int m = wm * 128 + mi * 32 + l32;
+            if (m < rows_valid) {
+                uint16_t* crow = C + (size_t)(r0 + m) * N;
+#pragma unroll
+                for (int ni = 0; ni < (DUAL ? 2 : 4); ++ni) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float v[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            v[j] = acc[mi][ni][q * 4 + j];
+                            if (DUAL) v[j] = silu_mul(v[j], acc[mi][ni + 2][q * 4 + j]);
+                        }
+                        const int col = n0 + (DUAL ? wn * 64 + ni * 32 : wn * 128 + ni * 32) + q * 8 + lh * 4;
+                        uint2 pk;
+                        pk.x = pack_bf16x2(v[0], v[1]);
+                        pk.y = pack_bf16x2(v[2], v[3]);
+                        *reinterpret_cast<uint2*>(crow + col) = pk;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // fp32 tile kernel (plain FMA): block tile 64 x 64 x 16, each thread 4 x 4 outputs.
 template <bool DUAL>
 __global__ __launch_bounds__(kThreads) void ffn_f32_kernel(const float* __restrict__ A,
@@ -464,20 +694,20 @@ hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void
     const int cus = device_cu_count();
     const int grid = cus * 2;
     if (dtype == 1 && d % 256 == 0 && n % 128 == 0) {
-        hipError_t aerr = hipFuncSetAttribute((const void*)ffn_wide_kernel<true>,
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds);
+        hipError_t aerr = hipFuncSetAttribute((const void*)ffn_p4_kernel<true>,
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
         if (aerr == hipSuccess)
-            aerr = hipFuncSetAttribute((const void*)ffn_wide_kernel<false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds);
+            aerr = hipFuncSetAttribute((const void*)ffn_p4_kernel<false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
         if (aerr != hipSuccess) return aerr;
         const int wg = (cus / 8) * 8;
-        hipLaunchKernelGGL(ffn_wide_kernel<true>, dim3(wg), dim3(kThreads), kWideLds, s,
+        hipLaunchKernelGGL(ffn_p4_kernel<true>, dim3(wg), dim3(kThreads), kP4Lds, s,
                            static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
                            static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(Act), counts,
                            offsets, E, d, n, rows);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(ffn_wide_kernel<false>, dim3(wg), dim3(kThreads), kWideLds, s,
+        hipLaunchKernelGGL(ffn_p4_kernel<false>, dim3(wg), dim3(kThreads), kP4Lds, s,
                            static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
                            static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(Y), counts,
                            offsets, E, n, d, rows);
