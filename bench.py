@@ -7,8 +7,10 @@ n=14336, bf16, fp32 accumulation), inputs resident in HBM.  Prints ONE JSON line
   value       = active layer TFLOPS = 6*T*K*d*n / time per step
   gate        = fused gate Gtokens/s on [T=262144, E=128, K=8] (cold MALL)
   steps_us    = per-entry-point times of the layer (HIP events, median)
-  roofline    = the grouped FFN (moe_grouped_ffn: the SwiGLU GEMM then the
-                down-projection GEMM), MFMA-bound, against 2.5 PFLOP/s dense bf16
+  roofline    = the dominant kernel, the SwiGLU GEMM (moe_ffn_up: one launch
+                of the pipelined MFMA kernel), MFMA-bound, against 2.5 PFLOP/s
+                dense bf16; its HBM traffic comes from the committed rocprofv3
+                counter table (profiles/traffic.json) when it matches ffn.hip
   cpu_baseline= the CPU oracle (per-token loop, fp64 accumulation) on a bounded
                 sample of the same layer, on this host's cores
 Inputs are seeded synthetic tensors (see synth/); nothing is read from disk
@@ -30,7 +32,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "traffic.json")
-FFN_SOURCE = os.path.join(ROOT, "mixture_experts_routing_gate_amd", "csrc", "ffn.hip")
+CSRC = os.path.join(ROOT, "mixture_experts_routing_gate_amd", "csrc")
 
 
 def parse():
@@ -40,6 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run a plain copy of known size and each step once (for rocprofv3 --pmc) and exit")
     return ap.parse_args()
 
 
@@ -60,25 +64,54 @@ def event_time_ms(torch, fn, iters, flush=None):
     return statistics.median(times), times
 
 
-def ffn_traffic(cfg_name):
-    """HBM bytes per grouped-FFN call from the committed rocprofv3 counter table,
-    or None when absent or taken from a different ffn.hip."""
+def kernel_traffic(workload, kernel):
+    """Calibrated bytes per launch of `kernel` from the committed rocprofv3
+    counter table (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when
+    absent or when the kernel's source file changed since the counters were taken."""
     try:
         tab = json.load(open(TRAFFIC_TABLE))
-        src = hashlib.sha256(open(FFN_SOURCE, "rb").read()).hexdigest()
-        ent = tab.get(cfg_name, {})
-        if ent.get("ffn_source_sha256") != src:
+        ent = tab["workloads"][workload][kernel]
+        src = ent["source"]
+        now = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
+        if tab["sources"].get(src) != now:
             return None
-        return ent.get("ffn_hbm_bytes")
-    except (OSError, ValueError):
+        return ent["hbm_bytes"]
+    except (OSError, ValueError, KeyError):
         return None
+
+
+def traffic_probe(moe, synth, torch, dev):
+    """A plain copy of known size, then each step of the layer once on the
+    mixtral-shaped workload and the gate on the large gate workload (each after
+    one warm-up call), for FETCH_SIZE / WRITE_SIZE counter runs."""
+    n = 256 << 20  # 512 MiB of bf16
+    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    cfg = synth.CONFIGS["mixtral"]
+    g = synth.make_inputs(cfg, dev, seed=0)
+    for _ in range(2):
+        idx, w, counts, offsets = moe.moe_route(g["logits"], cfg.K)
+        sp, inv, Xp = moe.moe_permute(g["X"], idx, cfg.E)
+        Act = moe.moe_ffn_up(Xp, g["W1"], g["W3"], counts, offsets, cfg.K)
+        Y = moe.moe_ffn_down(Act, g["W2"], counts, offsets, cfg.K)
+        moe.moe_combine(Y, w, inv)
+    torch.cuda.synchronize()
+    del g, Xp, Act, Y
+    gcfg = synth.CONFIGS["gate_l"]
+    glg = synth.make_inputs(gcfg, dev, seed=0)["logits"]
+    for _ in range(2):
+        moe.moe_route(glg, gcfg.K)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": "done", "copy_bytes_each_way": 2 * n}), flush=True)
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU sharding is "
-                                   "described in DESIGN.md but not built)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "one GPU only: --gpus must be 1 (the expert-parallel sharding across GPUs "
+                                   "is not built)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np
@@ -93,6 +126,9 @@ def main():
     moe.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.traffic_probe:
+        traffic_probe(moe, synth, torch, dev)
+        return
 
     cfg = synth.CONFIGS["mixtral"]
     T, d, E, K, n = cfg.T, cfg.d, cfg.E, cfg.K, cfg.n
@@ -121,8 +157,15 @@ def main():
     torch.cuda.synchronize()
     r_ms, _ = event_time_ms(torch, lambda: moe.moe_route(g["logits"], K), 20)
     p_ms, _ = event_time_ms(torch, lambda: moe.moe_permute(g["X"], idx, E), 20)
-    f_ms, f_all = event_time_ms(torch, lambda: moe.moe_grouped_ffn(Xp, g["W1"], g["W3"], g["W2"], counts, offsets, K),
-                                max(5, args.steps // 2))
+    f_ms, _ = event_time_ms(torch, lambda: moe.moe_grouped_ffn(Xp, g["W1"], g["W3"], g["W2"], counts, offsets, K),
+                            max(5, args.steps // 2))
+    # The dominant kernel alone: the SwiGLU GEMM (one launch), then the down GEMM.
+    up_ms, _ = event_time_ms(torch, lambda: moe.moe_ffn_up(Xp, g["W1"], g["W3"], counts, offsets, K),
+                             max(5, args.steps // 2))
+    dn_ms, _ = event_time_ms(torch, lambda: moe.moe_ffn_down(Act, g["W2"], counts, offsets, K),
+                             max(5, args.steps // 2))
+    up_flops = 4.0 * A * d * n
+    up_tflops = up_flops / (up_ms * 1e-3) / 1e12
     c_ms, _ = event_time_ms(torch, lambda: moe.moe_combine(Y, w, inv), 20)
     s = 2  # bf16 bytes
     perm_bytes = T * (s * d * (1 + K) + 12 * K)
@@ -143,7 +186,7 @@ def main():
             "value": gcfg.T / (g_ms * 1e-3) / 1e9, "unit": "Gtokens/s", "us_per_call": g_ms * 1e3,
             "roofline": {"bound": "hbm", "achieved": gate_bytes / (g_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": gate_bytes / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "traffic": None}}
+                         "traffic": kernel_traffic("gate_l", "gate_kernel")}}
     del flush_buf
 
     out = {
@@ -167,14 +210,16 @@ def main():
             "permute": {"us": p_ms * 1e3, "GB/s": perm_bytes / (p_ms * 1e-3) / 1e9,
                         "frac_hbm": perm_bytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
             "grouped_ffn": {"us": f_ms * 1e3, "TFLOPS": ffn_tflops},
+            "ffn_up": {"us": up_ms * 1e3, "TFLOPS": up_tflops},
+            "ffn_down": {"us": dn_ms * 1e3, "TFLOPS": 2.0 * A * d * n / (dn_ms * 1e-3) / 1e12},
             "combine": {"us": c_ms * 1e3, "GB/s": comb_bytes / (c_ms * 1e-3) / 1e9,
                         "frac_hbm": comb_bytes / (c_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
         },
-        "roofline": {"kernel": "moe_grouped_ffn (ffn_wide_kernel: SwiGLU GEMM launch + down-projection launch)",
-                     "bound": "mfma", "achieved": round(ffn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ffn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": ffn_traffic("mixtral"),
-                     "algorithmic_flops_per_call": flops},
+        "roofline": {"kernel": "ffn_p4_kernel<true> (moe_ffn_up: Act = SiLU(Xp W1) * (Xp W3), one launch)",
+                     "bound": "mfma", "achieved": round(up_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(up_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": kernel_traffic("mixtral", "ffn_up"),
+                     "algorithmic_flops_per_launch": up_flops, "us_per_launch": up_ms * 1e3},
     }
 
     if not args.no_cpu_baseline:

@@ -135,6 +135,24 @@ int moe_grouped_ffn(const void* Xp, const void* W1, const void* W3, const void* 
                     const int32_t* offsets, void* Act, void* Y, void* stream);
 
 /*
+ * moe_ffn_up -- step 4a alone: the SwiGLU GEMM of moe_grouped_ffn.
+ *   Act[r] = SiLU(Xp[r] W1[e]) * (Xp[r] W3[e]) for rows r of expert e
+ *   ([P4] section 1 first layer through SiLU; section 2.2 SwiGLU epilogue).
+ * Arguments and layouts as for moe_grouped_ffn.  Out: Act [T*K,n].
+ */
+int moe_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int T, int d, int E, int K,
+               int n, const int32_t* counts, const int32_t* offsets, void* Act, void* stream);
+
+/*
+ * moe_ffn_down -- step 4b alone: the down-projection GEMM of moe_grouped_ffn.
+ *   Y[r] = Act[r] W2[e] for rows r of expert e ([P4] section 1 second layer).
+ * In: Act [T*K,n] (dtype), W2 [E,n,d], counts [E], offsets [E+1].
+ * Out: Y [T*K,d].
+ */
+int moe_ffn_down(const void* Act, const void* W2, int dtype, int T, int d, int E, int K, int n,
+                 const int32_t* counts, const int32_t* offsets, void* Y, void* stream);
+
+/*
  * moe_combine -- step 5: gate-weighted combine back to token order ([P4]
  * section 1 scatter; [P2] sections 1 and 6: the selected experts' outputs are
  * averaged with the gate weights).  A gather-sum by token, no atomics:

@@ -51,6 +51,8 @@ def load_library() -> ctypes.CDLL:
         "moe_route": ([P, I, I, I, P, P, P, P, P, Z, P], I),
         "moe_permute": ([P, I, I, I, I, I, P, P, P, P, P, Z, P], I),
         "moe_grouped_ffn": ([P, P, P, P, I, I, I, I, I, I, P, P, P, P, P], I),
+        "moe_ffn_up": ([P, P, P, I, I, I, I, I, I, P, P, P, P], I),
+        "moe_ffn_down": ([P, P, I, I, I, I, I, I, P, P, P, P], I),
         "moe_combine": ([P, P, P, I, I, I, I, P, P], I),
         "moe_forward": ([P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P], I),
     }
@@ -149,6 +151,33 @@ def moe_grouped_ffn(Xp: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, W2: to
                                _dev(counts, "counts", torch.int32), _dev(offsets, "offsets", torch.int32),
                                Act.data_ptr(), Y.data_ptr(), _stream(dev)), "moe_grouped_ffn")
     return Act, Y
+
+
+def moe_ffn_up(Xp: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, counts: torch.Tensor,
+               offsets: torch.Tensor, K: int):
+    """Step 4a.  Xp [T*K,d], W1/W3 [E,d,n] -> Act [T*K,n] = SiLU(Xp W1) * (Xp W3)."""
+    lib = load_library()
+    A, d = Xp.shape
+    E, _, n = W1.shape
+    dev = Xp.device
+    Act = torch.empty((A, n), dtype=Xp.dtype, device=dev)
+    _check(lib.moe_ffn_up(_dev(Xp, "Xp"), _dev(W1, "W1", Xp.dtype), _dev(W3, "W3", Xp.dtype), dtype_code(Xp.dtype),
+                          A // K, d, E, K, n, _dev(counts, "counts", torch.int32),
+                          _dev(offsets, "offsets", torch.int32), Act.data_ptr(), _stream(dev)), "moe_ffn_up")
+    return Act
+
+
+def moe_ffn_down(Act: torch.Tensor, W2: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor, K: int):
+    """Step 4b.  Act [T*K,n], W2 [E,n,d] -> Y [T*K,d] = Act W2."""
+    lib = load_library()
+    A, n = Act.shape
+    E, _, d = W2.shape
+    dev = Act.device
+    Y = torch.empty((A, d), dtype=Act.dtype, device=dev)
+    _check(lib.moe_ffn_down(_dev(Act, "Act"), _dev(W2, "W2", Act.dtype), dtype_code(Act.dtype), A // K, d, E, K, n,
+                            _dev(counts, "counts", torch.int32), _dev(offsets, "offsets", torch.int32),
+                            Y.data_ptr(), _stream(dev)), "moe_ffn_down")
+    return Y
 
 
 def moe_combine(Y: torch.Tensor, topk_w: torch.Tensor, inv: torch.Tensor):

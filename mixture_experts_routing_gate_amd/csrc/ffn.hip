@@ -166,202 +166,19 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_bf16_kernel(
     }
 }
 
-// ---------------------------------------------------------------------------
-// bf16 MFMA "wide" kernel, used when every GEMM width is a multiple of 256.
-//
-// One 256-thread workgroup per CU computes a 256 x 256 output tile (FFN2) or a
-// 256 x 128 Act tile from 256 columns of [W1 | W3] (FFN1), K in steps of 64.
-// Each wave owns 128 x 128: 4 x 4 v_mfma_f32_32x32x16_bf16 tiles, 256 fp32
-// accumulators per lane.
-//  * Global -> LDS: global_load_lds_dwordx4 (no register staging).  Each wave
-//    instruction writes 1 KB of LDS contiguously; which global 16-byte chunk a
-//    lane fetches implements an XOR swizzle that makes the fragment reads
-//    below conflict-free.  Two LDS stages of 64 KB: the next K-step streams
-//    in while the current one feeds the MFMAs.
-//  * A (rows of Xp or Act, K-contiguous) fragments: ds_read_b128, 8 k per lane.
-//  * B (weights, N-contiguous) fragments: two ds_read_b64_tr_b16 per 8 k; in
-//    each 16-lane group that instruction returns to lane i element i%4 of the
-//    8-byte chunks addressed by lanes i/4, 4+i/4, 8+i/4, 12+i/4, i.e. a 4 x 16
-//    -> 16 x 4 transpose, which is exactly the MFMA operand layout.
-//  * The MFMA is issued as W^T * X^T, so each lane's accumulator holds 4
-//    consecutive output columns of one row and stores 8 bytes at a time.
-//  * Rows past the end of an expert's segment are loaded clamped to its last
-//    row and never stored, so ragged tails need no zero fill.
-//  * Tile order: tile v of round r goes to the workgroup on XCD (v / 32) % 8,
-//    so the 32 workgroups of one XCD share 8 row tiles and 4 column tiles of
-//    one expert in its L2.
-// ---------------------------------------------------------------------------
-constexpr int kWideBM = 256, kWideBK = 64;
-constexpr int kWideStageBytes = 256 * 64 * 2 * 2;  // A 32 KB + B 32 KB
-constexpr int kWideLds = 2 * kWideStageBytes;
+constexpr int kBM256 = 256;  // rows per tile of the pipelined kernel
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-MOE_DEV void lds_dma16(const void* g, char* l) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
-}
-
+// ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4 of the
+// 8-byte chunks addressed by lanes i/4, 4+i/4, 8+i/4 and 12+i/4 -- a 4 x 16 ->
+// 16 x 4 transpose of 16-bit values, which is the MFMA operand layout for an
+// N-contiguous B tile.
 MOE_DEV bf16x4 lds_read_tr(const char* l) {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(l));
     return __builtin_bit_cast(bf16x4, v);
-}
-
-template <bool DUAL>
-__global__ __launch_bounds__(kThreads, 1) void ffn_wide_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
-    uint16_t* __restrict__ C, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    int E, int Kd, int N, int rows) {
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
-    __shared__ int s_start[257];
-    __shared__ int s_tmp[256];
-
-    constexpr int OUTW = DUAL ? 128 : 256;  // output columns per tile
-    const int NT = N / OUTW;
-    build_schedule<kWideBM>(counts, E, NT, rows, s_start, s_tmp);
-    const int total = s_start[E];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int l32 = lane & 31, lh = lane >> 5;
-    const int g16 = lane >> 4, s16 = lane & 15;
-
-    // Persistent, XCD-aware walk: workgroups w and w+8 sit on one XCD.
-    const int G = gridDim.x;
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int per_xcd = G >> 3;
-    for (int round = 0;; ++round) {
-        const int tile = round * G + xcd * per_xcd + slot;
-        if (tile >= total) break;
-        const int e = uniform(find_expert(s_start, E, tile));
-        const int cnt = min(max(counts[e], 0), rows);
-        const int mt = (cnt + kWideBM - 1) / kWideBM;
-        const int local = tile - s_start[e];
-        const int m_tile = local % mt;
-        const int n_tile = local / mt;
-        const int r0 = offsets[e] + m_tile * kWideBM;
-        const int rows_valid = (r0 < 0 || r0 >= rows) ? 0 : min(min(kWideBM, cnt - m_tile * kWideBM), rows - r0);
-        if (rows_valid <= 0) continue;
-        const int n0 = n_tile * OUTW;
-
-        // Per-lane sources of this tile's 16 DMA chunks per K-step, as 32-bit
-        // element offsets from one base pointer per lane.
-        const uint16_t* abase = A + (size_t)r0 * Kd;
-        uint32_t aoff[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = (wave * 8 + i) * 8 + (lane >> 3);  // A row in the tile (8 rows per KB)
-            const int ch = (lane & 7) ^ ((r >> 1) & 7);
-            aoff[i] = (uint32_t)min(r, rows_valid - 1) * (uint32_t)Kd + ch * 8;
-        }
-        // B: 2 k-rows per KB; lane%32 picks the 16-byte chunk, XOR-swizzled by
-        // 4*(k%4), which keeps it inside the same 128-column half.
-        const uint16_t* bbase = (DUAL && (lane & 16)) ? B1 + (size_t)e * Kd * N : B0 + (size_t)e * Kd * N;
-        uint32_t boff[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int kr = (wave * 8 + i) * 2 + lh;
-            const int bc = (lane & 31) ^ ((kr & 3) << 2);
-            const int col = DUAL ? n0 + (bc & 15) * 8 : n0 + bc * 8;
-            boff[i] = (uint32_t)kr * (uint32_t)N + col;
-        }
-
-        f32x16 acc[4][4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
-
-        // Fragment addresses.  A: row r = wm*128 + mi*32 + lane%32 at k-chunk
-        // 2*ks + lane/32, swizzled by (r/2)%8 = (lane%32/2)%8, the same for all mi.
-        const int a_sw = (l32 >> 1) & 7;
-        const int a_row = (wm * 128 + l32) * 128;
-        // B (transposed reads): lane (g16, s16) of the wave addresses k-row
-        // 16*ks + 8*(g16/2) + 4*hh + s16/4 and columns col + 16*(g16%2) + 4*(s16%4).
-        const int b_krow = ((g16 >> 1) * 8 + (s16 >> 2)) * 512 + (s16 & 1) * 8;
-        const int b_x = (s16 >> 2) << 2;                 // swizzle 4*(k%4): k%4 == s16/4
-        const int b_c = (g16 & 1) * 2 + ((s16 & 3) >> 1);
-        int b_addr[4];
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const int bcol = DUAL ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32) : (wn * 128 + ni * 32);
-            b_addr[ni] = b_krow + ((((bcol >> 3) ^ b_x) + b_c) << 4);
-        }
-
-        const int KT = Kd / kWideBK;
-        auto issue = [&](int kt, int stage) {
-            char* sA = smem + stage * kWideStageBytes;
-            char* sB = sA + 32768;
-            const uint16_t* ak = abase + (size_t)kt * kWideBK;
-            const uint16_t* bk = bbase + (size_t)kt * kWideBK * N;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) lds_dma16(ak + aoff[i], sA + (wave * 8 + i) * 1024);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) lds_dma16(bk + boff[i], sB + (wave * 8 + i) * 1024);
-        };
-
-        __syncthreads();  // previous tile's readers are done with both stages
-        issue(0, 0);
-        for (int kt = 0; kt < KT; ++kt) {
-            const int cur = kt & 1;
-            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (kt + 1 < KT) issue(kt + 1, cur ^ 1);
-            const char* sA = smem + cur * kWideStageBytes;
-            const char* sB = sA + 32768;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                bf16x8 af[4], bfr[4];
-                const char* pa = sA + a_row + (((ks * 2 + lh) ^ a_sw) << 4);
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi) af[mi] = *reinterpret_cast<const bf16x8*>(pa + mi * 32 * 128);
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const char* pb = sB + b_addr[ni] + ks * 16 * 512;
-                    const bf16x4 h0 = lds_read_tr(pb);
-                    const bf16x4 h1 = lds_read_tr(pb + 4 * 512);
-                    bfr[ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
-            }
-        }
-
-        // Epilogue.  acc[mi][ni][i] is output row m = wm*128 + mi*32 + lane%32 and
-        // column (within the 32-column block) (i/4)*8 + (lane/32)*4 + i%4.
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int m = wm * 128 + mi * 32 + l32;
-            if (m < rows_valid) {
-                uint16_t* crow = C + (size_t)(r0 + m) * N;
-#pragma unroll
-                for (int ni = 0; ni < (DUAL ? 2 : 4); ++ni) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float v[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            v[j] = acc[mi][ni][q * 4 + j];
-                            if (DUAL) v[j] = silu_mul(v[j], acc[mi][ni + 2][q * 4 + j]);
-                        }
-                        const int col = n0 + (DUAL ? wn * 64 + ni * 32 : wn * 128 + ni * 32) + q * 8 + lh * 4;
-                        uint2 pk;
-                        pk.x = pack_bf16x2(v[0], v[1]);
-                        pk.y = pack_bf16x2(v[2], v[3]);
-                        *reinterpret_cast<uint2*>(crow + col) = pk;
-                    }
-                }
-            }
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -422,7 +239,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
 
     constexpr int OUTW = DUAL ? 128 : 256;
     const int NT = N / OUTW;
-    build_schedule<kWideBM>(counts, E, NT, rows, s_start, s_tmp);
+    build_schedule<kBM256>(counts, E, NT, rows, s_start, s_tmp);
     const int total = s_start[E];
 
     const int tid = threadIdx.x;
@@ -458,12 +275,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
         if (tile >= total) break;
         const int e = uniform(find_expert(s_start, E, tile));
         const int cnt = min(max(counts[e], 0), rows);
-        const int mt = (cnt + kWideBM - 1) / kWideBM;
+        const int mt = (cnt + kBM256 - 1) / kBM256;
         const int local = tile - s_start[e];
         const int m_tile = local % mt;
         const int n_tile = local / mt;
-        const int r0 = offsets[e] + m_tile * kWideBM;
-        const int rows_valid = (r0 < 0 || r0 >= rows) ? 0 : min(min(kWideBM, cnt - m_tile * kWideBM), rows - r0);
+        const int r0 = offsets[e] + m_tile * kBM256;
+        const int rows_valid = (r0 < 0 || r0 >= rows) ? 0 : min(min(kBM256, cnt - m_tile * kBM256), rows - r0);
         if (rows_valid <= 0) continue;
         const int n0 = n_tile * OUTW;
 
@@ -688,55 +505,68 @@ __global__ __launch_bounds__(kThreads) void ffn_f32_kernel(const float* __restri
 
 }  // namespace
 
+// The pipelined bf16 kernel needs 256-wide down-projection tiles and K in
+// multiples of 128 for both GEMMs.
+static bool ffn_pipelined_ok(int d, int n) { return d % 256 == 0 && n % 128 == 0; }
+
+// Step 4a: Act = SiLU(Xp W1) * (Xp W3).
+hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int rows, int d, int E,
+                         int n, const int32_t* counts, const int32_t* offsets, void* Act, hipStream_t s) {
+    const int cus = device_cu_count();
+    if (dtype == 1 && ffn_pipelined_ok(d, n)) {
+        const hipError_t aerr = hipFuncSetAttribute((const void*)ffn_p4_kernel<true>,
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
+        if (aerr != hipSuccess) return aerr;
+        hipLaunchKernelGGL(ffn_p4_kernel<true>, dim3((cus / 8) * 8), dim3(kThreads), kP4Lds, s,
+                           static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
+                           static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(Act), counts, offsets, E, d,
+                           n, rows);
+    } else if (dtype == 1) {
+        hipLaunchKernelGGL(ffn_bf16_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s,
+                           static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
+                           static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(Act), counts, offsets, E, d,
+                           n, rows);
+    } else {
+        hipLaunchKernelGGL(ffn_f32_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s,
+                           static_cast<const float*>(Xp), static_cast<const float*>(W1),
+                           static_cast<const float*>(W3), static_cast<float*>(Act), counts, offsets, E, d, n,
+                           rows);
+    }
+    return hipGetLastError();
+}
+
+// Step 4b: Y = Act W2.
+hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows, int d, int E, int n,
+                           const int32_t* counts, const int32_t* offsets, void* Y, hipStream_t s) {
+    const int cus = device_cu_count();
+    if (dtype == 1 && ffn_pipelined_ok(d, n)) {
+        const hipError_t aerr = hipFuncSetAttribute((const void*)ffn_p4_kernel<false>,
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
+        if (aerr != hipSuccess) return aerr;
+        hipLaunchKernelGGL(ffn_p4_kernel<false>, dim3((cus / 8) * 8), dim3(kThreads), kP4Lds, s,
+                           static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
+                           static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(Y), counts, offsets, E,
+                           n, d, rows);
+    } else if (dtype == 1) {
+        hipLaunchKernelGGL(ffn_bf16_kernel<false>, dim3(cus * 2), dim3(kThreads), 0, s,
+                           static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
+                           static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(Y), counts, offsets, E,
+                           n, d, rows);
+    } else {
+        hipLaunchKernelGGL(ffn_f32_kernel<false>, dim3(cus * 2), dim3(kThreads), 0, s,
+                           static_cast<const float*>(Act), static_cast<const float*>(W2),
+                           static_cast<const float*>(nullptr), static_cast<float*>(Y), counts, offsets, E, n, d,
+                           rows);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
                       int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
                       void* Act, void* Y, hipStream_t s) {
-    const int cus = device_cu_count();
-    const int grid = cus * 2;
-    if (dtype == 1 && d % 256 == 0 && n % 128 == 0) {
-        hipError_t aerr = hipFuncSetAttribute((const void*)ffn_p4_kernel<true>,
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
-        if (aerr == hipSuccess)
-            aerr = hipFuncSetAttribute((const void*)ffn_p4_kernel<false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
-        if (aerr != hipSuccess) return aerr;
-        const int wg = (cus / 8) * 8;
-        hipLaunchKernelGGL(ffn_p4_kernel<true>, dim3(wg), dim3(kThreads), kP4Lds, s,
-                           static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
-                           static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(Act), counts,
-                           offsets, E, d, n, rows);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(ffn_p4_kernel<false>, dim3(wg), dim3(kThreads), kP4Lds, s,
-                           static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
-                           static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(Y), counts,
-                           offsets, E, n, d, rows);
-        return hipGetLastError();
-    }
-    if (dtype == 1) {
-        hipLaunchKernelGGL(ffn_bf16_kernel<true>, dim3(grid), dim3(kThreads), 0, s,
-                           static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
-                           static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(Act), counts,
-                           offsets, E, d, n, rows);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(ffn_bf16_kernel<false>, dim3(grid), dim3(kThreads), 0, s,
-                           static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
-                           static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(Y), counts,
-                           offsets, E, n, d, rows);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL(ffn_f32_kernel<true>, dim3(grid), dim3(kThreads), 0, s,
-                       static_cast<const float*>(Xp), static_cast<const float*>(W1),
-                       static_cast<const float*>(W3), static_cast<float*>(Act), counts, offsets, E, d,
-                       n, rows);
-    hipError_t err = hipGetLastError();
+    const hipError_t err = launch_ffn_up(Xp, W1, W3, dtype, rows, d, E, n, counts, offsets, Act, s);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(ffn_f32_kernel<false>, dim3(grid), dim3(kThreads), 0, s,
-                       static_cast<const float*>(Act), static_cast<const float*>(W2),
-                       static_cast<const float*>(nullptr), static_cast<float*>(Y), counts, offsets, E,
-                       n, d, rows);
-    return hipGetLastError();
+    return launch_ffn_down(Act, W2, dtype, rows, d, E, n, counts, offsets, Y, s);
 }
 
 }  // namespace moe

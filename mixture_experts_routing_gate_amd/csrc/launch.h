@@ -29,7 +29,11 @@ hipError_t launch_rank(const int32_t* idx, int T, int E, int K, const int32_t* b
 hipError_t launch_copy_rows(const void* X, size_t row_bytes, int T, int K, const int32_t* inv,
                             void* Xp, hipStream_t s);
 
-// Step 4.  dtype: 0 = fp32, 1 = bf16.
+// Step 4.  dtype: 0 = fp32, 1 = bf16.  4a (SwiGLU GEMM), 4b (down GEMM), both.
+hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int rows, int d, int E,
+                         int n, const int32_t* counts, const int32_t* offsets, void* Act, hipStream_t s);
+hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows, int d, int E, int n,
+                           const int32_t* counts, const int32_t* offsets, void* Y, hipStream_t s);
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
                       int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
                       void* Act, void* Y, hipStream_t s);

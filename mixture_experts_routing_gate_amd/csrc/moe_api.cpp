@@ -245,6 +245,43 @@ int moe_grouped_ffn(const void* Xp, const void* W1, const void* W3, const void* 
     return MOE_OK;
 }
 
+int moe_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int T, int d, int E, int K, int n,
+               const int32_t* counts, const int32_t* offsets, void* Act, void* stream) {
+    CHECK(check_tek(T, E, K));
+    CHECK(check_dtype(dtype));
+    CHECK(check_dim("d", d, dtype));
+    CHECK(check_dim("n", n, dtype));
+    NONNULL(Xp);
+    NONNULL(W1);
+    NONNULL(W3);
+    NONNULL(counts);
+    NONNULL(offsets);
+    NONNULL(Act);
+    if ((long long)T * K * (long long)(d > n ? d : n) >= (1LL << 40))
+        return fail(MOE_ERR_UNSUPPORTED, "T*K*max(d,n) must be < 2^40");
+    HIPCHECK(launch_ffn_up(Xp, W1, W3, dtype, T * K, d, E, n, counts, offsets, Act,
+                           static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_ffn_down(const void* Act, const void* W2, int dtype, int T, int d, int E, int K, int n,
+                 const int32_t* counts, const int32_t* offsets, void* Y, void* stream) {
+    CHECK(check_tek(T, E, K));
+    CHECK(check_dtype(dtype));
+    CHECK(check_dim("d", d, dtype));
+    CHECK(check_dim("n", n, dtype));
+    NONNULL(Act);
+    NONNULL(W2);
+    NONNULL(counts);
+    NONNULL(offsets);
+    NONNULL(Y);
+    if ((long long)T * K * (long long)(d > n ? d : n) >= (1LL << 40))
+        return fail(MOE_ERR_UNSUPPORTED, "T*K*max(d,n) must be < 2^40");
+    HIPCHECK(launch_ffn_down(Act, W2, dtype, T * K, d, E, n, counts, offsets, Y,
+                             static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
 int moe_combine(const void* Y, const float* topk_w, const int32_t* inv, int dtype, int T, int d, int K,
                 void* out, void* stream) {
     if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1 (got %d)", T);

@@ -51,9 +51,10 @@ def _load():
         lib.oracle_gather_rows.argtypes = [P, I, I, I, I, P, P]
         lib.oracle_expert_ffn.argtypes = [P, I, I, P, P, I, P, P, P, I, I, I, P, P]
         lib.oracle_combine.argtypes = [P, P, P, I, I, I, P]
+        lib.oracle_expert_down.argtypes = [P, I, I, P, P, I, I, I, P]
         lib.oracle_layer.argtypes = [P, I, P, P, P, P, I, I, I, I, I, P, I, P]
         for f in (lib.oracle_softmax, lib.oracle_route, lib.oracle_permute, lib.oracle_gather_rows,
-                  lib.oracle_expert_ffn, lib.oracle_combine, lib.oracle_layer):
+                  lib.oracle_expert_ffn, lib.oracle_combine, lib.oracle_layer, lib.oracle_expert_down):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -142,6 +143,22 @@ def expert_ffn(Xp: np.ndarray, row_expert: np.ndarray, W1, W3, W2, rows=None):
     _check(_load().oracle_expert_ffn(_ptr(Xs), dt, nrows, _ptr(re), rp, nsel, _ptr(W1s), _ptr(W3s),
                                      _ptr(W2s), E, d, n, _ptr(act), _ptr(y)), "oracle_expert_ffn")
     return act, y
+
+
+def expert_down(act: np.ndarray, row_expert: np.ndarray, W2) -> np.ndarray:
+    """Second expert GEMM alone on expert-ordered rows.  -> y float32 [nrows, d]."""
+    As, dt = _storage(act)
+    W2s, d2 = _storage(W2)
+    if dt != d2:
+        raise ValueError("act and W2 must share one storage dtype")
+    nrows, n = As.shape
+    E, n_, d = W2s.shape
+    assert n_ == n
+    re = _c(row_expert, np.int32)
+    y = np.empty((nrows, d), np.float32)
+    _check(_load().oracle_expert_down(_ptr(As), dt, nrows, _ptr(re), _ptr(W2s), E, d, n, _ptr(y)),
+           "oracle_expert_down")
+    return y
 
 
 def combine(Y: np.ndarray, w: np.ndarray, inv: np.ndarray) -> np.ndarray:

@@ -26,6 +26,7 @@
  *   expert FFN / combine / layer - E=1,K=1 equals a dense SwiGLU MLP built
  *                  from library matmuls; identical experts reduce to that MLP
  *                  for any routing; zero row; exact scaling by 2
+ *   expert down  - reproduces expert FFN's y from its act; library matmul
  * Every function here is pinned; none is "parity unpinned".
  *
  * Errors: every entry point returns 0 on success and a negative value on a
@@ -201,6 +202,30 @@ int oracle_expert_ffn(const void* Xp, int dtype, int nrows, const int32_t* row_e
                    h1, h3, act + (size_t)s * n, y + (size_t)s * d);
         free(h1);
         free(h3);
+    }
+    return bad ? -1 : 0;
+}
+
+/* The second layer alone ([P4] section 1: the expert MLP's second GEMM):
+ * y[r, c] = sum_j act[r, j] W2[e_r][j, c] in fp64, stored fp32, where act is
+ * given in the storage dtype (fp32, or bf16 widened exactly).  Equals the y
+ * of oracle_expert_ffn when fed that function's act. */
+int oracle_expert_down(const void* act, int dtype, int nrows, const int32_t* row_expert,
+                       const void* W2, int E, int d, int n, float* y) {
+    if (!act || !row_expert || !W2 || !y || nrows < 0 || E < 1 || d < 1 || n < 1) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : bad)
+    for (int r = 0; r < nrows; ++r) {
+        const int e = row_expert[r];
+        if (e < 0 || e >= E) { bad |= 1; continue; }
+        double* acc = (double*)calloc((size_t)d, sizeof(double));
+        for (int j = 0; j < n; ++j) {
+            const double aj = load_elem(act, dtype, (size_t)r * n + j);
+            for (int c = 0; c < d; ++c) acc[c] += aj * load_elem(W2, dtype, (size_t)e * n * d + (size_t)j * d + c);
+        }
+        for (int c = 0; c < d; ++c) y[(size_t)r * d + c] = (float)acc[c];
+        free(acc);
     }
     return bad ? -1 : 0;
 }

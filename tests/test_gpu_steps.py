@@ -117,3 +117,30 @@ def test_combine_matches_oracle(cfg):
     torch.cuda.synchronize()
     ref = oracle.combine(Y.float().numpy(), w, inv)
     check_close(out, ref, cfg.dtype, "out")
+
+
+UPDOWN_CASES = [
+    synth.CONFIGS["tiny"],
+    synth.MoEConfig("ud_bf16", T=512, d=256, E=8, K=2, n=384),
+    synth.MoEConfig("ud_sparse", T=1000, d=512, E=64, K=4, n=256, logits="bias", bias_var=4.0),
+    synth.MoEConfig("ud_narrow", T=300, d=128, E=16, K=4, n=256, logits="bias", bias_var=2.0),
+]
+
+
+@pytest.mark.parametrize("cfg", UPDOWN_CASES, ids=lambda c: c.name)
+def test_ffn_up_and_down_separately(cfg):
+    """Step 4a and 4b through their own entry points, each against the oracle."""
+    inp, lg, idx, w, counts, offsets, sp, inv = routed(cfg)
+    Xp = oracle.gather_rows(to_np(inp["X"]), sp, cfg.K)
+    re = idx.ravel()[sp]
+    c_d, o_d = cuda(torch.from_numpy(counts)), cuda(torch.from_numpy(offsets))
+    Act = moe.moe_ffn_up(cuda(from_np(Xp)), cuda(inp["W1"]), cuda(inp["W3"]), c_d, o_d, cfg.K)
+    torch.cuda.synchronize()
+    ract, _ = oracle.expert_ffn(Xp, re, to_np(inp["W1"]), to_np(inp["W3"]), to_np(inp["W2"]))
+    check_close(Act, ract, cfg.dtype, "Act")
+    # down-projection fed the oracle's activation in the storage dtype
+    act_in = torch.from_numpy(ract).to(cfg.torch_dtype)
+    Y = moe.moe_ffn_down(cuda(act_in), cuda(inp["W2"]), c_d, o_d, cfg.K)
+    torch.cuda.synchronize()
+    ry = oracle.expert_down(to_np(act_in), re, to_np(inp["W2"]))
+    check_close(Y, ry, cfg.dtype, "Y")

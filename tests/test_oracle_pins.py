@@ -321,3 +321,21 @@ def test_synth_is_deterministic_and_shaped():
     assert abs(float(a["W2"].std()) - 1 / math.sqrt(256)) < 0.01
     c = synth.make_inputs(cfg, "cpu", 1)
     assert not torch.equal(a["X"], c["X"])
+
+
+def test_expert_down_matches_expert_ffn_and_matmul(oracle_lib):
+    """The down-projection alone reproduces expert_ffn's y from its act, and a library matmul."""
+    rows, d, n, E = 25, 16, 40, 3
+    Xp = _rng(80).normal(size=(rows, d)).astype(np.float32)
+    re = _rng(81).integers(0, E, size=rows).astype(np.int32)
+    W1, W3, W2 = _weights(E, d, n, 82)
+    act, y = oracle.expert_ffn(Xp, re, W1, W3, W2)
+    np.testing.assert_array_equal(oracle.expert_down(act, re, W2), y)
+    for r in range(rows):
+        np.testing.assert_allclose(oracle.expert_down(act[r:r + 1], re[r:r + 1], W2)[0],
+                                   act[r].astype(np.float64) @ W2[re[r]].astype(np.float64), rtol=1e-6, atol=1e-7)
+    # bf16 storage widens exactly
+    ab = _rng(83).integers(0x3000, 0x4000, size=(rows, n)).astype(np.uint16)
+    W2b = _rng(84).integers(0x3000, 0x3c00, size=(E, n, d)).astype(np.uint16)
+    np.testing.assert_array_equal(oracle.expert_down(ab, re, W2b),
+                                  oracle.expert_down(oracle.bf16_to_f32(ab), re, oracle.bf16_to_f32(W2b)))
