@@ -183,17 +183,22 @@ MOE_DEV bf16x4 lds_read_tr(const char* l) {
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel with a 4-stage LDS pipeline (used when d % 256 == 0 and
-// n % 128 == 0).  Same tiles as above (256 x 256 per CU, 4 waves of 128 x 128)
-// but K advances 32 at a time through four 32 KB LDS stages:
+// n % 128 == 0).  Tiles of 256 x 256 per CU, 4 waves of 128 x 128, K advancing
+// 32 at a time through four 32 KB LDS stages:
 //  * DMA is buffer_load ... lds: one scalar buffer resource per matrix, a
 //    fixed 32-bit per-lane offset per tile and a scalar offset per K-step, so
-//    issuing a load costs no vector ALU work.  The load for K-step kt+3 is
-//    issued during K-step kt, about 2.5 K-steps (~2.5k MFMA cycles) ahead of use.
+//    issuing a load costs no vector ALU work.
+//  * One barrier per K-step, at its start: it publishes step kt+1's stage
+//    (every wave first waits for its own part of that DMA) and retires the
+//    stage of step kt-1 (every read of it completed before the barrier), which
+//    is then refilled with step kt+3 -- two K-steps of lead time.
+//  * The K-loop has no branches: near the end of K the refill index is clamped
+//    to the last step (a duplicate load into a stage nobody reads again), so
+//    the schedule below can be pinned with scheduling fences.  The 8 DMAs of a
+//    step go out one per MFMA right after the barrier; the fragment reads of
+//    the next sub-step run under the current sub-step's 16 MFMAs.
 //  * Each 32-row B stage is stored as two 128-column halves so that every DMA
 //    instruction reads a single matrix (W1 or W3 for the SwiGLU GEMM).
-//  * Fragment reads use precomputed per-lane LDS addresses with immediate
-//    offsets; the next sub-step's fragments are read while the current
-//    sub-step's 16 MFMAs run; one barrier per K-step.
 // ---------------------------------------------------------------------------
 constexpr int kP4BK = 32, kP4Stage = 32768, kP4Lds = 4 * kP4Stage;
 
@@ -211,14 +216,14 @@ MOE_DEV rsrc_t make_rsrc(const void* base) {
     return r;
 }
 
-// 16 bytes per lane from global memory straight into LDS at M0 + 16*lane.
-// Issued through inline assembly on purpose: the compiler cannot tell which
-// LDS bytes an LDS-DMA writes, so for the builtin it waits for every
-// outstanding load before the next LDS read -- which would drain the whole
-// prefetch pipeline each K-step.  The kernel orders the DMA itself with
-// explicit vmcnt waits and barriers.
-MOE_DEV void dma16(const rsrc_t& r, char* lds, uint32_t voff, uint32_t soff) {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds;
+// 16 bytes per lane from global memory straight into LDS at m0 + 16*lane
+// (m0 is an LDS byte address).  Issued through inline assembly on purpose: the
+// compiler cannot tell which LDS bytes an LDS-DMA writes, so for the builtin it
+// waits for every outstanding load before the next LDS read -- which would
+// drain the whole prefetch pipeline each K-step.  The kernel orders the DMA
+// itself with explicit vmcnt waits and barriers.  The s_nop covers the wait
+// state required between writing M0 and an LDS-DMA that reads it.
+MOE_DEV void dma16(const rsrc_t& r, uint32_t m0, uint32_t voff, uint32_t soff) {
     __asm__ volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
@@ -267,6 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
         b_rd[ni] = b_lane + half * 8192 + ((((nn >> 3) ^ b_x) + b_c) << 4);
     }
 
+    const uint32_t lds_base = uniform((int)(uint32_t)(uintptr_t)(lds_void*)smem);
     const int G = gridDim.x;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int per_xcd = G >> 3;
@@ -303,15 +309,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
         }
         const uint32_t b_step = (uint32_t)kP4BK * (uint32_t)N * 2u;
         const int KT = Kd / kP4BK;
+        // DMA number i (0..7) of K-step kt into `stage`: i < 4 are A, the rest B.
+        auto issue_one = [&](int kt, int stage, int i) {
+            const uint32_t dst = lds_base + stage * kP4Stage + (wave * 4) * 1024;
+            if (i < 4) dma16(ra, dst + i * 1024, a_vo[i], (uint32_t)kt * (kP4BK * 2));
+            else dma16(rb, dst + 16384 + (i - 4) * 1024, b_vo[i - 4], (uint32_t)kt * b_step);
+        };
         auto issue = [&](int kt, int stage) {
-            char* sa = smem + stage * kP4Stage + (wave * 4) * 1024;
-            char* sb = smem + stage * kP4Stage + 16384 + (wave * 4) * 1024;
-            const uint32_t sa_off = (uint32_t)kt * (kP4BK * 2);
-            const uint32_t sb_off = (uint32_t)kt * b_step;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dma16(ra, sa + i * 1024, a_vo[i], sa_off);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dma16(rb, sb + i * 1024, b_vo[i], sb_off);
+            for (int i = 0; i < 8; ++i) issue_one(kt, stage, i);
         };
 
         f32x16 acc[4][4];
@@ -343,13 +349,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
             }
         };
 
-        // Prologue: K-steps 0..2 in flight, wait for step 0.
+        // Prologue (KT is a multiple of 4 here): K-steps 0..2 in flight, wait for step 0.
         issue(0, 0);
-        if (KT > 1) issue(1, 1);
-        if (KT > 2) issue(2, 2);
-        if (KT > 2) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else if (KT > 1) __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        issue(1, 1);
+        issue(2, 2);
+        __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
         __syncthreads();
         load_frags(0, 0, 0);
 
@@ -357,32 +361,45 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int kt = kt0 + u;
-                // sub-step 0: fragments of ks=1 stream in behind the 16 MFMAs of ks=0
+                // Step boundary: own DMA of step kt+1 done (8 younger ones may fly).
+                __builtin_amdgcn_sched_barrier(0);
+                __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                __syncthreads();
+                // Refill the stage of step kt-1 with step kt+3, one DMA per MFMA.
+                const int kn = min(kt + 3, KT - 1);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    issue_one(kn, (u + 3) & 3, i);
+                    mfma(0, i, i + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // Rest of sub-step 0 while sub-step 1's fragments are read.
                 load_frags(u, 1, 1);
-                mfma(0, 0, 16);
+                mfma(0, 8, 16);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // Sub-step 1 while the next step's sub-step-0 fragments are read.
+                load_frags((u + 1) & 3, 0, 0);
+                mfma(1, 0, 16);
 #pragma unroll
                 for (int i = 0; i < 12; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-                // sub-step 1: half the MFMAs, then wait for step kt+1 and sync,
-                // refill the stage of step kt-1 with step kt+3, read step kt+1's ks=0.
-                mfma(1, 0, 8);
-                if (kt + 2 < KT) __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
-                else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                __syncthreads();
-                if (kt + 3 < KT) issue(kt + 3, (u + 3) & 3);
-                if (kt + 1 < KT) load_frags((u + 1) & 3, 0, 0);
-                mfma(1, 8, 16);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                }
             }
         }
+        // The clamped refills of the last steps are still in flight.
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
