@@ -182,16 +182,17 @@ MOE_DEV bf16x4 lds_read_tr(const char* l) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel with a 4-stage LDS pipeline (used when d % 256 == 0 and
+// bf16 MFMA kernel with a 5-stage LDS pipeline (used when d % 256 == 0 and
 // n % 128 == 0).  Tiles of 256 x 256 per CU, 4 waves of 128 x 128, K advancing
-// 32 at a time through four 32 KB LDS stages:
+// 32 at a time through five 32 KB LDS stages (all 160 KB of a CU's LDS; the
+// tile schedule lives in registers):
 //  * DMA is buffer_load ... lds: one scalar buffer resource per matrix, a
 //    fixed 32-bit per-lane offset per tile and a scalar offset per K-step, so
 //    issuing a load costs no vector ALU work.
 //  * One barrier per K-step, at its start: it publishes step kt+1's stage
 //    (every wave first waits for its own part of that DMA) and retires the
 //    stage of step kt-1 (every read of it completed before the barrier), which
-//    is then refilled with step kt+3 -- two K-steps of lead time.
+//    is then refilled with step kt+4 -- three K-steps of lead time.
 //  * The K-loop has no branches: near the end of K the refill index is clamped
 //    to the last step (a duplicate load into a stage nobody reads again), so
 //    the schedule below can be pinned with scheduling fences.  The 8 DMAs of a
@@ -200,7 +201,7 @@ MOE_DEV bf16x4 lds_read_tr(const char* l) {
 //  * Each 32-row B stage is stored as two 128-column halves so that every DMA
 //    instruction reads a single matrix (W1 or W3 for the SwiGLU GEMM).
 // ---------------------------------------------------------------------------
-constexpr int kP4BK = 32, kP4Stage = 32768, kP4Lds = 4 * kP4Stage;
+constexpr int kP4BK = 32, kP4Stage = 32768, kP4Stages = 5, kP4Lds = kP4Stages * kP4Stage;
 
 // Raw buffer resource (4 scalar dwords): 48-bit base, stride 0, num_records,
 // and the gfx9 dword-3 format word.
@@ -233,19 +234,51 @@ MOE_DEV void dma16(const rsrc_t& r, uint32_t m0, uint32_t voff, uint32_t soff) {
         : "memory", "m0");
 }
 
+// The tile schedule of the pipelined kernel, held in registers (E <= 256): lane
+// l holds experts 4l..4l+3, and expert e owns the tiles [start_e, start_e +
+// ceil(count_e / 256) * NT) in expert order.  Returns the expert owning `tile`
+// (-1 if none) and writes its first tile to *start and the number of tiles to
+// *total.  All lanes of the wave must call it.
+MOE_DEV int sched_lookup(const int32_t* __restrict__ counts, int E, int NT, int rows, int lane, int tile,
+                         int* start, int* total) {
+    int v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane * 4 + j;
+        const int c = e < E ? min(max(counts[e], 0), rows) : 0;
+        v[j] = ((c + kBM256 - 1) / kBM256) * NT;
+    }
+    const int p0 = v[0], p1 = p0 + v[1], p2 = p1 + v[2], p3 = p2 + v[3];
+    int x = p3;  // inclusive scan of the per-lane totals
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+    }
+    const int base = x - p3;
+    *total = __shfl(x, kWave - 1, kWave);
+    const int b0 = base, b1 = base + p0, b2 = base + p1, b3 = base + p2, b4 = base + p3;
+    int hit = -1, st = 0;
+    if (tile >= b0 && tile < b1) { hit = 0; st = b0; }
+    if (tile >= b1 && tile < b2) { hit = 1; st = b1; }
+    if (tile >= b2 && tile < b3) { hit = 2; st = b2; }
+    if (tile >= b3 && tile < b4) { hit = 3; st = b3; }
+    const unsigned long long m = __ballot(hit >= 0);
+    if (m == 0ull) return -1;
+    const int src = __builtin_ctzll(m);
+    *start = __shfl(st, src, kWave);
+    return src * 4 + __shfl(hit, src, kWave);
+}
+
 template <bool DUAL>
 __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     int E, int Kd, int N, int rows) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    __shared__ int s_start[257];
-    __shared__ int s_tmp[256];
 
     constexpr int OUTW = DUAL ? 128 : 256;
     const int NT = N / OUTW;
-    build_schedule<kBM256>(counts, E, NT, rows, s_start, s_tmp);
-    const int total = s_start[E];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -253,8 +286,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, lh = lane >> 5;
     const int g16 = lane >> 4, s16 = lane & 15;
+    int total = 0, first = 0;
+    sched_lookup(counts, E, NT, rows, lane, -1, &first, &total);
+    total = uniform(total);
 
-    // LDS fragment addresses (byte offsets into a stage; stages 2-3 use +64 KB).
+    // LDS fragment addresses (byte offsets into a stage).
     // A row r, k-chunk c of 8 elements sits at r*64 + ((c ^ ((r/4)%4)) * 16).
     const int arow = wm * 128 + l32;
     int a_rd[2];
@@ -279,10 +315,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     for (int round = 0;; ++round) {
         const int tile = round * G + xcd * per_xcd + slot;
         if (tile >= total) break;
-        const int e = uniform(find_expert(s_start, E, tile));
+        const int e = uniform(sched_lookup(counts, E, NT, rows, lane, tile, &first, &total));
+        if (e < 0) break;
         const int cnt = min(max(counts[e], 0), rows);
         const int mt = (cnt + kBM256 - 1) / kBM256;
-        const int local = tile - s_start[e];
+        const int local = tile - uniform(first);
         const int m_tile = local % mt;
         const int n_tile = local / mt;
         const int r0 = offsets[e] + m_tile * kBM256;
@@ -309,15 +346,16 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
         }
         const uint32_t b_step = (uint32_t)kP4BK * (uint32_t)N * 2u;
         const int KT = Kd / kP4BK;
-        // DMA number i (0..7) of K-step kt into `stage`: i < 4 are A, the rest B.
-        auto issue_one = [&](int kt, int stage, int i) {
-            const uint32_t dst = lds_base + stage * kP4Stage + (wave * 4) * 1024;
+        // DMA number i (0..7) of K-step kt into the stage at byte offset soff:
+        // i < 4 are A, the rest B.
+        auto issue_one = [&](int kt, int soff, int i) {
+            const uint32_t dst = lds_base + soff + (wave * 4) * 1024;
             if (i < 4) dma16(ra, dst + i * 1024, a_vo[i], (uint32_t)kt * (kP4BK * 2));
             else dma16(rb, dst + 16384 + (i - 4) * 1024, b_vo[i - 4], (uint32_t)kt * b_step);
         };
-        auto issue = [&](int kt, int stage) {
+        auto issue = [&](int kt, int soff) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) issue_one(kt, stage, i);
+            for (int i = 0; i < 8; ++i) issue_one(kt, soff, i);
         };
 
         f32x16 acc[4][4];
@@ -329,13 +367,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                 for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
 
         bf16x8 af[2][4], bfr[2][4];
-        auto load_frags = [&](int stage, int ks, int buf) {
-            const char* sa = smem + stage * kP4Stage + a_rd[ks];
+        auto load_frags = [&](int soff, int ks, int buf) {
+            const char* sa = smem + soff + a_rd[ks];
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * 64);
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) {
-                const char* pb = smem + stage * kP4Stage + b_rd[ni] + ks * 16 * 256;
+                const char* pb = smem + soff + b_rd[ni] + ks * 16 * 256;
                 const bf16x4 h0 = lds_read_tr(pb);
                 const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
                 bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -349,32 +387,36 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
             }
         };
 
-        // Prologue (KT is a multiple of 4 here): K-steps 0..2 in flight, wait for step 0.
+        // Prologue (KT is a multiple of 4 here): K-steps 0..3 in flight, wait for step 0.
         issue(0, 0);
-        issue(1, 1);
-        issue(2, 2);
-        __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        issue(1, kP4Stage);
+        issue(2, 2 * kP4Stage);
+        issue(3, 3 * kP4Stage);
+        __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
         __syncthreads();
         load_frags(0, 0, 0);
 
+        int s_cur = 0;  // byte offset of step kt's stage
         for (int kt0 = 0; kt0 < KT; kt0 += 4) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int kt = kt0 + u;
-                // Step boundary: own DMA of step kt+1 done (8 younger ones may fly).
+                const int s_nxt = s_cur == (kP4Stages - 1) * kP4Stage ? 0 : s_cur + kP4Stage;
+                const int s_old = s_cur == 0 ? (kP4Stages - 1) * kP4Stage : s_cur - kP4Stage;
+                // Step boundary: own DMA of step kt+1 done (16 younger ones may fly).
                 __builtin_amdgcn_sched_barrier(0);
-                __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
                 __syncthreads();
-                // Refill the stage of step kt-1 with step kt+3, one DMA per MFMA.
-                const int kn = min(kt + 3, KT - 1);
+                // Refill the stage of step kt-1 with step kt+4, one DMA per MFMA.
+                const int kn = min(kt + 4, KT - 1);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    issue_one(kn, (u + 3) & 3, i);
+                    issue_one(kn, s_old, i);
                     mfma(0, i, i + 1);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 // Rest of sub-step 0 while sub-step 1's fragments are read.
-                load_frags(u, 1, 1);
+                load_frags(s_cur, 1, 1);
                 mfma(0, 8, 16);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -388,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 // Sub-step 1 while the next step's sub-step-0 fragments are read.
-                load_frags((u + 1) & 3, 0, 0);
+                load_frags(s_nxt, 0, 0);
                 mfma(1, 0, 16);
 #pragma unroll
                 for (int i = 0; i < 12; ++i) {
@@ -396,6 +438,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                s_cur = s_nxt;
             }
         }
         // The clamped refills of the last steps are still in flight.
