@@ -47,4 +47,38 @@ MOE_DEV float group_sum(float x) {
 
 MOE_DEV int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Raw buffer resource (4 scalar dwords): 48-bit base, stride 0, num_records
+// (loads at byte offsets past it return zeros), and the gfx9 dword-3 format word.
+typedef int32_t rsrc_t __attribute__((ext_vector_type(4)));
+
+MOE_DEV rsrc_t make_rsrc(const void* base, uint32_t num_records = 0x7fffffffu) {
+    const uint64_t a = (uint64_t)base;
+    rsrc_t r;
+    r[0] = uniform((int)(uint32_t)a);
+    r[1] = uniform((int)(uint32_t)(a >> 32) & 0xffff);
+    r[2] = uniform((int)num_records);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16*lane
+// (m0 is an LDS byte address).  Issued through inline assembly on purpose: the
+// compiler cannot tell which LDS bytes an LDS-DMA writes, so for the builtin it
+// waits for every outstanding load before the next LDS read -- which would
+// drain the whole prefetch pipeline each K-step.  The kernel orders the DMA
+// itself with explicit vmcnt waits and barriers.  The s_nop covers the wait
+// state required between writing M0 and an LDS-DMA that reads it.
+MOE_DEV void dma16(const rsrc_t& r, uint32_t m0, uint32_t voff, uint32_t soff) {
+    __asm__ volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(uniform((int)m0)), "v"(voff), "s"(r), "s"(uniform((int)soff))
+        : "memory", "m0");
+}
+
+
 }  // namespace moe

@@ -168,7 +168,6 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_bf16_kernel(
 
 constexpr int kBM256 = 256;  // rows per tile of the pipelined kernel
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4 of the
@@ -202,37 +201,6 @@ MOE_DEV bf16x4 lds_read_tr(const char* l) {
 //    instruction reads a single matrix (W1 or W3 for the SwiGLU GEMM).
 // ---------------------------------------------------------------------------
 constexpr int kP4BK = 32, kP4Stage = 32768, kP4Stages = 5, kP4Lds = kP4Stages * kP4Stage;
-
-// Raw buffer resource (4 scalar dwords): 48-bit base, stride 0, num_records,
-// and the gfx9 dword-3 format word.
-typedef int32_t rsrc_t __attribute__((ext_vector_type(4)));
-
-MOE_DEV rsrc_t make_rsrc(const void* base) {
-    const uint64_t a = (uint64_t)base;
-    rsrc_t r;
-    r[0] = uniform((int)(uint32_t)a);
-    r[1] = uniform((int)(uint32_t)(a >> 32) & 0xffff);
-    r[2] = 0x7fffffff;
-    r[3] = 0x00020000;
-    return r;
-}
-
-// 16 bytes per lane from global memory straight into LDS at m0 + 16*lane
-// (m0 is an LDS byte address).  Issued through inline assembly on purpose: the
-// compiler cannot tell which LDS bytes an LDS-DMA writes, so for the builtin it
-// waits for every outstanding load before the next LDS read -- which would
-// drain the whole prefetch pipeline each K-step.  The kernel orders the DMA
-// itself with explicit vmcnt waits and barriers.  The s_nop covers the wait
-// state required between writing M0 and an LDS-DMA that reads it.
-MOE_DEV void dma16(const rsrc_t& r, uint32_t m0, uint32_t voff, uint32_t soff) {
-    __asm__ volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds"
-        :
-        : "s"(uniform((int)m0)), "v"(voff), "s"(r), "s"(uniform((int)soff))
-        : "memory", "m0");
-}
 
 // The tile schedule of the pipelined kernel, held in registers (E <= 256): lane
 // l holds experts 4l..4l+3, and expert e owns the tiles [start_e, start_e +

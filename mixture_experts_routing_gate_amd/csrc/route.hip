@@ -34,13 +34,25 @@ namespace {
 // share the upper 32-IB bits.  The fast result is therefore accepted only if
 // no two of the K chosen keys share that prefix and exactly one key of the
 // whole row has the prefix of the K-th chosen key; otherwise (exact ties,
-// near-ties) the row is redone by the exact path: K rounds of a group-wide
-// argmax on the fp32 logits, largest first, lower index among equal values.
+// near-ties) the row is listed and, after the main loop, redone by the exact
+// path: one wave per row, K rounds of a wave-wide argmax on the fp32 logits,
+// largest first, lower index among equal values.
 //
 // Weights use the exact logits of the chosen experts (re-read from cache):
 // w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0), the softmax renormalised over
 // the K chosen experts.
+//
+// Staging (E % 4 == 0).  Each wave owns an LDS region for the RPW rows of its
+// pass.  The rows of the wave's next pass are copied into it by LDS-DMA as
+// soon as the current ones have been read into registers, so the HBM reads of
+// one pass overlap the selection work of the previous one.  The copy is
+// 16-byte chunks, XOR-swizzled within each 1 KB so that the per-lane reads
+// (lanes 128 bytes apart) spread over the LDS banks; rows past the chunk read
+// as zeros (buffer bounds) and are discarded.
 // ---------------------------------------------------------------------------
+
+// Largest token chunk of one gate workgroup (chunk_tokens() never exceeds it).
+constexpr int kMaxChunk = 1024;
 
 MOE_DEV void cswap_desc(uint32_t& a, uint32_t& b) {
     const uint32_t hi = max(a, b), lo = min(a, b);
@@ -98,67 +110,76 @@ MOE_DEV uint32_t ord_key(float x) {
     return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
-// Exact selection for the rows of one wave whose fast result was rejected
-// (`mine`): K rounds of a group-wide argmax on the fp32 logits, largest first,
-// lower expert index among equal values (-0.0 == +0.0).  All lanes of the wave
-// take part in the cross-lane reductions; only `mine` lanes write.
-template <int V, int G>
-__device__ __attribute__((noinline)) void gate_exact_rows(const float* lrow, bool mine, int t, int E, int K, int g,
-                                                          int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_w, int* hist) {
-    float v[V];
+// (v, i) <- the better of (v, i) and (ov, oi): larger value, then lower index.
+MOE_DEV void argmax_take(float& v, int& i, float ov, int oi) {
+    const bool take = (ov > v) | ((ov == v) & (oi < i));
+    v = take ? ov : v;
+    i = take ? oi : i;
+}
+template <int CTRL, int ROW_MASK>
+MOE_DEV void argmax_dpp(float& v, int& i) {
+    const int vb = __builtin_bit_cast(int, v);
+    const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(vb, vb, CTRL, ROW_MASK, 0xF, false));
+    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xF, false);
+    argmax_take(v, i, ov, oi);
+}
+// Wave-wide argmax, returned wave-uniform: quads, half rows, rows (xor 1, xor 2,
+// half-row and row mirrors), then rows 0-1 into row 1 and rows 0-3 into row 3
+// (row broadcasts of lanes 15 and 31); lane 63 ends with the whole wave.
+MOE_DEV void wave_argmax(float& v, int& i) {
+    argmax_dpp<0xB1, 0xF>(v, i);
+    argmax_dpp<0x4E, 0xF>(v, i);
+    argmax_dpp<0x141, 0xF>(v, i);
+    argmax_dpp<0x140, 0xF>(v, i);
+    argmax_dpp<0x142, 0xA>(v, i);
+    argmax_dpp<0x143, 0xC>(v, i);
+    v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
+    i = __builtin_amdgcn_readlane(i, kWave - 1);
+}
+MOE_DEV float wave_sum(float x) {
+    x += dpp_partner_f<0>(x);
+    x += dpp_partner_f<1>(x);
+    x += dpp_partner_f<2>(x);
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xC, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), kWave - 1));
+}
+
+// Exact selection of one row by a whole wave (the row index is wave-uniform):
+// lane l holds experts l + 64*j (j < 4, E <= 256).  K rounds of a wave-wide
+// argmax on the fp32 logits, largest first, lower expert index among equal
+// values (-0.0 == +0.0); lane r keeps slot r.
+MOE_DEV void gate_exact_row(const float* __restrict__ lrow, int t, int E, int K, int lane,
+                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int* hist) {
+    float v[4];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-        const int e = g * V + j;
-        const float x = lrow[e < E ? e : 0] + 0.0f;
-        v[j] = (mine && e < E) ? x : -INFINITY;
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane + kWave * j;
+        v[j] = e < E ? lrow[e] + 0.0f : -INFINITY;
     }
-    float sv[8];
-    int si[8];
+    float mine_v = 0.0f, first_v = 0.0f;
+    int mine_i = 0;
+    for (int r = 0; r < K; ++r) {
+        float bv = v[0];
+        int bi = lane;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        sv[r] = 0.0f;
-        si[r] = 0;
-        if (r < K) {
-            float bv = v[0];
-            int bj = 0;
+        for (int j = 1; j < 4; ++j) argmax_take(bv, bi, v[j], lane + kWave * j);
+        wave_argmax(bv, bi);
+        const bool owner = (bi & (kWave - 1)) == lane;
 #pragma unroll
-            for (int j = 1; j < V; ++j)
-                if (v[j] > bv) {
-                    bv = v[j];
-                    bj = j;
-                }
-            const float M = group_max<G>(bv);
-            const int cand = (bv == M) ? g * V + bj : 0x7fffffff;
-            const int I = group_min<G>(cand);
-#pragma unroll
-            for (int j = 0; j < V; ++j)
-                if (g * V + j == I) v[j] = -INFINITY;
-            sv[r] = M;
-            si[r] = I;
-        }
+        for (int j = 0; j < 4; ++j) v[j] = (owner && j == bi / kWave) ? -INFINITY : v[j];
+        mine_v = lane == r ? bv : mine_v;
+        mine_i = lane == r ? bi : mine_i;
+        if (r == 0) first_v = bv;
     }
-    float exs[8];
-    float ps = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        exs[r] = 0.0f;
-        if (r < K && (r % G) == g) {
-            exs[r] = expf(sv[r] - sv[0]);
-            ps += exs[r];
-        }
-    }
-    const float S2 = group_sum<G>(ps);
-    if (mine) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            if (r < K && (r % G) == g) {
-                topk_idx[(size_t)t * K + r] = si[r];
-                topk_w[(size_t)t * K + r] = exs[r] / S2;
-                // only non-finite logits (outside the contract) leave si out of range
-                if ((unsigned)si[r] < (unsigned)E) atomicAdd(&hist[si[r]], 1);
-            }
-        }
+    const float ex = lane < K ? expf(mine_v - first_v) : 0.0f;
+    const float S = wave_sum(ex);
+    if (lane < K) {
+        topk_idx[(size_t)t * K + lane] = mine_i;
+        topk_w[(size_t)t * K + lane] = ex / S;
+        // only non-finite logits (outside the contract) leave mine_i out of range
+        if ((unsigned)mine_i < (unsigned)E) atomicAdd(&hist[mine_i], 1);
     }
 }
 
@@ -173,7 +194,17 @@ __global__ __launch_bounds__(THREADS) void gate_kernel(const float* __restrict__
     constexpr uint32_t IMASK = (1u << IB) - 1u;
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
     static_assert(V % KP == 0 && V % 4 == 0, "lane width");
+    constexpr int NWAVE = THREADS / kWave;
+    constexpr int REG = RPW * EP * 4;              // bytes of one staged pass of a wave
+    static_assert(REG % 1024 == 0, "staging region");
+    // two regions per wave (the next pass lands while this one is used) when
+    // they fit in 128 KB, else one (refilled once this pass's reads are done)
+    constexpr int NBUF = NWAVE * 2 * REG <= 128 * 1024 ? 2 : 1;
+    constexpr int SPL = (KP + G - 1) / G;          // output slots per lane: r = g + G*i
     __shared__ int hist[256];
+    __shared__ __attribute__((aligned(1024))) char stage[VEC ? NWAVE * NBUF * REG : 16];
+    __shared__ int flagged[kMaxChunk];  // rows left to the exact path
+    __shared__ int n_flagged;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -181,29 +212,86 @@ __global__ __launch_bounds__(THREADS) void gate_kernel(const float* __restrict__
     const int g = lane % G;
     const int rw = lane / G;
     for (int e = tid; e < E; e += THREADS) hist[e] = 0;
+    if (tid == 0) n_flagged = 0;
     __syncthreads();
 
     const int chunk = blockIdx.x;
     const int t0 = chunk * CH;
     const int t1 = min(T, t0 + CH);
-    for (int base = t0 + wave * RPW; base < t1; base += RPB) {
+
+    // Staging copy (E % 4 == 0) of the RPW rows starting at row pb into region
+    // `buf` of this wave.  The buffer's range is the chunk, so rows past it read
+    // as zeros.
+    char* const wstage = stage + wave * NBUF * REG;
+    const uint32_t wstage_lds = (uint32_t)(uintptr_t)(lds_void*)wstage;
+    const rsrc_t rsrc = make_rsrc(logits + (size_t)t0 * E, (uint32_t)(t1 - t0) * (uint32_t)E * 4u);
+    const uint32_t lane_src = 16u * (uint32_t)(lane ^ ((lane >> 3) & 7));
+    const int ndma = PAD ? (RPW * E * 4 + 1023) >> 10 : REG / 1024;  // 1 KB copies per pass
+    auto stage_rows = [&](int pb, int buf) {
+        const uint32_t roff = (uint32_t)(pb - t0) * (uint32_t)E * 4u;
+#pragma unroll
+        for (int i = 0; i < REG / 1024; ++i)
+            if (i < ndma) dma16(rsrc, wstage_lds + buf * REG + i * 1024, roff + i * 1024 + lane_src, 0u);
+    };
+    // float f of the wave's staged rows in region `buf` (16-byte chunks swizzled)
+    auto staged_chunk = [&](int buf, int c) -> const char* {
+        return wstage + buf * REG + ((c ^ ((c >> 3) & 7)) << 4);
+    };
+    if constexpr (VEC) stage_rows(t0 + wave * RPW, 0);
+
+    // Outputs go through buffer stores over the chunk's slice of topk_idx and
+    // topk_w; a lane with nothing to store writes past the range, which drops
+    // the store.  With staging, a pass's outputs are stored early in the next
+    // pass (right after its wait for the staged rows), so that the wait never
+    // has to cover stores issued just before it.
+    const __amdgpu_buffer_rsrc_t out_idx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(topk_idx + (size_t)t0 * K), (short)0, (t1 - t0) * K * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t out_w = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(topk_w + (size_t)t0 * K), (short)0, (t1 - t0) * K * 4, 0x00020000);
+    constexpr uint32_t kDrop = 0x80000000u;  // an offset past any chunk's outputs
+    uint32_t pend_off[SPL], pend_idx[SPL], pend_w[SPL];  // outputs not stored yet
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+        pend_off[i] = kDrop;
+        pend_idx[i] = 0u;
+        pend_w[i] = 0u;
+    }
+    auto store_pending = [&]() {
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            __builtin_amdgcn_raw_buffer_store_b32(pend_idx[i], out_idx, pend_off[i], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(pend_w[i], out_w, pend_off[i], 0, 0);
+        }
+    };
+
+    int pass = 0;
+    for (int base = t0 + wave * RPW; base < t1; base += RPB, ++pass) {
         const int t = base + rw;
         const bool valid = t < t1;
+        const int buf = NBUF == 2 ? (pass & 1) : 0;
         // ---- keys ----
-        // Loads are unconditional (row and column clamped into the tensor) so
-        // that all of a lane's loads are in flight together; padding columns
-        // get key 0 (below every logit).  Rows past the chunk are computed and
-        // discarded: nothing of theirs is stored or counted.
+        // Padding columns get key 0 (below every logit).  Rows past the chunk
+        // are computed and discarded: nothing of theirs is stored or counted.
         const float* lrow = logits + (size_t)min(t, T - 1) * E;
         // index bits IMASK - e; V is a power of two, so IMASK - g*V - j == (IMASK - g*V) ^ j
         const uint32_t ibase = IMASK - (uint32_t)(g * V);
         uint32_t key[V];
         if constexpr (VEC) {
+            // this pass's rows have landed; with two regions, the next pass's
+            // copy goes into the other one, whose reads all completed in the
+            // previous pass; then the previous pass's outputs are stored
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if constexpr (NBUF == 2) {
+                __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                stage_rows(base + RPB, buf ^ 1);
+            }
+            store_pending();
             f32x4 x[V / 4];
 #pragma unroll
             for (int q = 0; q < V / 4; ++q) {
                 const int e0 = g * V + q * 4;
-                x[q] = *reinterpret_cast<const f32x4*>(lrow + (e0 < E ? e0 : 0));
+                const int c = (rw * E + (e0 < E ? e0 : 0)) >> 2;  // 16-byte chunk in the region
+                x[q] = *reinterpret_cast<const f32x4*>(staged_chunk(buf, c));
             }
 #pragma unroll
             for (int q = 0; q < V / 4; ++q) {
@@ -215,6 +303,7 @@ __global__ __launch_bounds__(THREADS) void gate_kernel(const float* __restrict__
                 }
             }
         } else {
+            // loads are unconditional (column clamped) so that they are all in flight together
             float x[V];
 #pragma unroll
             for (int j = 0; j < V; ++j) {
@@ -284,8 +373,7 @@ __global__ __launch_bounds__(THREADS) void gate_kernel(const float* __restrict__
         // ---- weights and outputs of accepted rows ----
         // Lane g of the group owns slots r = g + G*i.  Its slot keys are picked
         // from the group-uniform list with a static select chain (no divergent
-        // branches), and the exact logits of all its slots are loaded together.
-        constexpr int SPL = (KP + G - 1) / G;  // slots per lane
+        // branches), and the exact logits of its slots are read together.
         uint32_t mk[SPL];
 #pragma unroll
         for (int i = 0; i < SPL; ++i) {
@@ -299,9 +387,25 @@ __global__ __launch_bounds__(THREADS) void gate_kernel(const float* __restrict__
         float xr[SPL];
 #pragma unroll
         for (int i = 0; i < SPL; ++i) er[i] = min((int)(IMASK - (mk[i] & IMASK)), E - 1);
-        const float l0 = lrow[e0];
+        float l0;
+        if constexpr (VEC) {
+            auto staged = [&](int e) {
+                const int f = rw * E + e;  // float index in the region
+                return *reinterpret_cast<const float*>(staged_chunk(buf, f >> 2) + ((f & 3) << 2));
+            };
+            l0 = staged(e0);
 #pragma unroll
-        for (int i = 0; i < SPL; ++i) xr[i] = lrow[er[i]];
+            for (int i = 0; i < SPL; ++i) xr[i] = staged(er[i]);
+            if constexpr (NBUF == 1) {
+                // the region is free once these reads are done: refill it
+                __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (base + RPB < t1) stage_rows(base + RPB, 0);
+            }
+        } else {
+            l0 = lrow[e0];
+#pragma unroll
+            for (int i = 0; i < SPL; ++i) xr[i] = lrow[er[i]];
+        }
         float ex[SPL];
         float part = 0.0f;
 #pragma unroll
@@ -314,21 +418,42 @@ __global__ __launch_bounds__(THREADS) void gate_kernel(const float* __restrict__
         if constexpr (G >= 2) S += dpp_partner_f<0>(S);
         if constexpr (G >= 4) S += dpp_partner_f<1>(S);
         if constexpr (G >= 8) S += dpp_partner_f<2>(S);
-        if (valid && exact_fast) {
+        const float rS = __builtin_amdgcn_rcpf(S);
 #pragma unroll
-            for (int i = 0; i < SPL; ++i) {
-                const int r = g + G * i;
-                if (r < K) {
-                    topk_idx[(size_t)t * K + r] = er[i];
-                    topk_w[(size_t)t * K + r] = ex[i] / S;
-                    atomicAdd(&hist[er[i]], 1);
-                }
-            }
+        for (int i = 0; i < SPL; ++i) {
+            const int r = g + G * i;
+            const bool st = valid && exact_fast && r < K;
+            pend_off[i] = st ? (uint32_t)((t - t0) * K + r) * 4u : kDrop;
+            pend_idx[i] = (uint32_t)er[i];
+            pend_w[i] = __float_as_uint(ex[i] * rS);
+            if (st) atomicAdd(&hist[er[i]], 1);
+        }
+        if constexpr (!VEC) {
+            store_pending();
+#pragma unroll
+            for (int i = 0; i < SPL; ++i) pend_off[i] = kDrop;
         }
 
-        // ---- exact path for rows with (near-)ties ----
-        if (__builtin_amdgcn_ballot_w64(valid && !exact_fast) != 0)
-            gate_exact_rows<V, G>(lrow, valid && !exact_fast, t, E, K, g, topk_idx, topk_w, hist);
+        // ---- rows with (near-)ties: listed for the exact path after the loop ----
+        const bool flag = valid && !exact_fast && g == 0;
+        if (__builtin_amdgcn_ballot_w64(flag) != 0) {
+            if (flag) flagged[atomicAdd(&n_flagged, 1)] = t;
+        }
+    }
+    // the last pass's outputs; a copy may still be in flight (the first one of
+    // a wave with no rows in this chunk, or with two regions the one past the
+    // wave's last pass)
+    if constexpr (VEC) {
+        store_pending();
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+
+    // ---- exact path: one wave per listed row ----
+    const int nf = n_flagged;
+    for (int i = wave; i < nf; i += NWAVE) {
+        const int tf = uniform(flagged[i]);
+        gate_exact_row(logits + (size_t)tf * E, tf, E, K, lane, topk_idx, topk_w, hist);
     }
     __syncthreads();
     for (int e = tid; e < E; e += THREADS) blk[(size_t)chunk * E + e] = hist[e];
