@@ -331,6 +331,9 @@ __global__ __launch_bounds__(THREADS) void gate_kernel(const float* __restrict__
             sort_desc<KP>(nxt);
             merge_top<KP>(top, nxt);
         }
+        uint32_t own[KP];  // the lane's own best KP keys, for the exactness check
+#pragma unroll
+        for (int i = 0; i < KP; ++i) own[i] = top[i];
         // ---- merge across the G lanes of the row ----
         if constexpr (G >= 2) {
             uint32_t o[KP];
@@ -359,16 +362,35 @@ __global__ __launch_bounds__(THREADS) void gate_kernel(const float* __restrict__
             if (i + 1 < KP && i + 1 < K) dup |= (top[i] >> IB) == (top[i + 1] >> IB);
             if (i == K - 1) kth = top[i];
         }
-        // keys whose prefix is >= the K-th key's prefix: exactly K unless some
-        // unchosen logit shares the K-th one's prefix (internal ones are in dup)
+        // No unchosen key may share the K-th key's prefix.  With several lanes
+        // per row: a lane's largest unchosen key is the largest of its own best
+        // KP below the K-th key, unless all of those were chosen ("full"); then
+        // the lane counts its keys whose prefix reaches the K-th one's, which
+        // must be exactly its KP chosen ones.  With one lane per row that count
+        // is the whole check (the lane's KP keys are the chosen ones).
         const uint32_t thr = kth & ~IMASK;
-        int same = 0;
+        auto count_reaching = [&]() {
+            int c = 0;
 #pragma unroll
-        for (int j = 0; j < V; ++j) same += (key[j] >= thr) ? 1 : 0;
-        if constexpr (G >= 2) same += (int)dpp_partner<0>((uint32_t)same);
-        if constexpr (G >= 4) same += (int)dpp_partner<1>((uint32_t)same);
-        if constexpr (G >= 8) same += (int)dpp_partner<2>((uint32_t)same);
-        const bool exact_fast = !dup && same == K;
+            for (int j = 0; j < V; ++j) c += (key[j] >= thr) ? 1 : 0;
+            return c;
+        };
+        bool exact_fast;
+        if constexpr (G == 1) {
+            exact_fast = !dup && count_reaching() == K;
+        } else {
+            uint32_t below = 0u;
+#pragma unroll
+            for (int i = 0; i < KP; ++i) below = max(below, own[i] < kth ? own[i] : 0u);
+            uint32_t extra = 0u;  // a full lane with an unchosen key at the K-th prefix
+            if (__builtin_amdgcn_ballot_w64(own[KP - 1] >= kth) != 0)
+                extra = (own[KP - 1] >= kth && count_reaching() > KP) ? 1u : 0u;
+            below = max(below, dpp_partner<0>(below));
+            extra |= dpp_partner<0>(extra);
+            if constexpr (G >= 4) { below = max(below, dpp_partner<1>(below)); extra |= dpp_partner<1>(extra); }
+            if constexpr (G >= 8) { below = max(below, dpp_partner<2>(below)); extra |= dpp_partner<2>(extra); }
+            exact_fast = !dup && extra == 0u && (below >> IB) != (kth >> IB);
+        }
 
         // ---- weights and outputs of accepted rows ----
         // Lane g of the group owns slots r = g + G*i.  Its slot keys are picked
@@ -464,6 +486,7 @@ __global__ __launch_bounds__(THREADS) void gate_kernel(const float* __restrict__
 // offsets[E] = total, and (if blkbase != nullptr) the placement base of every
 // chunk: blkbase[b,e] = offsets[e] + sum_{b' < b} blk[b',e].
 constexpr int kScanThreads = 1024;
+constexpr int kScanBatch = 32;
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ blk, int B,
                                                             int E, int32_t* __restrict__ counts,
@@ -479,17 +502,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
     const int b0 = act ? (int)(((long long)B * q) / Q) : 0;
     const int b1 = act ? (int)(((long long)B * (q + 1)) / Q) : 0;
     if (act) {
-        // batches of 8 independent loads keep the latency of the strided reads overlapped
+        // batches of 32 independent loads (rows clamped into the group's range)
+        // keep the latency of the strided reads overlapped
         int s = 0;
-        int b = b0;
-        for (; b + 8 <= b1; b += 8) {
-            int x[8];
+        for (int b = b0; b < b1; b += kScanBatch) {
+            int x[kScanBatch];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = blk[(size_t)(b + i) * E + e];
+            for (int i = 0; i < kScanBatch; ++i) x[i] = blk[(size_t)min(b + i, b1 - 1) * E + e];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) s += x[i];
+            for (int i = 0; i < kScanBatch; ++i) s += (b + i < b1) ? x[i] : 0;
         }
-        for (; b < b1; ++b) s += blk[(size_t)b * E + e];
         part[tid] = s;
     }
     __syncthreads();
@@ -524,20 +546,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
     }
     if (blkbase != nullptr && act) {
         int run = (e == 0 ? 0 : sc[cur][e - 1]) + part[q * E + e];
-        int b = b0;
-        for (; b + 8 <= b1; b += 8) {
-            int x[8];
+        for (int b = b0; b < b1; b += kScanBatch) {
+            int x[kScanBatch];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = blk[(size_t)(b + i) * E + e];
+            for (int i = 0; i < kScanBatch; ++i) x[i] = blk[(size_t)min(b + i, b1 - 1) * E + e];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                blkbase[(size_t)(b + i) * E + e] = run;
-                run += x[i];
+            for (int i = 0; i < kScanBatch; ++i) {
+                if (b + i < b1) {
+                    blkbase[(size_t)(b + i) * E + e] = run;
+                    run += x[i];
+                }
             }
-        }
-        for (; b < b1; ++b) {
-            blkbase[(size_t)b * E + e] = run;
-            run += blk[(size_t)b * E + e];
         }
     }
 }
