@@ -71,6 +71,9 @@ const char* moe_last_error(void);
 size_t moe_route_workspace_bytes(int T, int E, int K);
 size_t moe_permute_workspace_bytes(int T, int E, int K);
 size_t moe_forward_workspace_bytes(int T, int d, int E, int K, int n, int dtype);
+/* Optional workspace of moe_grouped_ffn / moe_ffn_up / moe_ffn_down on the
+ * current device (0 when the sizes take no split, e.g. fp32). */
+size_t moe_ffn_workspace_bytes(int d, int n, int dtype);
 
 /*
  * moe_route -- steps 1 and 2: fused softmax top-K gate, per-expert histogram
@@ -127,12 +130,19 @@ int moe_permute(const void* X, int dtype, int T, int d, int E, int K, const int3
  *   fp32 accumulation; Act and Y stored in dtype.
  * In:  Xp [T*K,d], W1 [E,d,n], W3 [E,d,n], W2 [E,n,d], counts [E],
  *      offsets [E+1].
- * Out: Act [T*K,n], Y [T*K,d].  No workspace: the ragged tile schedule is
- *      derived from counts on the device.
+ * Out: Act [T*K,n], Y [T*K,d].  The ragged tile schedule is derived from
+ *      counts on the device.
+ * Workspace (optional): NULL, or moe_ffn_workspace_bytes(d,n,dtype) bytes.
+ *      With it, the tiles of each GEMM's last, partial round are split along K
+ *      over the otherwise idle workgroups; the fp32 parts are added in a fixed
+ *      order, so results stay deterministic (they may differ from the unsplit
+ *      ones by fp32 rounding).  A non-NULL ws that is too small is
+ *      MOE_ERR_WORKSPACE.
  */
 int moe_grouped_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
                     int T, int d, int E, int K, int n, const int32_t* counts,
-                    const int32_t* offsets, void* Act, void* Y, void* stream);
+                    const int32_t* offsets, void* Act, void* Y, void* ws, size_t ws_bytes,
+                    void* stream);
 
 /*
  * moe_ffn_up -- step 4a alone: the SwiGLU GEMM of moe_grouped_ffn.
@@ -141,16 +151,18 @@ int moe_grouped_ffn(const void* Xp, const void* W1, const void* W3, const void* 
  * Arguments and layouts as for moe_grouped_ffn.  Out: Act [T*K,n].
  */
 int moe_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int T, int d, int E, int K,
-               int n, const int32_t* counts, const int32_t* offsets, void* Act, void* stream);
+               int n, const int32_t* counts, const int32_t* offsets, void* Act, void* ws,
+               size_t ws_bytes, void* stream);
 
 /*
  * moe_ffn_down -- step 4b alone: the down-projection GEMM of moe_grouped_ffn.
  *   Y[r] = Act[r] W2[e] for rows r of expert e ([P4] section 1 second layer).
  * In: Act [T*K,n] (dtype), W2 [E,n,d], counts [E], offsets [E+1].
- * Out: Y [T*K,d].
+ * Out: Y [T*K,d].  Workspace as for moe_grouped_ffn.
  */
 int moe_ffn_down(const void* Act, const void* W2, int dtype, int T, int d, int E, int K, int n,
-                 const int32_t* counts, const int32_t* offsets, void* Y, void* stream);
+                 const int32_t* counts, const int32_t* offsets, void* Y, void* ws, size_t ws_bytes,
+                 void* stream);
 
 /*
  * moe_combine -- step 5: gate-weighted combine back to token order ([P4]

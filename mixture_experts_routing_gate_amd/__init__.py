@@ -48,11 +48,12 @@ def load_library() -> ctypes.CDLL:
         "moe_route_workspace_bytes": ([I, I, I], Z),
         "moe_permute_workspace_bytes": ([I, I, I], Z),
         "moe_forward_workspace_bytes": ([I, I, I, I, I, I], Z),
+        "moe_ffn_workspace_bytes": ([I, I, I], Z),
         "moe_route": ([P, I, I, I, P, P, P, P, P, Z, P], I),
         "moe_permute": ([P, I, I, I, I, I, P, P, P, P, P, Z, P], I),
-        "moe_grouped_ffn": ([P, P, P, P, I, I, I, I, I, I, P, P, P, P, P], I),
-        "moe_ffn_up": ([P, P, P, I, I, I, I, I, I, P, P, P, P], I),
-        "moe_ffn_down": ([P, P, I, I, I, I, I, I, P, P, P, P], I),
+        "moe_grouped_ffn": ([P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
+        "moe_ffn_up": ([P, P, P, I, I, I, I, I, I, P, P, P, P, Z, P], I),
+        "moe_ffn_down": ([P, P, I, I, I, I, I, I, P, P, P, P, Z, P], I),
         "moe_combine": ([P, P, P, I, I, I, I, P, P], I),
         "moe_forward": ([P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P], I),
     }
@@ -136,9 +137,27 @@ def moe_permute(X: torch.Tensor, topk_idx: torch.Tensor, E: int):
     return sp, inv, Xp
 
 
+def ffn_workspace(d: int, n: int, dtype, device, split: bool = True, ws: torch.Tensor | None = None):
+    """(pointer, bytes) of the optional grouped-GEMM workspace: none when split
+    is off or the sizes take no split; `ws` (uint8 tensor) is used when given."""
+    if not split:
+        return None, 0
+    nbytes = load_library().moe_ffn_workspace_bytes(d, n, dtype_code(dtype))
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = _workspace(nbytes, device)
+    if ws.numel() < nbytes:
+        raise MoEError(MOE_ERR_WORKSPACE, "ffn workspace", f"needs {nbytes} bytes, got {ws.numel()}")
+    return ws.data_ptr(), nbytes
+
+
 def moe_grouped_ffn(Xp: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, W2: torch.Tensor,
-                    counts: torch.Tensor, offsets: torch.Tensor, K: int):
-    """Step 4.  Xp [T*K,d], W1/W3 [E,d,n], W2 [E,n,d] -> (Act [T*K,n], Y [T*K,d])."""
+                    counts: torch.Tensor, offsets: torch.Tensor, K: int, split: bool = True,
+                    ws: torch.Tensor | None = None):
+    """Step 4.  Xp [T*K,d], W1/W3 [E,d,n], W2 [E,n,d] -> (Act [T*K,n], Y [T*K,d]).
+    split: let the last partial round of tiles be split along K (workspace `ws`
+    or one allocated here)."""
     lib = load_library()
     A, d = Xp.shape
     E, _, n = W1.shape
@@ -146,37 +165,42 @@ def moe_grouped_ffn(Xp: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, W2: to
     dev = Xp.device
     Act = torch.empty((A, n), dtype=Xp.dtype, device=dev)
     Y = torch.empty((A, d), dtype=Xp.dtype, device=dev)
+    wp, wn = ffn_workspace(d, n, Xp.dtype, dev, split, ws)
     _check(lib.moe_grouped_ffn(_dev(Xp, "Xp"), _dev(W1, "W1", Xp.dtype), _dev(W3, "W3", Xp.dtype),
                                _dev(W2, "W2", Xp.dtype), dtype_code(Xp.dtype), T, d, E, K, n,
                                _dev(counts, "counts", torch.int32), _dev(offsets, "offsets", torch.int32),
-                               Act.data_ptr(), Y.data_ptr(), _stream(dev)), "moe_grouped_ffn")
+                               Act.data_ptr(), Y.data_ptr(), wp, wn, _stream(dev)), "moe_grouped_ffn")
     return Act, Y
 
 
 def moe_ffn_up(Xp: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, counts: torch.Tensor,
-               offsets: torch.Tensor, K: int):
+               offsets: torch.Tensor, K: int, split: bool = True, ws: torch.Tensor | None = None):
     """Step 4a.  Xp [T*K,d], W1/W3 [E,d,n] -> Act [T*K,n] = SiLU(Xp W1) * (Xp W3)."""
     lib = load_library()
     A, d = Xp.shape
     E, _, n = W1.shape
     dev = Xp.device
     Act = torch.empty((A, n), dtype=Xp.dtype, device=dev)
+    wp, wn = ffn_workspace(d, n, Xp.dtype, dev, split, ws)
     _check(lib.moe_ffn_up(_dev(Xp, "Xp"), _dev(W1, "W1", Xp.dtype), _dev(W3, "W3", Xp.dtype), dtype_code(Xp.dtype),
                           A // K, d, E, K, n, _dev(counts, "counts", torch.int32),
-                          _dev(offsets, "offsets", torch.int32), Act.data_ptr(), _stream(dev)), "moe_ffn_up")
+                          _dev(offsets, "offsets", torch.int32), Act.data_ptr(), wp, wn, _stream(dev)),
+           "moe_ffn_up")
     return Act
 
 
-def moe_ffn_down(Act: torch.Tensor, W2: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor, K: int):
+def moe_ffn_down(Act: torch.Tensor, W2: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor, K: int,
+                 split: bool = True, ws: torch.Tensor | None = None):
     """Step 4b.  Act [T*K,n], W2 [E,n,d] -> Y [T*K,d] = Act W2."""
     lib = load_library()
     A, n = Act.shape
     E, _, d = W2.shape
     dev = Act.device
     Y = torch.empty((A, d), dtype=Act.dtype, device=dev)
+    wp, wn = ffn_workspace(d, n, Act.dtype, dev, split, ws)
     _check(lib.moe_ffn_down(_dev(Act, "Act"), _dev(W2, "W2", Act.dtype), dtype_code(Act.dtype), A // K, d, E, K, n,
                             _dev(counts, "counts", torch.int32), _dev(offsets, "offsets", torch.int32),
-                            Y.data_ptr(), _stream(dev)), "moe_ffn_down")
+                            Y.data_ptr(), wp, wn, _stream(dev)), "moe_ffn_down")
     return Y
 
 

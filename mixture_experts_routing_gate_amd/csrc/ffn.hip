@@ -238,11 +238,85 @@ MOE_DEV int sched_lookup(const int32_t* __restrict__ counts, int E, int NT, int 
     return src * 4 + __shfl(hit, src, kWave);
 }
 
+// Rows and columns of pipelined-kernel tile `tile` (wave-uniform results).
+struct TileGeom {
+    int e, r0, rows_valid, n0;
+};
+MOE_DEV bool tile_geom(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int E, int NT,
+                       int OUTW, int rows, int lane, int tile, TileGeom& t) {
+    int first = 0, total = 0;
+    const int e = uniform(sched_lookup(counts, E, NT, rows, lane, tile, &first, &total));
+    if (e < 0) return false;
+    const int cnt = min(max(counts[e], 0), rows);
+    const int mt = (cnt + kBM256 - 1) / kBM256;
+    const int local = tile - uniform(first);
+    const int m_tile = local % mt;
+    const int n_tile = local / mt;
+    t.e = e;
+    t.r0 = offsets[e] + m_tile * kBM256;
+    t.rows_valid = (t.r0 < 0 || t.r0 >= rows) ? 0 : min(min(kBM256, cnt - m_tile * kBM256), rows - t.r0);
+    t.n0 = n_tile * OUTW;
+    return true;
+}
+
+// Split of the last, partial round of tiles over the idle workgroups: with
+// G workgroups and `total` tiles, the first R*G tiles are computed whole and
+// each of the Tr = total - R*G remaining ones in S parts of consecutive K-steps
+// (S = min(G / Tr, KT / 4), parts of whole groups of 4 K-steps).  Part p (of
+// Tr*S) writes its fp32 accumulators to slot p of the split workspace; the
+// fixup kernel adds a tile's S slots in order and runs the epilogue.
+struct SplitPlan {
+    int R, Tr, S;
+};
+MOE_DEV SplitPlan split_plan(int total, int G, int KT, bool enabled) {
+    SplitPlan sp;
+    sp.R = total / G;
+    sp.Tr = total - sp.R * G;
+    sp.S = (enabled && sp.Tr > 0) ? min(G / sp.Tr, KT / 4) : 1;
+    return sp;
+}
+constexpr int kPartFloats = 256 * 256;  // one 256 x 256 fp32 tile per slot
+
+// Output of one 32-row slice mi of a wave's 128 x 128 quadrant from its four
+// accumulators: bf16, rows past rows_valid skipped; with DUAL, the pairs
+// (ni, ni + 2) are (W1 part, W3 part) and give SiLU(W1 part) * (W3 part).
+template <bool DUAL>
+MOE_DEV void store_rows(const f32x16 (&a)[4], int mi, uint16_t* __restrict__ C, int r0, int rows_valid, int n0,
+                        int N, int wm, int wn, int l32, int lh) {
+    const int m = wm * 128 + mi * 32 + l32;
+    if (m < rows_valid) {
+        uint16_t* crow = C + (size_t)(r0 + m) * N;
+#pragma unroll
+        for (int ni = 0; ni < (DUAL ? 2 : 4); ++ni) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[j] = a[ni][q * 4 + j];
+                    if (DUAL) v[j] = silu_mul(v[j], a[ni + 2][q * 4 + j]);
+                }
+                const int col = n0 + (DUAL ? wn * 64 + ni * 32 : wn * 128 + ni * 32) + q * 8 + lh * 4;
+                uint2 pk;
+                pk.x = pack_bf16x2(v[0], v[1]);
+                pk.y = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<uint2*>(crow + col) = pk;
+            }
+        }
+    }
+}
+
+// Slot layout: per wave 16 fragments of 16 floats per lane, as float4 vectors
+// [wave][fragment][quarter][lane], so that each store and load is 1 KB per wave.
+MOE_DEV size_t part_index(int wave, int f, int q, int lane) {
+    return ((size_t)((wave * 16 + f) * 4 + q) * kWave + lane);
+}
+
 template <bool DUAL>
 __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    int E, int Kd, int N, int rows) {
+    int E, int Kd, int N, int rows, float* __restrict__ part) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     constexpr int OUTW = DUAL ? 128 : 256;
@@ -280,20 +354,27 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     const int G = gridDim.x;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int per_xcd = G >> 3;
+    const int KT = Kd / kP4BK;
+    const SplitPlan sp = split_plan(total, G, KT, part != nullptr);
+    const int whole = sp.S > 1 ? sp.R * G : total;  // tiles computed in one piece
     for (int round = 0;; ++round) {
-        const int tile = round * G + xcd * per_xcd + slot;
-        if (tile >= total) break;
-        const int e = uniform(sched_lookup(counts, E, NT, rows, lane, tile, &first, &total));
-        if (e < 0) break;
-        const int cnt = min(max(counts[e], 0), rows);
-        const int mt = (cnt + kBM256 - 1) / kBM256;
-        const int local = tile - uniform(first);
-        const int m_tile = local % mt;
-        const int n_tile = local / mt;
-        const int r0 = offsets[e] + m_tile * kBM256;
-        const int rows_valid = (r0 < 0 || r0 >= rows) ? 0 : min(min(kBM256, cnt - m_tile * kBM256), rows - r0);
+        int tile = round * G + xcd * per_xcd + slot;
+        int ks0 = 0, ksn = KT;  // K-steps of this work item
+        int pslot = -1;         // split-workspace slot of a tile part
+        if (tile >= whole) {
+            if (sp.S == 1 || round != sp.R) break;
+            const int p = xcd * per_xcd + slot;
+            if (p >= sp.Tr * sp.S) break;
+            tile = whole + p / sp.S;
+            const int j = p % sp.S, q = KT / 4;
+            ks0 = (j * q / sp.S) * 4;
+            ksn = ((j + 1) * q / sp.S) * 4 - ks0;
+            pslot = p;
+        }
+        TileGeom tg;
+        if (!tile_geom(counts, offsets, E, NT, OUTW, rows, lane, tile, tg)) break;
+        const int e = tg.e, r0 = tg.r0, rows_valid = tg.rows_valid, n0 = tg.n0;
         if (rows_valid <= 0) continue;
-        const int n0 = n_tile * OUTW;
 
         // DMA sources.  A: 16 rows of 64 bytes per KB; rows past the segment are
         // clamped to its last row.  B: 4 k-rows of one 128-column half per KB.
@@ -313,13 +394,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
             b_vo[i] = ((uint32_t)kr * (uint32_t)N + col) * 2u;
         }
         const uint32_t b_step = (uint32_t)kP4BK * (uint32_t)N * 2u;
-        const int KT = Kd / kP4BK;
         // DMA number i (0..7) of K-step kt into the stage at byte offset soff:
         // i < 4 are A, the rest B.
         auto issue_one = [&](int kt, int soff, int i) {
             const uint32_t dst = lds_base + soff + (wave * 4) * 1024;
-            if (i < 4) dma16(ra, dst + i * 1024, a_vo[i], (uint32_t)kt * (kP4BK * 2));
-            else dma16(rb, dst + 16384 + (i - 4) * 1024, b_vo[i - 4], (uint32_t)kt * b_step);
+            const uint32_t ka = (uint32_t)(ks0 + kt);
+            if (i < 4) dma16(ra, dst + i * 1024, a_vo[i], ka * (kP4BK * 2));
+            else dma16(rb, dst + 16384 + (i - 4) * 1024, b_vo[i - 4], ka * b_step);
         };
         auto issue = [&](int kt, int soff) {
 #pragma unroll
@@ -355,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
             }
         };
 
-        // Prologue (KT is a multiple of 4 here): K-steps 0..3 in flight, wait for step 0.
+        // Prologue (ksn is a multiple of 4 here): K-steps 0..3 in flight, wait for step 0.
         issue(0, 0);
         issue(1, kP4Stage);
         issue(2, 2 * kP4Stage);
@@ -365,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
         load_frags(0, 0, 0);
 
         int s_cur = 0;  // byte offset of step kt's stage
-        for (int kt0 = 0; kt0 < KT; kt0 += 4) {
+        for (int kt0 = 0; kt0 < ksn; kt0 += 4) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int kt = kt0 + u;
@@ -376,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                 __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
                 __syncthreads();
                 // Refill the stage of step kt-1 with step kt+4, one DMA per MFMA.
-                const int kn = min(kt + 4, KT - 1);
+                const int kn = min(kt + 4, ksn - 1);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     issue_one(kn, s_old, i);
@@ -412,29 +493,63 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
         // The clamped refills of the last steps are still in flight.
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+        if (pslot >= 0) {
+            f32x4* dst = reinterpret_cast<f32x4*>(part + (size_t)pslot * kPartFloats);
+#pragma unroll
+            for (int f = 0; f < 16; ++f)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x16& a = acc[f >> 2][f & 3];
+                    dst[part_index(wave, f, q, lane)] = f32x4{a[q * 4], a[q * 4 + 1], a[q * 4 + 2], a[q * 4 + 3]};
+                }
+        } else {
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) store_rows<DUAL>(acc[mi], mi, C, r0, rows_valid, n0, N, wm, wn, l32, lh);
+        }
+    }
+}
+
+// Finishes the split tiles of the pipelined kernel launched with G workgroups:
+// adds each tile's S partial slots in slot order and runs the epilogue.
+template <bool DUAL>
+__global__ __launch_bounds__(kThreads) void ffn_split_fixup(const float* __restrict__ part, uint16_t* __restrict__ C,
+                                                            const int32_t* __restrict__ counts,
+                                                            const int32_t* __restrict__ offsets, int E, int Kd, int N,
+                                                            int rows, int G) {
+    constexpr int OUTW = DUAL ? 128 : 256;
+    const int NT = N / OUTW;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, lh = lane >> 5;
+    int total = 0, first = 0;
+    sched_lookup(counts, E, NT, rows, lane, -1, &first, &total);
+    total = uniform(total);
+    const SplitPlan sp = split_plan(total, G, Kd / kP4BK, true);
+    if (sp.S == 1) return;
+    for (int i = blockIdx.x; i < sp.Tr; i += gridDim.x) {
+        TileGeom tg;
+        if (!tile_geom(counts, offsets, E, NT, OUTW, rows, lane, sp.R * G + i, tg)) return;
+        if (tg.rows_valid <= 0) continue;
+        const f32x4* src = reinterpret_cast<const f32x4*>(part + (size_t)i * sp.S * kPartFloats);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            const int m = wm * 128 + mi * 32 + l32;
-            if (m < rows_valid) {
-                uint16_t* crow = C + (size_t)(r0 + m) * N;
+            f32x16 acc[4];
 #pragma unroll
-                for (int ni = 0; ni < (DUAL ? 2 : 4); ++ni) {
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int c = 0; c < 16; ++c) acc[ni][c] = 0.0f;
+            for (int j = 0; j < sp.S; ++j) {  // parts in slot order
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        float v[4];
+                        const f32x4 v = src[(size_t)j * (kPartFloats / 4) + part_index(wave, mi * 4 + ni, q, lane)];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            v[j] = acc[mi][ni][q * 4 + j];
-                            if (DUAL) v[j] = silu_mul(v[j], acc[mi][ni + 2][q * 4 + j]);
-                        }
-                        const int col = n0 + (DUAL ? wn * 64 + ni * 32 : wn * 128 + ni * 32) + q * 8 + lh * 4;
-                        uint2 pk;
-                        pk.x = pack_bf16x2(v[0], v[1]);
-                        pk.y = pack_bf16x2(v[2], v[3]);
-                        *reinterpret_cast<uint2*>(crow + col) = pk;
+                        for (int c = 0; c < 4; ++c) acc[ni][q * 4 + c] += v[c];
                     }
-                }
             }
+            store_rows<DUAL>(acc, mi, C, tg.r0, tg.rows_valid, tg.n0, N, wm, wn, l32, lh);
         }
     }
 }
@@ -537,19 +652,39 @@ __global__ __launch_bounds__(kThreads) void ffn_f32_kernel(const float* __restri
 // multiples of 128 for both GEMMs.
 static bool ffn_pipelined_ok(int d, int n) { return d % 256 == 0 && n % 128 == 0; }
 
+static int ffn_grid() { return (device_cu_count() / 8) * 8; }
+
+size_t ffn_split_bytes(int dtype, int d, int n) {
+    return (dtype == 1 && ffn_pipelined_ok(d, n)) ? (size_t)ffn_grid() * kPartFloats * sizeof(float) : 0;
+}
+
+// One pipelined GEMM (SwiGLU or plain), then the fixup of its split tail.
+template <bool DUAL>
+static hipError_t launch_pipelined(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C,
+                                   const int32_t* counts, const int32_t* offsets, int E, int Kd, int N, int rows,
+                                   float* part, hipStream_t s) {
+    const hipError_t aerr =
+        hipFuncSetAttribute((const void*)ffn_p4_kernel<DUAL>, hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
+    if (aerr != hipSuccess) return aerr;
+    const int G = ffn_grid();
+    hipLaunchKernelGGL(ffn_p4_kernel<DUAL>, dim3(G), dim3(kThreads), kP4Lds, s, A, B0, B1, C, counts, offsets, E, Kd,
+                       N, rows, part);
+    if (part != nullptr)
+        hipLaunchKernelGGL(ffn_split_fixup<DUAL>, dim3(G), dim3(kThreads), 0, s, part, C, counts, offsets, E, Kd, N,
+                           rows, G);
+    return hipGetLastError();
+}
+
 // Step 4a: Act = SiLU(Xp W1) * (Xp W3).
 hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int rows, int d, int E,
-                         int n, const int32_t* counts, const int32_t* offsets, void* Act, hipStream_t s) {
+                         int n, const int32_t* counts, const int32_t* offsets, void* Act, float* part,
+                         hipStream_t s) {
     const int cus = device_cu_count();
-    if (dtype == 1 && ffn_pipelined_ok(d, n)) {
-        const hipError_t aerr = hipFuncSetAttribute((const void*)ffn_p4_kernel<true>,
-                                                    hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
-        if (aerr != hipSuccess) return aerr;
-        hipLaunchKernelGGL(ffn_p4_kernel<true>, dim3((cus / 8) * 8), dim3(kThreads), kP4Lds, s,
-                           static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
-                           static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(Act), counts, offsets, E, d,
-                           n, rows);
-    } else if (dtype == 1) {
+    if (dtype == 1 && ffn_pipelined_ok(d, n))
+        return launch_pipelined<true>(static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
+                                      static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(Act), counts,
+                                      offsets, E, d, n, rows, part, s);
+    if (dtype == 1) {
         hipLaunchKernelGGL(ffn_bf16_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s,
                            static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
                            static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(Act), counts, offsets, E, d,
@@ -565,17 +700,13 @@ hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dty
 
 // Step 4b: Y = Act W2.
 hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows, int d, int E, int n,
-                           const int32_t* counts, const int32_t* offsets, void* Y, hipStream_t s) {
+                           const int32_t* counts, const int32_t* offsets, void* Y, float* part, hipStream_t s) {
     const int cus = device_cu_count();
-    if (dtype == 1 && ffn_pipelined_ok(d, n)) {
-        const hipError_t aerr = hipFuncSetAttribute((const void*)ffn_p4_kernel<false>,
-                                                    hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
-        if (aerr != hipSuccess) return aerr;
-        hipLaunchKernelGGL(ffn_p4_kernel<false>, dim3((cus / 8) * 8), dim3(kThreads), kP4Lds, s,
-                           static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
-                           static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(Y), counts, offsets, E,
-                           n, d, rows);
-    } else if (dtype == 1) {
+    if (dtype == 1 && ffn_pipelined_ok(d, n))
+        return launch_pipelined<false>(static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
+                                       static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(Y), counts,
+                                       offsets, E, n, d, rows, part, s);
+    if (dtype == 1) {
         hipLaunchKernelGGL(ffn_bf16_kernel<false>, dim3(cus * 2), dim3(kThreads), 0, s,
                            static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
                            static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(Y), counts, offsets, E,
@@ -591,10 +722,10 @@ hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows,
 
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
                       int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
-                      void* Act, void* Y, hipStream_t s) {
-    const hipError_t err = launch_ffn_up(Xp, W1, W3, dtype, rows, d, E, n, counts, offsets, Act, s);
+                      void* Act, void* Y, float* part, hipStream_t s) {
+    const hipError_t err = launch_ffn_up(Xp, W1, W3, dtype, rows, d, E, n, counts, offsets, Act, part, s);
     if (err != hipSuccess) return err;
-    return launch_ffn_down(Act, W2, dtype, rows, d, E, n, counts, offsets, Y, s);
+    return launch_ffn_down(Act, W2, dtype, rows, d, E, n, counts, offsets, Y, part, s);
 }
 
 }  // namespace moe

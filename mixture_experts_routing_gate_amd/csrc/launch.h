@@ -30,13 +30,17 @@ hipError_t launch_copy_rows(const void* X, size_t row_bytes, int T, int K, const
                             void* Xp, hipStream_t s);
 
 // Step 4.  dtype: 0 = fp32, 1 = bf16.  4a (SwiGLU GEMM), 4b (down GEMM), both.
+// `part` (nullable) is the split workspace of ffn_split_bytes() bytes: with it,
+// the last partial round of tiles is split over the idle workgroups along K.
+size_t ffn_split_bytes(int dtype, int d, int n);
 hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int rows, int d, int E,
-                         int n, const int32_t* counts, const int32_t* offsets, void* Act, hipStream_t s);
+                         int n, const int32_t* counts, const int32_t* offsets, void* Act, float* part,
+                         hipStream_t s);
 hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows, int d, int E, int n,
-                           const int32_t* counts, const int32_t* offsets, void* Y, hipStream_t s);
+                           const int32_t* counts, const int32_t* offsets, void* Y, float* part, hipStream_t s);
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
                       int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
-                      void* Act, void* Y, hipStream_t s);
+                      void* Act, void* Y, float* part, hipStream_t s);
 
 // Step 5.
 hipError_t launch_combine(const void* Y, const float* w, const int32_t* inv, int dtype, int T, int d,

@@ -118,7 +118,21 @@ size_t forward_ws(int T, int d, int E, int K, int n, int dtype) {
     b += align_up(E * 4) + align_up((E + 1) * 4);      // counts, offsets
     b += align_up(A * 4) * 2;                          // sorted_pair, inv
     b += align_up(A * d * s) * 2 + align_up(A * n * s);  // Xp, Y, Act
+    b += align_up(ffn_split_bytes(dtype, d, n));        // split tail of the grouped GEMMs
     return b;
+}
+
+// Optional split workspace of the grouped GEMMs: NULL disables the split.
+int ffn_split_arg(void* ws, size_t ws_bytes, int dtype, int d, int n, float** part) {
+    *part = nullptr;
+    if (ws == nullptr) return MOE_OK;
+    const size_t need = ffn_split_bytes(dtype, d, n);
+    if (need == 0) return MOE_OK;
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "the grouped GEMM workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+    *part = static_cast<float*>(ws);
+    return MOE_OK;
 }
 
 std::atomic<int> g_cu_count[64];
@@ -166,6 +180,12 @@ size_t moe_route_workspace_bytes(int T, int E, int K) {
 size_t moe_permute_workspace_bytes(int T, int E, int K) {
     if (check_tek(T, E, K) != MOE_OK) return 0;
     return permute_ws(T, E);
+}
+
+size_t moe_ffn_workspace_bytes(int d, int n, int dtype) {
+    if (check_dtype(dtype) != MOE_OK || check_dim("d", d, dtype) != MOE_OK || check_dim("n", n, dtype) != MOE_OK)
+        return 0;
+    return ffn_split_bytes(dtype, d, n);
 }
 
 size_t moe_forward_workspace_bytes(int T, int d, int E, int K, int n, int dtype) {
@@ -225,7 +245,7 @@ int moe_permute(const void* X, int dtype, int T, int d, int E, int K, const int3
 
 int moe_grouped_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype, int T,
                     int d, int E, int K, int n, const int32_t* counts, const int32_t* offsets, void* Act,
-                    void* Y, void* stream) {
+                    void* Y, void* ws, size_t ws_bytes, void* stream) {
     CHECK(check_tek(T, E, K));
     CHECK(check_dtype(dtype));
     CHECK(check_dim("d", d, dtype));
@@ -240,13 +260,16 @@ int moe_grouped_ffn(const void* Xp, const void* W1, const void* W3, const void* 
     NONNULL(Y);
     if ((long long)T * K * (long long)(d > n ? d : n) >= (1LL << 40))
         return fail(MOE_ERR_UNSUPPORTED, "T*K*max(d,n) must be < 2^40");
-    HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, T * K, d, E, n, counts, offsets, Act, Y,
+    float* part = nullptr;
+    CHECK(ffn_split_arg(ws, ws_bytes, dtype, d, n, &part));
+    HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, T * K, d, E, n, counts, offsets, Act, Y, part,
                         static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
 
 int moe_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int T, int d, int E, int K, int n,
-               const int32_t* counts, const int32_t* offsets, void* Act, void* stream) {
+               const int32_t* counts, const int32_t* offsets, void* Act, void* ws, size_t ws_bytes,
+               void* stream) {
     CHECK(check_tek(T, E, K));
     CHECK(check_dtype(dtype));
     CHECK(check_dim("d", d, dtype));
@@ -259,13 +282,16 @@ int moe_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int T,
     NONNULL(Act);
     if ((long long)T * K * (long long)(d > n ? d : n) >= (1LL << 40))
         return fail(MOE_ERR_UNSUPPORTED, "T*K*max(d,n) must be < 2^40");
-    HIPCHECK(launch_ffn_up(Xp, W1, W3, dtype, T * K, d, E, n, counts, offsets, Act,
+    float* part = nullptr;
+    CHECK(ffn_split_arg(ws, ws_bytes, dtype, d, n, &part));
+    HIPCHECK(launch_ffn_up(Xp, W1, W3, dtype, T * K, d, E, n, counts, offsets, Act, part,
                            static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
 
 int moe_ffn_down(const void* Act, const void* W2, int dtype, int T, int d, int E, int K, int n,
-                 const int32_t* counts, const int32_t* offsets, void* Y, void* stream) {
+                 const int32_t* counts, const int32_t* offsets, void* Y, void* ws, size_t ws_bytes,
+                 void* stream) {
     CHECK(check_tek(T, E, K));
     CHECK(check_dtype(dtype));
     CHECK(check_dim("d", d, dtype));
@@ -277,7 +303,9 @@ int moe_ffn_down(const void* Act, const void* W2, int dtype, int T, int d, int E
     NONNULL(Y);
     if ((long long)T * K * (long long)(d > n ? d : n) >= (1LL << 40))
         return fail(MOE_ERR_UNSUPPORTED, "T*K*max(d,n) must be < 2^40");
-    HIPCHECK(launch_ffn_down(Act, W2, dtype, T * K, d, E, n, counts, offsets, Y,
+    float* part = nullptr;
+    CHECK(ffn_split_arg(ws, ws_bytes, dtype, d, n, &part));
+    HIPCHECK(launch_ffn_down(Act, W2, dtype, T * K, d, E, n, counts, offsets, Y, part,
                              static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
@@ -339,6 +367,8 @@ int moe_forward(const void* X, const float* logits, const void* W1, const void* 
     void* Xp = c.take<char>(A * d * sz);
     void* Yb = c.take<char>(A * d * sz);
     void* Act = c.take<char>(A * n * sz);
+    const size_t split_bytes = ffn_split_bytes(dtype, d, n);
+    float* part = split_bytes ? c.take<float>(split_bytes / sizeof(float)) : nullptr;
     if (!topk_idx) topk_idx = ws_idx;
     if (!topk_w) topk_w = ws_w;
     if (!counts) counts = ws_cnt;
@@ -350,7 +380,7 @@ int moe_forward(const void* X, const float* logits, const void* W1, const void* 
     HIPCHECK(launch_scan(blk, B, E, counts, offsets, blkbase, s));
     HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s));
     HIPCHECK(launch_copy_rows(X, (size_t)d * sz, T, K, inv, Xp, s));
-    HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, (int)A, d, E, n, counts, offsets, Act, Yb, s));
+    HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, (int)A, d, E, n, counts, offsets, Act, Yb, part, s));
     HIPCHECK(launch_combine(Yb, topk_w, inv, dtype, T, d, K, out, s));
     return MOE_OK;
 }

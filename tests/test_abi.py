@@ -76,12 +76,17 @@ def test_grouped_ffn_rejects(lib):
     def call(**kw):
         a = dict(args, **kw)
         return lib.moe_grouped_ffn(a["Xp"], a["W1"], a["W3"], a["W2"], a["dt"], a["T"], a["d"], a["E"],
-                                   a["K"], a["n"], a["c"], a["o"], a["act"], a["y"], None)
+                                   a["K"], a["n"], a["c"], a["o"], a["act"], a["y"], a.get("ws"),
+                                   a.get("wsb", 0), None)
     assert call(W3=None) == INVALID
     assert call(d=192) == UNSUPPORTED          # bf16 needs multiples of 128
     assert call(n=0) == INVALID
     assert call(dt=0, d=192, n=64, c=None) == INVALID
     assert call(K=3, E=2) == INVALID
+    # the optional split workspace: NULL is fine, a too small one is rejected
+    assert lib.moe_ffn_workspace_bytes(256, 128, 1) > 0
+    assert lib.moe_ffn_workspace_bytes(64, 64, 0) == 0
+    assert call(d=256, ws=P, wsb=4) == WORKSPACE
 
 
 def test_combine_and_forward_reject(lib):
