@@ -11,6 +11,8 @@
 //
 //   FFN1: Act[r] = SiLU(Xp[r] W1[e]) * (Xp[r] W3[e])   (both products in one tile)
 //   FFN2: Y[r]   = Act[r] W2[e]
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -280,9 +282,15 @@ constexpr int kPartFloats = 256 * 256;  // one 256 x 256 fp32 tile per slot
 // Output of one 32-row slice mi of a wave's 128 x 128 quadrant from its four
 // accumulators: bf16, rows past rows_valid skipped; with DUAL, the pairs
 // (ni, ni + 2) are (W1 part, W3 part) and give SiLU(W1 part) * (W3 part).
+// (The lane index is re-derived here rather than kept live from the kernel's
+// start: after the K-loop registers are scarce, and a spilled lane index would
+// cost a scratch reload per tile.)
 template <bool DUAL>
 MOE_DEV void store_rows(const f32x16 (&a)[4], int mi, uint16_t* __restrict__ C, int r0, int rows_valid, int n0,
-                        int N, int wm, int wn, int l32, int lh) {
+                        int N, int wm, int wn) {
+    int lane = __lane_id();
+    __asm__ volatile("" : "+v"(lane));  // keeps the row math here instead of hoisted (and spilled)
+    const int l32 = lane & 31, lh = lane >> 5;
     const int m = wm * 128 + mi * 32 + l32;
     if (m < rows_valid) {
         uint16_t* crow = C + (size_t)(r0 + m) * N;
@@ -376,136 +384,146 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
         const int e = tg.e, r0 = tg.r0, rows_valid = tg.rows_valid, n0 = tg.n0;
         if (rows_valid <= 0) continue;
 
-        // DMA sources.  A: 16 rows of 64 bytes per KB; rows past the segment are
-        // clamped to its last row.  B: 4 k-rows of one 128-column half per KB.
-        const rsrc_t ra = make_rsrc(A + (size_t)r0 * Kd);
-        const int half = wave >> 1;
-        const uint16_t* bmat = (DUAL && half) ? B1 : B0;
-        const rsrc_t rb = make_rsrc(bmat + (size_t)e * Kd * N);
-        uint32_t a_vo[4], b_vo[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = (wave * 4 + i) * 16 + (lane >> 2);
-            const int ch = (lane & 3) ^ ((r >> 2) & 3);
-            a_vo[i] = ((uint32_t)min(r, rows_valid - 1) * (uint32_t)Kd + ch * 8) * 2u;
-            const int kr = (wave & 1) * 16 + i * 4 + (lane >> 4);
-            const int bc = (lane & 15) ^ ((kr & 3) << 2);
-            const int col = (DUAL ? n0 : n0 + half * 128) + bc * 8;
-            b_vo[i] = ((uint32_t)kr * (uint32_t)N + col) * 2u;
-        }
-        const uint32_t b_step = (uint32_t)kP4BK * (uint32_t)N * 2u;
-        // DMA number i (0..7) of K-step kt into the stage at byte offset soff:
-        // i < 4 are A, the rest B.
-        auto issue_one = [&](int kt, int soff, int i) {
-            const uint32_t dst = lds_base + soff + (wave * 4) * 1024;
-            const uint32_t ka = (uint32_t)(ks0 + kt);
-            if (i < 4) dma16(ra, dst + i * 1024, a_vo[i], ka * (kP4BK * 2));
-            else dma16(rb, dst + 16384 + (i - 4) * 1024, b_vo[i - 4], ka * b_step);
-        };
-        auto issue = [&](int kt, int soff) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) issue_one(kt, soff, i);
-        };
-
-        f32x16 acc[4][4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
-
-        bf16x8 af[2][4], bfr[2][4];
-        auto load_frags = [&](int soff, int ks, int buf) {
-            const char* sa = smem + soff + a_rd[ks];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * 64);
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                const char* pb = smem + soff + b_rd[ni] + ks * 16 * 256;
-                const bf16x4 h0 = lds_read_tr(pb);
-                const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
-                bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+        // The tile body, instantiated twice so that the partial-slot epilogue of
+        // the split round does not weigh on the register allocation of the rest.
+        auto run_tile = [&](auto part_tag) {
+            constexpr bool PART = decltype(part_tag)::value;
+            // DMA sources.  A: 16 rows of 64 bytes per KB; rows past the segment are
+            // clamped to its last row.  B: 4 k-rows of one 128-column half per KB.
+            const rsrc_t ra = make_rsrc(A + (size_t)r0 * Kd);
+            const int half = wave >> 1;
+            const uint16_t* bmat = (DUAL && half) ? B1 : B0;
+            const rsrc_t rb = make_rsrc(bmat + (size_t)e * Kd * N);
+            uint32_t a_vo[4], b_vo[4];
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = (wave * 4 + i) * 16 + (lane >> 2);
+                const int ch = (lane & 3) ^ ((r >> 2) & 3);
+                a_vo[i] = ((uint32_t)min(r, rows_valid - 1) * (uint32_t)Kd + ch * 8) * 2u;
+                const int kr = (wave & 1) * 16 + i * 4 + (lane >> 4);
+                const int bc = (lane & 15) ^ ((kr & 3) << 2);
+                const int col = (DUAL ? n0 : n0 + half * 128) + bc * 8;
+                b_vo[i] = ((uint32_t)kr * (uint32_t)N + col) * 2u;
             }
-        };
-        auto mfma = [&](int buf, int lo, int hi) {
-#pragma unroll
-            for (int q = lo; q < hi; ++q) {
-                const int mi = q >> 2, ni = q & 3;
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
-            }
-        };
+            const uint32_t b_step = (uint32_t)kP4BK * (uint32_t)N * 2u;
+            // DMA number i (0..7) of K-step kt into the stage at byte offset soff:
+            // i < 4 are A, the rest B.
+            auto issue_one = [&](int kt, int soff, int i) {
+                const uint32_t dst = lds_base + soff + (wave * 4) * 1024;
+                const uint32_t ka = (uint32_t)(ks0 + kt);
+                if (i < 4) dma16(ra, dst + i * 1024, a_vo[i], ka * (kP4BK * 2));
+                else dma16(rb, dst + 16384 + (i - 4) * 1024, b_vo[i - 4], ka * b_step);
+            };
+            auto issue = [&](int kt, int soff) {
+    #pragma unroll
+                for (int i = 0; i < 8; ++i) issue_one(kt, soff, i);
+            };
 
-        // Prologue (ksn is a multiple of 4 here): K-steps 0..3 in flight, wait for step 0.
-        issue(0, 0);
-        issue(1, kP4Stage);
-        issue(2, 2 * kP4Stage);
-        issue(3, 3 * kP4Stage);
-        __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
-        __syncthreads();
-        load_frags(0, 0, 0);
+            f32x16 acc[4][4];
+    #pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+    #pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+    #pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
 
-        int s_cur = 0;  // byte offset of step kt's stage
-        for (int kt0 = 0; kt0 < ksn; kt0 += 4) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int kt = kt0 + u;
-                const int s_nxt = s_cur == (kP4Stages - 1) * kP4Stage ? 0 : s_cur + kP4Stage;
-                const int s_old = s_cur == 0 ? (kP4Stages - 1) * kP4Stage : s_cur - kP4Stage;
-                // Step boundary: own DMA of step kt+1 done (16 younger ones may fly).
-                __builtin_amdgcn_sched_barrier(0);
-                __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
-                __syncthreads();
-                // Refill the stage of step kt-1 with step kt+4, one DMA per MFMA.
-                const int kn = min(kt + 4, ksn - 1);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    issue_one(kn, s_old, i);
-                    mfma(0, i, i + 1);
+            bf16x8 af[2][4], bfr[2][4];
+            auto load_frags = [&](int soff, int ks, int buf) {
+                const char* sa = smem + soff + a_rd[ks];
+    #pragma unroll
+                for (int mi = 0; mi < 4; ++mi) af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * 64);
+    #pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const char* pb = smem + soff + b_rd[ni] + ks * 16 * 256;
+                    const bf16x4 h0 = lds_read_tr(pb);
+                    const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
+                    bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            };
+            auto mfma = [&](int buf, int lo, int hi) {
+    #pragma unroll
+                for (int q = lo; q < hi; ++q) {
+                    const int mi = q >> 2, ni = q & 3;
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
+                }
+            };
+
+            // Prologue (ksn is a multiple of 4 here): K-steps 0..3 in flight, wait for step 0.
+            issue(0, 0);
+            issue(1, kP4Stage);
+            issue(2, 2 * kP4Stage);
+            issue(3, 3 * kP4Stage);
+            __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
+            __syncthreads();
+            load_frags(0, 0, 0);
+
+            int s_cur = 0;  // byte offset of step kt's stage
+            for (int kt0 = 0; kt0 < ksn; kt0 += 4) {
+    #pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int kt = kt0 + u;
+                    const int s_nxt = s_cur == (kP4Stages - 1) * kP4Stage ? 0 : s_cur + kP4Stage;
+                    const int s_old = s_cur == 0 ? (kP4Stages - 1) * kP4Stage : s_cur - kP4Stage;
+                    // Step boundary: own DMA of step kt+1 done (16 younger ones may fly).
                     __builtin_amdgcn_sched_barrier(0);
+                    __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+                    __syncthreads();
+                    // Refill the stage of step kt-1 with step kt+4, one DMA per MFMA.
+                    const int kn = min(kt + 4, ksn - 1);
+    #pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        issue_one(kn, s_old, i);
+                        mfma(0, i, i + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    // Rest of sub-step 0 while sub-step 1's fragments are read.
+                    load_frags(s_cur, 1, 1);
+                    mfma(0, 8, 16);
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    }
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    // Sub-step 1 while the next step's sub-step-0 fragments are read.
+                    load_frags(s_nxt, 0, 0);
+                    mfma(1, 0, 16);
+    #pragma unroll
+                    for (int i = 0; i < 12; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                    s_cur = s_nxt;
                 }
-                // Rest of sub-step 0 while sub-step 1's fragments are read.
-                load_frags(s_cur, 1, 1);
-                mfma(0, 8, 16);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                // Sub-step 1 while the next step's sub-step-0 fragments are read.
-                load_frags(s_nxt, 0, 0);
-                mfma(1, 0, 16);
-#pragma unroll
-                for (int i = 0; i < 12; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-                s_cur = s_nxt;
             }
-        }
-        // The clamped refills of the last steps are still in flight.
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // The clamped refills of the last steps are still in flight.
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-        if (pslot >= 0) {
-            f32x4* dst = reinterpret_cast<f32x4*>(part + (size_t)pslot * kPartFloats);
 #pragma unroll
-            for (int f = 0; f < 16; ++f)
+            for (int mi = 0; mi < 4; ++mi) {
+                if constexpr (PART) {
+                    f32x4* dst =
+                        reinterpret_cast<f32x4*>(part + (size_t)pslot * kPartFloats) + part_index(wave, mi * 4, 0, __lane_id());
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x16& a = acc[f >> 2][f & 3];
-                    dst[part_index(wave, f, q, lane)] = f32x4{a[q * 4], a[q * 4 + 1], a[q * 4 + 2], a[q * 4 + 3]};
+                    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const f32x16& av = acc[mi][ni];
+                            dst[(ni * 4 + q) * kWave] = f32x4{av[q * 4], av[q * 4 + 1], av[q * 4 + 2], av[q * 4 + 3]};
+                        }
+                } else {
+                    store_rows<DUAL>(acc[mi], mi, C, r0, rows_valid, n0, N, wm, wn);
                 }
-        } else {
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) store_rows<DUAL>(acc[mi], mi, C, r0, rows_valid, n0, N, wm, wn, l32, lh);
-        }
+            }
+        };
+        if (pslot >= 0) run_tile(std::true_type{});
+        else run_tile(std::false_type{});
     }
 }
 
@@ -527,30 +545,33 @@ __global__ __launch_bounds__(kThreads) void ffn_split_fixup(const float* __restr
     total = uniform(total);
     const SplitPlan sp = split_plan(total, G, Kd / kP4BK, true);
     if (sp.S == 1) return;
-    for (int i = blockIdx.x; i < sp.Tr; i += gridDim.x) {
+    // one work unit per (split tile, 32-row slice of every wave's quadrant)
+    for (int u = blockIdx.x; u < sp.Tr * 4; u += gridDim.x) {
+        const int i = u >> 2, mi = u & 3;
         TileGeom tg;
         if (!tile_geom(counts, offsets, E, NT, OUTW, rows, lane, sp.R * G + i, tg)) return;
         if (tg.rows_valid <= 0) continue;
         const f32x4* src = reinterpret_cast<const f32x4*>(part + (size_t)i * sp.S * kPartFloats);
+        f32x16 acc[4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            f32x16 acc[4];
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[ni][c] = 0.0f;
+        for (int j = 0; j < sp.S; ++j) {  // parts in slot order
+            f32x4 v[16];
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-                for (int c = 0; c < 16; ++c) acc[ni][c] = 0.0f;
-            for (int j = 0; j < sp.S; ++j) {  // parts in slot order
+                for (int q = 0; q < 4; ++q)
+                    v[ni * 4 + q] = src[(size_t)j * (kPartFloats / 4) + part_index(wave, mi * 4 + ni, q, lane)];
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
+            for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 v = src[(size_t)j * (kPartFloats / 4) + part_index(wave, mi * 4 + ni, q, lane)];
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) acc[ni][q * 4 + c] += v[c];
-                    }
-            }
-            store_rows<DUAL>(acc, mi, C, tg.r0, tg.rows_valid, tg.n0, N, wm, wn, l32, lh);
+                    for (int c = 0; c < 4; ++c) acc[ni][q * 4 + c] += v[ni * 4 + q][c];
         }
+        store_rows<DUAL>(acc, mi, C, tg.r0, tg.rows_valid, tg.n0, N, wm, wn);
     }
 }
 
