@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the DeepSeek-V3-shaped and fine-grained layer timings")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a plain copy of known size and each step once (for rocprofv3 --pmc) and exit")
     return ap.parse_args()
@@ -238,7 +240,52 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, g, args.cpu_seconds, np, torch, synth)
+    if not args.no_other_workloads:
+        del g, plan, Xp, Act, Y
+        torch.cuda.empty_cache()
+        out["other_workloads"] = {name: other_workload(name, moe, synth, torch, np, dev)
+                                  for name in ("dsv3", "fine")}
     print(json.dumps(out), flush=True)
+
+
+def other_workload(name, moe, synth, torch, np, dev, steps=5):
+    """Whole-layer time of another workload shape (context, not the headline):
+    active TFLOP/s and the fraction of a per-step roofline that sums, over the
+    kernels, max(FLOPs / bf16 peak, algorithmic bytes / HBM peak), with the
+    weights of non-empty experts read once."""
+    c = synth.CONFIGS[name]
+    g = synth.make_inputs(c, dev, seed=0)
+    plan = moe.ForwardPlan(c.T, c.d, c.E, c.K, c.n, c.torch_dtype, dev)
+
+    def run():
+        plan(g["X"], g["logits"], g["W1"], g["W3"], g["W2"])
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    counts = plan.counts.cpu().numpy().astype(np.int64)
+    A, d, n, E, K, T, s = c.T * c.K, c.d, c.n, c.E, c.K, c.T, 2
+    e_act = int((counts > 0).sum())
+    P, BW = PEAK_BF16_TFLOPS * 1e12, PEAK_HBM_GBS * 1e9
+    roof_s = (T * (4 * E + 8 * K)) / BW                                                        # gate
+    roof_s += 2 * T * (s * d * (K + 1)) / BW                                                   # permute + combine
+    roof_s += max(4.0 * A * d * n / P, (2 * e_act * d * n * s + A * (d + n) * s) / BW)        # SwiGLU GEMM
+    roof_s += max(2.0 * A * d * n / P, (e_act * n * d * s + A * (n + d) * s) / BW)            # down GEMM
+    padded = int(sum(-(-int(x) // 256) * 256 for x in counts))
+    res = {"workload": f"{name}: T={T}, d={d}, E={E}, K={K}, n={n}, {c.dtype}, logits {c.logits}"
+                       + (f" (per-expert bias variance {c.bias_var})" if c.bias_var else ""),
+           "ms_per_step": round(ms, 4), "TFLOPS": 6.0 * A * d * n / (ms * 1e-3) / 1e12,
+           "roofline_ms": round(roof_s * 1e3, 4), "frac_of_roofline": roof_s * 1e3 / ms,
+           "experts_nonempty": e_act, "max_count": int(counts.max()),
+           "tile_padding": padded / A - 1.0}
+    del g, plan
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(cfg, g, budget_s, np, torch, synth):
