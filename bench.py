@@ -276,7 +276,12 @@ def other_workload(name, moe, synth, torch, np, dev, steps=5):
     roof_s += 2 * T * (s * d * (K + 1)) / BW                                                   # permute + combine
     roof_s += max(4.0 * A * d * n / P, (2 * e_act * d * n * s + A * (d + n) * s) / BW)        # SwiGLU GEMM
     roof_s += max(2.0 * A * d * n / P, (e_act * n * d * s + A * (n + d) * s) / BW)            # down GEMM
-    padded = int(sum(-(-int(x) // 256) * 256 for x in counts))
+    # rows the MFMA tiles compute: whole 256-row tiles, and the last tile of an
+    # expert at 32, 64 or 128 rows when its remainder fits
+    def rows_computed(c):
+        full, rem = divmod(int(c), 256)
+        return full * 256 + (0 if rem == 0 else next(h for h in (32, 64, 128, 256) if rem <= h))
+    padded = sum(rows_computed(x) for x in counts)
     res = {"workload": f"{name}: T={T}, d={d}, E={E}, K={K}, n={n}, {c.dtype}, logits {c.logits}"
                        + (f" (per-expert bias variance {c.bias_var})" if c.bias_var else ""),
            "ms_per_step": round(ms, 4), "TFLOPS": 6.0 * A * d * n / (ms * 1e-3) / 1e12,

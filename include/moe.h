@@ -136,8 +136,12 @@ int moe_permute(const void* X, int dtype, int T, int d, int E, int K, const int3
  *      With it, the tiles of each GEMM's last, partial round are split along K
  *      over the otherwise idle workgroups; the fp32 parts are added in a fixed
  *      order, so results stay deterministic (they may differ from the unsplit
- *      ones by fp32 rounding).  A non-NULL ws that is too small is
- *      MOE_ERR_WORKSPACE.
+ *      ones by fp32 rounding).  It also holds the counters from which the
+ *      workgroups of each XCD claim their tiles one at a time (cleared by the
+ *      library before each GEMM), so that workgroups that drew short tiles
+ *      take more; which workgroup computes a tile does not change the result.
+ *      Calls that share one workspace must not overlap.  A non-NULL ws that
+ *      is too small is MOE_ERR_WORKSPACE.
  */
 int moe_grouped_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
                     int T, int d, int E, int K, int n, const int32_t* counts,

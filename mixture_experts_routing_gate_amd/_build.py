@@ -21,11 +21,15 @@ ARCH = "gfx950"
 # form them from ordinary float arithmetic.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
+# Per-source flags.  ffn.hip: one thread claims the next tile with an atomic
+# whose result is needed only after the K-loop; the wave-level atomic
+# combining pass would instead wait for it (and every older store) at once.
+EXTRA = {"ffn.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, *EXTRA.get(src, [])]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

@@ -53,7 +53,12 @@ __device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) 
     return lo;
 }
 
-MOE_DEV float silu_mul(float h1, float h3) { return h1 / (1.0f + __expf(-h1)) * h3; }
+// SiLU(h1) * h3 with SiLU(z) = z / (1 + e^-z) (page [P4] section 2.2).  The
+// quotient uses the hardware reciprocal (1 ulp) rather than an IEEE division
+// sequence: the result is rounded to bf16 right after, and the division was
+// most of the SwiGLU epilogue's cost.  Large negative z gives e^-z = inf and a
+// zero reciprocal, so the limit 0 comes out as it should.
+MOE_DEV float silu_mul(float h1, float h3) { return h1 * __builtin_amdgcn_rcpf(1.0f + __expf(-h1)) * h3; }
 
 // bf16 MFMA tile kernel.  Block tile 128 x 128 x 64, four waves in 2 x 2, each
 // wave 64 x 64 as 2 x 2 v_mfma_f32_32x32x16_bf16 tiles (x2 for the W1/W3 pair).
@@ -203,6 +208,10 @@ MOE_DEV bf16x4 lds_read_tr(const char* l) {
 //    instruction reads a single matrix (W1 or W3 for the SwiGLU GEMM).
 // ---------------------------------------------------------------------------
 constexpr int kP4BK = 32, kP4Stage = 32768, kP4Stages = 5, kP4Lds = kP4Stages * kP4Stage;
+// LDS word that passes a claimed work ticket to all waves (in the last stage).
+constexpr int kP4TicketOff = (kP4Stages - 1) * kP4Stage;
+// Claim counters of the dynamic schedule: one per XCD, 64 bytes apart.
+constexpr int kTicketInts = 8 * 16;
 
 // The tile schedule of the pipelined kernel, held in registers (E <= 256): lane
 // l holds experts 4l..4l+3, and expert e owns the tiles [start_e, start_e +
@@ -238,6 +247,22 @@ MOE_DEV int sched_lookup(const int32_t* __restrict__ counts, int E, int NT, int 
     const int src = __builtin_ctzll(m);
     *start = __shfl(st, src, kWave);
     return src * 4 + __shfl(hit, src, kWave);
+}
+
+// Number of tiles of the pipelined kernel's schedule with at most 128 rows
+// (the short-tile layouts).  All lanes of the wave must call it.
+MOE_DEV int count_short_tiles(const int32_t* __restrict__ counts, int E, int NT, int rows, int lane) {
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane * 4 + j;
+        const int c = e < E ? min(max(counts[e], 0), rows) : 0;
+        const int rem = c % kBM256;
+        n += (rem > 0 && rem <= 128) ? NT : 0;
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) n += __shfl_xor(n, o, kWave);
+    return uniform(n);
 }
 
 // Rows and columns of pipelined-kernel tile `tile` (wave-uniform results).
@@ -314,6 +339,97 @@ MOE_DEV void store_rows(const f32x16 (&a)[4], int mi, uint16_t* __restrict__ C, 
     }
 }
 
+// The same output through LDS, for whole tiles: the slice (32 rows of the
+// wave's 128 x 128 quadrant) is written to the wave's own 8 KB of stage 0 --
+// the parts of it that only this wave's DMAs fill, so no other wave's reads
+// or loads touch them -- and read back as 16-byte pieces of whole row
+// segments, so that each store instruction writes 4 rows of 256 bytes (8 rows
+// of 128 bytes for the SwiGLU GEMM) instead of 32 rows of 16 bytes.  Staged
+// rows are XOR-swizzled by 16-byte piece so that writes and reads are free of
+// bank conflicts.  Every wave must be done reading the stages, and this wave's
+// own loads into them must be complete.
+template <bool DUAL>
+MOE_DEV void store_rows_lds(const f32x16 (&a)[4], int mi, char* smem, uint16_t* __restrict__ C, int r0,
+                            int rows_valid, int n0, int N, int wave, int wm, int wn) {
+    int lane = __lane_id();
+    __asm__ volatile("" : "+v"(lane));
+    const int l32 = lane & 31, lh = lane >> 5;
+    constexpr int CH = DUAL ? 8 : 16;   // 16-byte pieces per staged row (64 or 128 columns)
+    constexpr int RPI = kWave / CH;     // rows per store instruction
+    // Staged row r: SwiGLU rows at wave*4K + r*128; otherwise rows 0..15 at
+    // wave*4K + r*256 and rows 16..31 at 16K + wave*4K + (r-16)*256.
+    auto row_at = [&](int r) -> char* {
+        return DUAL ? smem + wave * 4096 + r * 128
+                    : smem + (r >> 4) * 16384 + wave * 4096 + (r & 15) * 256;
+    };
+    auto swz = [](int r, int c) { return DUAL ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15)); };
+    char* wr = row_at(l32);
+#pragma unroll
+    for (int ni = 0; ni < (DUAL ? 2 : 4); ++ni) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[j] = a[ni][q * 4 + j];
+                if (DUAL) v[j] = silu_mul(v[j], a[ni + 2][q * 4 + j]);
+            }
+            uint2 pk;
+            pk.x = pack_bf16x2(v[0], v[1]);
+            pk.y = pack_bf16x2(v[2], v[3]);
+            const int c = ni * 4 + q;  // column (ni*32 + q*8 + lh*4) / 8
+            *reinterpret_cast<uint2*>(wr + swz(l32, c) * 16 + lh * 8) = pk;
+        }
+    }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int c = lane % CH;
+    const int colb = n0 + (DUAL ? wn * 64 : wn * 128) + c * 8;
+    u32x4 val[32 / RPI];
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = i * RPI + lane / CH;
+        val[i] = *reinterpret_cast<const u32x4*>(row_at(r) + swz(r, c) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = i * RPI + lane / CH;
+        const int m = wm * 128 + mi * 32 + r;
+        if (m < rows_valid) *reinterpret_cast<u32x4*>(C + (size_t)(r0 + m) * N + colb) = val[i];
+    }
+}
+
+// Output of row slice mi of a short tile (rows mi*32 .. mi*32+31, all four
+// waves): wave w holds output columns w*32.. (SwiGLU: a[0] the W1 part, a[1]
+// the W3 part) or w*64 + ni*32.. (plain GEMM).
+template <bool DUAL>
+MOE_DEV void store_rows_short(const f32x16 (&a)[2], int mi, uint16_t* __restrict__ C, int r0, int rows_valid,
+                              int n0, int N, int wave) {
+    int lane = __lane_id();
+    __asm__ volatile("" : "+v"(lane));
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int m = mi * 32 + l32;
+    if (m < rows_valid) {
+        uint16_t* crow = C + (size_t)(r0 + m) * N;
+#pragma unroll
+        for (int ni = 0; ni < (DUAL ? 1 : 2); ++ni) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[j] = a[ni][q * 4 + j];
+                    if (DUAL) v[j] = silu_mul(v[j], a[1][q * 4 + j]);
+                }
+                const int col = n0 + (DUAL ? wave * 32 : wave * 64 + ni * 32) + q * 8 + lh * 4;
+                uint2 pk;
+                pk.x = pack_bf16x2(v[0], v[1]);
+                pk.y = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<uint2*>(crow + col) = pk;
+            }
+        }
+    }
+}
+
 // Slot layout: per wave 16 fragments of 16 floats per lane, as float4 vectors
 // [wave][fragment][quarter][lane], so that each store and load is 1 KB per wave.
 MOE_DEV size_t part_index(int wave, int f, int q, int lane) {
@@ -324,7 +440,7 @@ template <bool DUAL>
 __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    int E, int Kd, int N, int rows, float* __restrict__ part) {
+    int E, int Kd, int N, int rows, float* __restrict__ part, int* __restrict__ ticket_ctr) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     constexpr int OUTW = DUAL ? 128 : 256;
@@ -339,6 +455,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     int total = 0, first = 0;
     sched_lookup(counts, E, NT, rows, lane, -1, &first, &total);
     total = uniform(total);
+    // Claim tiles from the counters only when at least one tile in eight is
+    // short.  With tiles of equal length the fixed order keeps the 32
+    // workgroups of an XCD in step along K, so that they share the K-slices
+    // of their panels in L2; claiming staggers them and costs a few percent.
+    int* const tickets = (ticket_ctr != nullptr && 8 * count_short_tiles(counts, E, NT, rows, lane) > total)
+                             ? ticket_ctr : nullptr;
 
     // LDS fragment addresses (byte offsets into a stage).
     // A row r, k-chunk c of 8 elements sits at r*64 + ((c ^ ((r/4)%4)) * 16).
@@ -365,29 +487,63 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     const int KT = Kd / kP4BK;
     const SplitPlan sp = split_plan(total, G, KT, part != nullptr);
     const int whole = sp.S > 1 ? sp.R * G : total;  // tiles computed in one piece
-    for (int round = 0;; ++round) {
-        int tile = round * G + xcd * per_xcd + slot;
+    // Work item j of this XCD is round j / per_xcd, slot j % per_xcd.  Without
+    // tickets, workgroup `slot` of the XCD takes items slot, slot + per_xcd, ...;
+    // with them, the XCD's workgroups claim its items in order from the XCD's
+    // counter, so that a workgroup that drew short tiles takes more.  Thread 0
+    // claims the next item as soon as a tile starts (the atomic's latency hides
+    // under the K-loop) and passes it on after the K-loop.
+    int j = slot;
+    int claimed = 0;  // thread 0 only
+    auto claim = [&]() {
+        if (tid == 0) claimed = atomicAdd(tickets + xcd * 16, 1);
+    };
+    // Hands thread 0's claim to every wave through a word of the last stage.
+    // The first barrier retires every read of the stages; the word is read
+    // before the next tile's first in-loop barrier, and only the refill after
+    // that barrier writes the last stage again.
+    auto take = [&]() -> int {
+        __syncthreads();
+        if (tid == 0) *reinterpret_cast<volatile int*>(smem + kP4TicketOff) = claimed;
+        __syncthreads();
+        return uniform(*reinterpret_cast<volatile int*>(smem + kP4TicketOff));
+    };
+    if (tickets != nullptr) {
+        claim();
+        j = take();
+    }
+    for (;;) {
+        const int round = j / per_xcd, jslot = j - round * per_xcd;
+        int tile = round * G + xcd * per_xcd + jslot;
         int ks0 = 0, ksn = KT;  // K-steps of this work item
         int pslot = -1;         // split-workspace slot of a tile part
         if (tile >= whole) {
             if (sp.S == 1 || round != sp.R) break;
-            const int p = xcd * per_xcd + slot;
+            const int p = xcd * per_xcd + jslot;
             if (p >= sp.Tr * sp.S) break;
             tile = whole + p / sp.S;
-            const int j = p % sp.S, q = KT / 4;
-            ks0 = (j * q / sp.S) * 4;
-            ksn = ((j + 1) * q / sp.S) * 4 - ks0;
+            const int pj = p % sp.S, q = KT / 4;
+            ks0 = (pj * q / sp.S) * 4;
+            ksn = ((pj + 1) * q / sp.S) * 4 - ks0;
             pslot = p;
         }
         TileGeom tg;
         if (!tile_geom(counts, offsets, E, NT, OUTW, rows, lane, tile, tg)) break;
         const int e = tg.e, r0 = tg.r0, rows_valid = tg.rows_valid, n0 = tg.n0;
-        if (rows_valid <= 0) continue;
+        if (tickets != nullptr) claim();
+        int j_next = j + per_xcd;
+        if (rows_valid <= 0) {
+            j = tickets != nullptr ? take() : j_next;
+            continue;
+        }
 
-        // The tile body, instantiated twice so that the partial-slot epilogue of
-        // the split round does not weigh on the register allocation of the rest.
-        auto run_tile = [&](auto part_tag) {
+        // The tile body, instantiated per case so that neither the partial-slot
+        // epilogue of the split round nor the short-tile layouts weigh on the
+        // register allocation of the full tile.  MI == 0: full 256-row layout;
+        // MI > 0: short tile of at most 32 * MI rows (see below).
+        auto run_tile = [&](auto part_tag, auto mi_tag) {
             constexpr bool PART = decltype(part_tag)::value;
+            constexpr int MI = decltype(mi_tag)::value;
             // DMA sources.  A: 16 rows of 64 bytes per KB; rows past the segment are
             // clamped to its last row.  B: 4 k-rows of one 128-column half per KB.
             const rsrc_t ra = make_rsrc(A + (size_t)r0 * Kd);
@@ -419,6 +575,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                 for (int i = 0; i < 8; ++i) issue_one(kt, soff, i);
             };
 
+            if constexpr (MI == 0) {
             f32x16 acc[4][4];
     #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
@@ -504,6 +661,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
             }
             // The clamped refills of the last steps are still in flight.
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // Every wave is done reading the stages (the staged epilogue below
+            // reuses them).
+            if (tickets != nullptr) j_next = take();
+            else __syncthreads();
 
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
@@ -518,12 +679,85 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                             dst[(ni * 4 + q) * kWave] = f32x4{av[q * 4], av[q * 4 + 1], av[q * 4 + 2], av[q * 4 + 3]};
                         }
                 } else {
-                    store_rows<DUAL>(acc[mi], mi, C, r0, rows_valid, n0, N, wm, wn);
+                    store_rows_lds<DUAL>(acc[mi], mi, smem, C, r0, rows_valid, n0, N, wave, wm, wn);
                 }
             }
+            } else {
+            // Short tile: every row sits in the first 32 * MI.  The four waves
+            // share those rows and each takes a quarter of the columns (the W1
+            // and W3 halves of 32 output columns for the SwiGLU GEMM, 64
+            // columns otherwise), so only row slices that hold rows are
+            // multiplied.  Stages, DMA, waits and barriers are the full tile's.
+            int sa_rd[2], sb_rd[2];
+    #pragma unroll
+            for (int ks = 0; ks < 2; ++ks) sa_rd[ks] = l32 * 64 + (((ks * 2 + lh) ^ ((l32 >> 2) & 3)) << 4);
+    #pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                const int sh = DUAL ? ni : (wave >> 1);
+                const int nn = DUAL ? wave * 32 : (wave & 1) * 64 + ni * 32;
+                sb_rd[ni] = b_lane + sh * 8192 + ((((nn >> 3) ^ b_x) + b_c) << 4);
+            }
+            f32x16 acc[MI][2];
+    #pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+    #pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+    #pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+            bf16x8 af[2][MI], bfr[2][2];
+            auto load_frags = [&](int soff, int ks, int buf) {
+                const char* sa = smem + soff + sa_rd[ks];
+    #pragma unroll
+                for (int mi = 0; mi < MI; ++mi) af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * 64);
+    #pragma unroll
+                for (int ni = 0; ni < 2; ++ni) {
+                    const char* pb = smem + soff + sb_rd[ni] + ks * 16 * 256;
+                    const bf16x4 h0 = lds_read_tr(pb);
+                    const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
+                    bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            };
+            auto mfma = [&](int buf) {
+    #pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+    #pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
+            };
+            issue(0, 0);
+            issue(1, kP4Stage);
+            issue(2, 2 * kP4Stage);
+            issue(3, 3 * kP4Stage);
+            __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
+            __syncthreads();
+            load_frags(0, 0, 0);
+            int s_cur = 0;
+            for (int kt = 0; kt < ksn; ++kt) {
+                const int s_nxt = s_cur == (kP4Stages - 1) * kP4Stage ? 0 : s_cur + kP4Stage;
+                const int s_old = s_cur == 0 ? (kP4Stages - 1) * kP4Stage : s_cur - kP4Stage;
+                __builtin_amdgcn_sched_barrier(0);
+                __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+                __syncthreads();
+                issue(min(kt + 4, ksn - 1), s_old);
+                load_frags(s_cur, 1, 1);
+                mfma(0);
+                load_frags(s_nxt, 0, 0);
+                mfma(1);
+                s_cur = s_nxt;
+            }
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (tickets != nullptr) j_next = take();
+    #pragma unroll
+            for (int mi = 0; mi < MI; ++mi) store_rows_short<DUAL>(acc[mi], mi, C, r0, rows_valid, n0, N, wave);
+            }
         };
-        if (pslot >= 0) run_tile(std::true_type{});
-        else run_tile(std::false_type{});
+        using Full = std::integral_constant<int, 0>;
+        if (pslot >= 0) run_tile(std::true_type{}, Full{});
+        else if (rows_valid <= 32) run_tile(std::false_type{}, std::integral_constant<int, 1>{});
+        else if (rows_valid <= 64) run_tile(std::false_type{}, std::integral_constant<int, 2>{});
+        else if (rows_valid <= 128) run_tile(std::false_type{}, std::integral_constant<int, 4>{});
+        else run_tile(std::false_type{}, Full{});
+        j = j_next;
     }
 }
 
@@ -573,6 +807,11 @@ __global__ __launch_bounds__(kThreads) void ffn_split_fixup(const float* __restr
         }
         store_rows<DUAL>(acc, mi, C, tg.r0, tg.rows_valid, tg.n0, N, wm, wn);
     }
+}
+
+// Clears the claim counters before a launch of the pipelined kernel.
+__global__ void zero_ints(int* __restrict__ p, int n) {
+    if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
 }
 
 // fp32 tile kernel (plain FMA): block tile 64 x 64 x 16, each thread 4 x 4 outputs.
@@ -675,8 +914,11 @@ static bool ffn_pipelined_ok(int d, int n) { return d % 256 == 0 && n % 128 == 0
 
 static int ffn_grid() { return (device_cu_count() / 8) * 8; }
 
+// Split slots for every workgroup, then the claim counters.
 size_t ffn_split_bytes(int dtype, int d, int n) {
-    return (dtype == 1 && ffn_pipelined_ok(d, n)) ? (size_t)ffn_grid() * kPartFloats * sizeof(float) : 0;
+    return (dtype == 1 && ffn_pipelined_ok(d, n))
+               ? (size_t)ffn_grid() * kPartFloats * sizeof(float) + kTicketInts * sizeof(int)
+               : 0;
 }
 
 // One pipelined GEMM (SwiGLU or plain), then the fixup of its split tail.
@@ -688,8 +930,10 @@ static hipError_t launch_pipelined(const uint16_t* A, const uint16_t* B0, const 
         hipFuncSetAttribute((const void*)ffn_p4_kernel<DUAL>, hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
     if (aerr != hipSuccess) return aerr;
     const int G = ffn_grid();
+    int* tickets = part != nullptr ? reinterpret_cast<int*>(part + (size_t)G * kPartFloats) : nullptr;
+    if (tickets != nullptr) hipLaunchKernelGGL(zero_ints, dim3(1), dim3(kTicketInts), 0, s, tickets, kTicketInts);
     hipLaunchKernelGGL(ffn_p4_kernel<DUAL>, dim3(G), dim3(kThreads), kP4Lds, s, A, B0, B1, C, counts, offsets, E, Kd,
-                       N, rows, part);
+                       N, rows, part, tickets);
     if (part != nullptr)
         hipLaunchKernelGGL(ffn_split_fixup<DUAL>, dim3(G), dim3(kThreads), 0, s, part, C, counts, offsets, E, Kd, N,
                            rows, G);

@@ -31,7 +31,8 @@ hipError_t launch_copy_rows(const void* X, size_t row_bytes, int T, int K, const
 
 // Step 4.  dtype: 0 = fp32, 1 = bf16.  4a (SwiGLU GEMM), 4b (down GEMM), both.
 // `part` (nullable) is the split workspace of ffn_split_bytes() bytes: with it,
-// the last partial round of tiles is split over the idle workgroups along K.
+// the last partial round of tiles is split over the idle workgroups along K,
+// and tiles are claimed from per-XCD counters kept at its end.
 size_t ffn_split_bytes(int dtype, int d, int n);
 hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int rows, int d, int E,
                          int n, const int32_t* counts, const int32_t* offsets, void* Act, float* part,

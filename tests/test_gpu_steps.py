@@ -7,7 +7,7 @@ import torch
 import mixture_experts_routing_gate_amd as moe
 import oracle
 import synth
-from parity_util import check_close, check_equal, cuda, from_np, to_np
+from parity_util import as_f64, check_close, check_equal, cuda, from_np, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -181,3 +181,37 @@ def test_ffn_split_tail_matches_unsplit_and_oracle(cfg):
     # split and unsplit differ only by fp32 summation order before one bf16 rounding
     da = (act_s.float() - act_u.float()).abs().max().item()
     assert da <= 2e-2 * act_u.float().abs().max().item(), da
+
+
+# Expert row counts that give every tile height of the pipelined bf16 kernel
+# (d % 256 == 0, n % 128 == 0): remainder tiles of 1..32, 33..64 and 65..128
+# rows, full-height tiles, several tiles per expert, and an empty expert.
+SHORT_TILE_COUNTS = [1, 31, 32, 33, 64, 65, 100, 128, 129, 200, 256, 257, 300, 0, 520]
+
+
+@pytest.mark.parametrize("split", [False, True], ids=["whole", "split"])
+def test_grouped_ffn_short_tiles(split):
+    counts = SHORT_TILE_COUNTS
+    E = len(counts)
+    cfg = synth.MoEConfig("short_tiles", T=sum(counts), d=256, E=E, K=1, n=256)
+    idx = forced_counts_idx(counts)
+    c = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+    assert list(c) == counts
+    off = np.concatenate([[0], np.cumsum(c)]).astype(np.int32)
+    sp, inv = oracle.permute(idx, E)
+    inp = synth.make_inputs(cfg, "cpu", 3)
+    Xp = oracle.gather_rows(to_np(inp["X"]), sp, 1)
+    re = idx.ravel()[sp]
+    Act, Y = moe.moe_grouped_ffn(cuda(from_np(Xp)), cuda(inp["W1"]), cuda(inp["W3"]), cuda(inp["W2"]),
+                                 cuda(torch.from_numpy(c)), cuda(torch.from_numpy(off)), 1, split=split)
+    torch.cuda.synchronize()
+    ract, ry = oracle.expert_ffn(Xp, re, to_np(inp["W1"]), to_np(inp["W3"]), to_np(inp["W2"]))
+    check_close(Act, ract, cfg.dtype, "Act")
+    check_close(Y, ry, cfg.dtype, "Y")
+    # row by row (relative L2 of each row), so that a wrong row or column slice
+    # of a short tile cannot hide in the whole-tensor norms
+    for name, o, r in (("Act", as_f64(Act), as_f64(ract)), ("Y", as_f64(Y), as_f64(ry))):
+        rel = np.linalg.norm(o - r, axis=1) / np.linalg.norm(r, axis=1)
+        bad = np.flatnonzero(rel > 1e-2)
+        assert bad.size == 0, (name, [(int(np.searchsorted(off, b, "right") - 1), int(b)) for b in bad[:8]],
+                               rel[bad[:8]])
