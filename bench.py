@@ -66,6 +66,25 @@ def event_time_ms(torch, fn, iters, flush=None):
     return statistics.median(times), times
 
 
+def b2b_time_ms(torch, fn, n=20, reps=3):
+    """Per-call time of n calls issued back to back (best of `reps`), from HIP
+    events on the current stream: the steady-state rate without the launch
+    latency that a single timed call includes."""
+    fn()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(n):
+            fn()
+        e.record()
+        e.synchronize()
+        best = min(best, s.elapsed_time(e) / n)
+    return best
+
+
 def kernel_traffic(workload, kernel):
     """Calibrated bytes per launch of `kernel` from the committed rocprofv3
     counter table (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when
@@ -169,6 +188,8 @@ def main():
     up_flops = 4.0 * A * d * n
     up_tflops = up_flops / (up_ms * 1e-3) / 1e12
     c_ms, _ = event_time_ms(torch, lambda: moe.moe_combine(Y, w, inv), 20)
+    p_b2b = b2b_time_ms(torch, lambda: moe.moe_permute(g["X"], idx, E))
+    c_b2b = b2b_time_ms(torch, lambda: moe.moe_combine(Y, w, inv))
     s = 2  # bf16 bytes
     perm_bytes = T * (s * d * (1 + K) + 12 * K)
     comb_bytes = T * (s * d * (K + 1) + 8 * K)
@@ -224,12 +245,16 @@ def main():
         "steps_us": {
             "route": {"us": r_ms * 1e3, "GB/s": route_bytes / (r_ms * 1e-3) / 1e9},
             "permute": {"us": p_ms * 1e3, "GB/s": perm_bytes / (p_ms * 1e-3) / 1e9,
-                        "frac_hbm": perm_bytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                        "frac_hbm": perm_bytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "us_back_to_back": p_b2b * 1e3,
+                        "frac_hbm_back_to_back": perm_bytes / (p_b2b * 1e-3) / 1e9 / PEAK_HBM_GBS},
             "grouped_ffn": {"us": f_ms * 1e3, "TFLOPS": ffn_tflops},
             "ffn_up": {"us": up_ms * 1e3, "TFLOPS": up_tflops},
             "ffn_down": {"us": dn_ms * 1e3, "TFLOPS": 2.0 * A * d * n / (dn_ms * 1e-3) / 1e12},
             "combine": {"us": c_ms * 1e3, "GB/s": comb_bytes / (c_ms * 1e-3) / 1e9,
-                        "frac_hbm": comb_bytes / (c_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                        "frac_hbm": comb_bytes / (c_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "us_back_to_back": c_b2b * 1e3,
+                        "frac_hbm_back_to_back": comb_bytes / (c_b2b * 1e-3) / 1e9 / PEAK_HBM_GBS},
         },
         "roofline": {"kernel": "ffn_p4_kernel<true> (moe_ffn_up: Act = SiLU(Xp W1) * (Xp W3), one launch)",
                      "bound": "mfma", "achieved": round(up_tflops, 2), "peak": PEAK_BF16_TFLOPS,

@@ -26,6 +26,12 @@ hipError_t launch_scan(const int32_t* blk, int B, int E, int32_t* counts, int32_
 hipError_t launch_chunk_hist(const int32_t* idx, int T, int E, int K, int32_t* blk, hipStream_t s);
 hipError_t launch_rank(const int32_t* idx, int T, int E, int K, const int32_t* blkbase,
                        int32_t* sorted_pair, int32_t* inv, hipStream_t s);
+// Scan and rank in one launch: each rank workgroup scans blk[B,E] itself
+// (worth it while B*E is small, see scan_rank_fused()); counts and offsets are
+// written when not null.
+hipError_t launch_scan_rank(const int32_t* idx, int T, int E, int K, const int32_t* blk, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted_pair, int32_t* inv, hipStream_t s);
+inline bool scan_rank_fused(int T, int E) { return (long long)num_chunks(T) * E <= 16384; }
 hipError_t launch_copy_rows(const void* X, size_t row_bytes, int T, int K, const int32_t* inv,
                             void* Xp, hipStream_t s);
 

@@ -237,8 +237,12 @@ int moe_permute(const void* X, int dtype, int T, int d, int E, int K, const int3
     int32_t* cnt = c.take<int32_t>(E);
     int32_t* off = c.take<int32_t>(E + 1);
     HIPCHECK(launch_chunk_hist(topk_idx, T, E, K, blk, s));
-    HIPCHECK(launch_scan(blk, B, E, cnt, off, blkbase, s));
-    HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s));
+    if (scan_rank_fused(T, E)) {
+        HIPCHECK(launch_scan_rank(topk_idx, T, E, K, blk, nullptr, nullptr, sorted_pair, inv, s));
+    } else {
+        HIPCHECK(launch_scan(blk, B, E, cnt, off, blkbase, s));
+        HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s));
+    }
     HIPCHECK(launch_copy_rows(X, (size_t)d * elem_bytes(dtype), T, K, inv, Xp, s));
     return MOE_OK;
 }
@@ -377,8 +381,12 @@ int moe_forward(const void* X, const float* logits, const void* W1, const void* 
     if (!inv) inv = ws_inv;
 
     HIPCHECK(launch_gate(logits, T, E, K, topk_idx, topk_w, blk, s));
-    HIPCHECK(launch_scan(blk, B, E, counts, offsets, blkbase, s));
-    HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s));
+    if (scan_rank_fused(T, E)) {
+        HIPCHECK(launch_scan_rank(topk_idx, T, E, K, blk, counts, offsets, sorted_pair, inv, s));
+    } else {
+        HIPCHECK(launch_scan(blk, B, E, counts, offsets, blkbase, s));
+        HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s));
+    }
     HIPCHECK(launch_copy_rows(X, (size_t)d * sz, T, K, inv, Xp, s));
     HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, (int)A, d, E, n, counts, offsets, Act, Yb, part, s));
     HIPCHECK(launch_combine(Yb, topk_w, inv, dtype, T, d, K, out, s));

@@ -40,9 +40,19 @@ __global__ __launch_bounds__(kThreads) void chunk_hist_kernel(const int32_t* __r
 // wave w sets bit `lane` of mask[w][e] for each expert e its token selected.
 // Position of (t,k) = base(chunk,e) + earlier sub-chunks + earlier waves +
 // popcount(mask[w][e] & lanes below).
+//
+// base(chunk,e) comes from blkbase when it is given.  Otherwise (small B*E)
+// every workgroup does the scan of step 2 itself from the per-chunk counts
+// blk[B,E]: thread e adds expert e over all chunks (its count) and over the
+// chunks before this one, then an exclusive scan over experts gives offsets.
+// Workgroup 0 writes counts and offsets when they are not null.  The sums are
+// of integers, so every workgroup gets the same values in any order.
 __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restrict__ idx, int T, int E,
                                                         int K, int CH,
                                                         const int32_t* __restrict__ blkbase,
+                                                        const int32_t* __restrict__ blk, int B,
+                                                        int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ sorted_pair,
                                                         int32_t* __restrict__ inv) {
     __shared__ unsigned long long mask[kWaves][256];
@@ -52,8 +62,48 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int chunk = blockIdx.x;
+    if (blkbase != nullptr) {
+        for (int e = tid; e < E; e += kThreads) run[e] = blkbase[(size_t)chunk * E + e];
+    } else {  // E <= 256 == kThreads: thread e owns expert e
+        constexpr int kBatch = 16;
+        int tot = 0, below = 0;
+        if (tid < E) {
+            for (int b0 = 0; b0 < B; b0 += kBatch) {
+                int x[kBatch];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) x[i] = blk[(size_t)min(b0 + i, B - 1) * E + tid];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) {
+                    const int v = (b0 + i < B) ? x[i] : 0;
+                    tot += v;
+                    below += (b0 + i < chunk) ? v : 0;
+                }
+            }
+        }
+        int* sc0 = pre[0];
+        int* sc1 = pre[1];
+        sc0[tid] = tot;
+        __syncthreads();
+        for (int sh = 1; sh < 256; sh <<= 1) {  // inclusive scan over experts
+            const int x = sc0[tid] + (tid >= sh ? sc0[tid - sh] : 0);
+            __syncthreads();
+            sc1[tid] = x;
+            __syncthreads();
+            int* t = sc0;
+            sc0 = sc1;
+            sc1 = t;
+        }
+        if (tid < E) {
+            const int excl = sc0[tid] - tot;
+            run[tid] = excl + below;
+            if (chunk == 0 && counts != nullptr) counts[tid] = tot;
+            if (chunk == 0 && offsets != nullptr) {
+                offsets[tid] = excl;
+                if (tid == E - 1) offsets[E] = sc0[tid];
+            }
+        }
+    }
     for (int e = tid; e < E; e += kThreads) {
-        run[e] = blkbase[(size_t)chunk * E + e];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) mask[w][e] = 0ull;
     }
@@ -156,7 +206,16 @@ hipError_t launch_chunk_hist(const int32_t* idx, int T, int E, int K, int32_t* b
 hipError_t launch_rank(const int32_t* idx, int T, int E, int K, const int32_t* blkbase,
                        int32_t* sorted_pair, int32_t* inv, hipStream_t s) {
     hipLaunchKernelGGL(rank_kernel, dim3(num_chunks(T)), dim3(kThreads), 0, s, idx, T, E, K,
-                       chunk_tokens(T), blkbase, sorted_pair, inv);
+                       chunk_tokens(T), blkbase, static_cast<const int32_t*>(nullptr), 0,
+                       static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr), sorted_pair, inv);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_rank(const int32_t* idx, int T, int E, int K, const int32_t* blk, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted_pair, int32_t* inv, hipStream_t s) {
+    hipLaunchKernelGGL(rank_kernel, dim3(num_chunks(T)), dim3(kThreads), 0, s, idx, T, E, K,
+                       chunk_tokens(T), static_cast<const int32_t*>(nullptr), blk, num_chunks(T), counts,
+                       offsets, sorted_pair, inv);
     return hipGetLastError();
 }
 

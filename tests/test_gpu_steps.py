@@ -41,6 +41,8 @@ PERMUTE_CASES = [
     synth.MoEConfig("p3", T=1000, d=384, E=64, K=4, n=128, logits="bias", bias_var=2.0),
     synth.MoEConfig("p4", T=513, d=128, E=256, K=8, n=128, dtype="f32"),
     synth.MoEConfig("p5", T=70001, d=128, E=16, K=2, n=128),
+    # many chunks times many experts: the scan runs as its own launch
+    synth.MoEConfig("p6", T=70001, d=128, E=256, K=2, n=128),
 ]
 
 
