@@ -53,8 +53,10 @@ def _load():
         lib.oracle_combine.argtypes = [P, P, P, I, I, I, P]
         lib.oracle_expert_down.argtypes = [P, I, I, P, P, I, I, I, P]
         lib.oracle_layer.argtypes = [P, I, P, P, P, P, I, I, I, I, I, P, I, P]
+        lib.oracle_router.argtypes = [P, I, P, P, I, I, I, P]
         for f in (lib.oracle_softmax, lib.oracle_route, lib.oracle_permute, lib.oracle_gather_rows,
-                  lib.oracle_expert_ffn, lib.oracle_combine, lib.oracle_layer, lib.oracle_expert_down):
+                  lib.oracle_expert_ffn, lib.oracle_combine, lib.oracle_layer, lib.oracle_expert_down,
+                  lib.oracle_router):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -78,6 +80,21 @@ def _storage(x: np.ndarray):
     if x.dtype == np.uint16:
         return np.ascontiguousarray(x), BF16
     return np.ascontiguousarray(x, dtype=np.float32), F32
+
+
+def router(X, Wr, bias=None) -> np.ndarray:
+    """Router logits X @ Wr (+ bias), fp64 sums rounded to fp32.  -> float32 [T, E]."""
+    Xs, dt = _storage(X)
+    W = _c(Wr, np.float32)
+    T, d = Xs.shape
+    d_, E = W.shape
+    assert d_ == d
+    b = None if bias is None else _c(bias, np.float32)
+    assert b is None or b.shape == (E,)
+    out = np.empty((T, E), np.float32)
+    _check(_load().oracle_router(_ptr(Xs), dt, _ptr(W), None if b is None else _ptr(b), T, d, E, _ptr(out)),
+           "oracle_router")
+    return out
 
 
 def softmax(logits: np.ndarray) -> np.ndarray:

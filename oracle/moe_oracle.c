@@ -285,3 +285,25 @@ int oracle_layer(const void* X, int dtype, const float* logits, const void* W1, 
     }
     return bad ? -1 : 0;
 }
+
+/* Router projection, the step upstream of the gate: page [P1] section 2.1
+ * starts its fused flow from the logit computation, and page [P2] section 6
+ * computes the gate logits with a linear layer over the token's features.
+ * logits[t,e] = sum_i X[t,i] * Wr[i,e] (+ bias[e] when bias is not NULL),
+ * summed in fp64 in index order, bias added last, rounded once to fp32.
+ * X is [T,d] in dtype; Wr is [d,E] fp32; bias is [E] fp32. */
+int oracle_router(const void* X, int dtype, const float* Wr, const float* bias, int T, int d, int E,
+                  float* logits) {
+    if (!X || !Wr || !logits || T < 0 || d < 1 || E < 1) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int i = 0; i < d; ++i) s += load_elem(X, dtype, (size_t)t * d + i) * (double)Wr[(size_t)i * E + e];
+            if (bias) s += (double)bias[e];
+            logits[(size_t)t * E + e] = (float)s;
+        }
+    }
+    return 0;
+}

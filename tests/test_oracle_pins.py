@@ -339,3 +339,47 @@ def test_expert_down_matches_expert_ffn_and_matmul(oracle_lib):
     W2b = _rng(84).integers(0x3000, 0x3c00, size=(E, n, d)).astype(np.uint16)
     np.testing.assert_array_equal(oracle.expert_down(ab, re, W2b),
                                   oracle.expert_down(oracle.bf16_to_f32(ab), re, oracle.bf16_to_f32(W2b)))
+
+
+# ---- router projection (logits = X @ Wr + bias) ----
+
+def test_router_matches_library_matmul(oracle_lib):
+    """fp64 library matmul (a different summation order) agrees to fp32 rounding."""
+    rng = np.random.default_rng(7)
+    X = rng.normal(size=(37, 96)).astype(np.float32)
+    W = (rng.normal(size=(96, 12)) / np.sqrt(96)).astype(np.float32)
+    b = rng.normal(size=12).astype(np.float32)
+    got = oracle.router(X, W, b).astype(np.float64)
+    ref = X.astype(np.float64) @ W.astype(np.float64) + b.astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -23 * np.abs(ref) + 1e-30)
+    got0 = oracle.router(X, W).astype(np.float64)
+    ref0 = X.astype(np.float64) @ W.astype(np.float64)
+    assert np.all(np.abs(got0 - ref0) <= 2.0 ** -23 * np.abs(ref0) + 1e-30)
+
+
+def test_router_one_hot_rows_and_columns(oracle_lib):
+    """A unit row of X picks a row of Wr exactly (plus the bias); a unit column of
+    Wr copies a column of X exactly.  A transposed Wr index or a dropped bias fails."""
+    rng = np.random.default_rng(8)
+    d, E = 24, 5
+    W = rng.normal(size=(d, E)).astype(np.float32)
+    b = np.array([0.5, -1.0, 2.0, 0.0, 3.25], np.float32)
+    X = np.zeros((d, d), np.float32)
+    X[np.arange(d), np.arange(d)] = 1.0
+    lg = oracle.router(X, W, b)
+    assert np.array_equal(lg, (W.astype(np.float64) + b).astype(np.float32))
+    Xr = rng.normal(size=(9, d)).astype(np.float32)
+    Wc = np.zeros((d, E), np.float32)
+    for e in range(E):
+        Wc[(3 * e + 1) % d, e] = 1.0
+    lg2 = oracle.router(Xr, Wc)
+    for e in range(E):
+        assert np.array_equal(lg2[:, e], Xr[:, (3 * e + 1) % d])
+
+
+def test_router_bf16_input_widens_exactly(oracle_lib):
+    rng = np.random.default_rng(9)
+    Xf = rng.normal(size=(11, 64)).astype(np.float32)
+    Xb = synth.to_numpy(torch.from_numpy(Xf).to(torch.bfloat16))
+    W = rng.normal(size=(64, 8)).astype(np.float32)
+    assert np.array_equal(oracle.router(Xb, W), oracle.router(oracle.bf16_to_f32(Xb), W))
