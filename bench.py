@@ -188,6 +188,12 @@ def main():
     up_flops = 4.0 * A * d * n
     up_tflops = up_flops / (up_ms * 1e-3) / 1e12
     c_ms, _ = event_time_ms(torch, lambda: moe.moe_combine(Y, w, inv), 20)
+    # Router projection upstream of the gate (logits = X Wr for this workload).
+    Wr, rb = synth.make_router(cfg, dev, seed=0)
+    rws = torch.empty(max(moe.load_library().moe_router_workspace_bytes(d, E, 1), 1), dtype=torch.uint8, device=dev)
+    rt_ms, _ = event_time_ms(torch, lambda: moe.moe_router(g["X"], Wr, rb, ws=rws), 20)
+    rt_b2b = b2b_time_ms(torch, lambda: moe.moe_router(g["X"], Wr, rb, ws=rws))
+    router_bytes = T * d * 2 + d * E * 4 + T * E * 4
     p_b2b = b2b_time_ms(torch, lambda: moe.moe_permute(g["X"], idx, E))
     c_b2b = b2b_time_ms(torch, lambda: moe.moe_combine(Y, w, inv))
     s = 2  # bf16 bytes
@@ -243,6 +249,8 @@ def main():
                    "active_flops_per_step": flops, "expert_counts": counts_h.tolist()},
         "gate": gate,
         "steps_us": {
+            "router": {"us": rt_ms * 1e3, "us_back_to_back": rt_b2b * 1e3,
+                       "frac_hbm_back_to_back": router_bytes / (rt_b2b * 1e-3) / 1e9 / PEAK_HBM_GBS},
             "route": {"us": r_ms * 1e3, "GB/s": route_bytes / (r_ms * 1e-3) / 1e9},
             "permute": {"us": p_ms * 1e3, "GB/s": perm_bytes / (p_ms * 1e-3) / 1e9,
                         "frac_hbm": perm_bytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -295,6 +303,19 @@ def other_workload(name, moe, synth, torch, np, dev, steps=5):
     ms = (time.perf_counter() - t0) * 1e3 / steps
     counts = plan.counts.cpu().numpy().astype(np.int64)
     A, d, n, E, K, T, s = c.T * c.K, c.d, c.n, c.E, c.K, c.T, 2
+    # the router projection and the memory-bound steps on their own, back to back
+    Wr, rb = synth.make_router(c, dev, seed=0)
+    rws = torch.empty(max(moe.load_library().moe_router_workspace_bytes(d, E, 1), 1), dtype=torch.uint8, device=dev)
+    rt = b2b_time_ms(torch, lambda: moe.moe_router(g["X"], Wr, rb, ws=rws))
+    pt = b2b_time_ms(torch, lambda: moe.moe_permute(g["X"], plan.topk_idx, E))
+    Yc = torch.zeros((A, d), dtype=c.torch_dtype, device=dev)
+    ct = b2b_time_ms(torch, lambda: moe.moe_combine(Yc, plan.topk_w, plan.inv))
+    BW = PEAK_HBM_GBS * 1e9
+    steps = {"router_us": round(rt * 1e3, 1),
+             "router_frac_of_roof": (max(2.0 * T * d * E / (PEAK_BF16_TFLOPS * 1e12),
+                                         (T * d * s + d * E * 4 + T * E * 4) / BW) * 1e3) / rt,
+             "permute_us": round(pt * 1e3, 1), "permute_frac_hbm": T * (s * d * (1 + K) + 12 * K) / BW * 1e3 / pt,
+             "combine_us": round(ct * 1e3, 1), "combine_frac_hbm": T * (s * d * (K + 1) + 8 * K) / BW * 1e3 / ct}
     e_act = int((counts > 0).sum())
     P, BW = PEAK_BF16_TFLOPS * 1e12, PEAK_HBM_GBS * 1e9
     roof_s = (T * (4 * E + 8 * K)) / BW                                                        # gate
@@ -311,9 +332,9 @@ def other_workload(name, moe, synth, torch, np, dev, steps=5):
                        + (f" (per-expert bias variance {c.bias_var})" if c.bias_var else ""),
            "ms_per_step": round(ms, 4), "TFLOPS": 6.0 * A * d * n / (ms * 1e-3) / 1e12,
            "roofline_ms": round(roof_s * 1e3, 4), "frac_of_roofline": roof_s * 1e3 / ms,
-           "experts_nonempty": e_act, "max_count": int(counts.max()),
+           "experts_nonempty": e_act, "max_count": int(counts.max()), "steps_back_to_back": steps,
            "tile_padding": padded / A - 1.0}
-    del g, plan
+    del g, plan, Yc, Wr, rb, rws
     torch.cuda.empty_cache()
     return res
 

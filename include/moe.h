@@ -74,6 +74,31 @@ size_t moe_forward_workspace_bytes(int T, int d, int E, int K, int n, int dtype)
 /* Optional workspace of moe_grouped_ffn / moe_ffn_up / moe_ffn_down on the
  * current device (0 when the sizes take no split, e.g. fp32). */
 size_t moe_ffn_workspace_bytes(int d, int n, int dtype);
+/* Workspace of moe_router (0 when none is needed: fp32 X, or d % 256 != 0). */
+size_t moe_router_workspace_bytes(int d, int E, int dtype);
+
+/* Router projection, upstream of step 1: the router logits from the tokens.
+ *   [P1] section 2.1: the fused gating flow starts from the logit
+ *   computation; [P2] section 6: the gate logits are a linear layer over the
+ *   token's features.
+ * Semantics: logits[t,e] = sum_i X[t,i] * Wr[i,e] + bias[e] (no bias term when
+ *   bias is NULL).
+ * In:  X [T,d] in dtype (row-major), Wr [d,E] fp32 (row-major: expert index
+ *      fastest), bias [E] fp32 or NULL.
+ * Out: logits [T,E] fp32, the input of moe_route / moe_forward.
+ * Precision: bf16 X with d % 256 == 0 runs on bf16 MFMA with each weight
+ *   split into two bf16 terms (hi = bf16(w), lo = bf16(w - hi), so that
+ *   |w - hi - lo| <= 2^-18 |w|) and fp32 accumulation; otherwise fp32 fused
+ *   multiply-adds in index order.  The error is that of an fp32 dot product
+ *   (over 2d terms on the MFMA path), plus at most 2^-18 * S from the split,
+ *   S = sum_i |X[t,i] Wr[i,e]|; the tests hold it to 2^-16 * S.
+ * Workspace: moe_router_workspace_bytes(d,E,dtype) bytes (the split weights,
+ *   rewritten on every call); NULL allowed when that is 0.  X and ws must be
+ *   16-byte aligned on the MFMA path.
+ * Sizes: T >= 1, d >= 1, 1 <= E <= 256, T*E < 2^31.  Deterministic.
+ */
+int moe_router(const void* X, int dtype, int T, int d, int E, const float* Wr, const float* bias,
+               float* logits, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_route -- steps 1 and 2: fused softmax top-K gate, per-expert histogram

@@ -49,6 +49,8 @@ def load_library() -> ctypes.CDLL:
         "moe_permute_workspace_bytes": ([I, I, I], Z),
         "moe_forward_workspace_bytes": ([I, I, I, I, I, I], Z),
         "moe_ffn_workspace_bytes": ([I, I, I], Z),
+        "moe_router_workspace_bytes": ([I, I, I], Z),
+        "moe_router": ([P, I, I, I, I, P, P, P, P, Z, P], I),
         "moe_route": ([P, I, I, I, P, P, P, P, P, Z, P], I),
         "moe_permute": ([P, I, I, I, I, I, P, P, P, P, P, Z, P], I),
         "moe_grouped_ffn": ([P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
@@ -102,6 +104,23 @@ def _stream(device) -> int:
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def moe_router(X: torch.Tensor, Wr: torch.Tensor, bias: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Router projection.  X [T,d] (f32/bf16), Wr [d,E] f32, bias [E] f32 or None -> logits [T,E] f32."""
+    lib = load_library()
+    T, d = X.shape
+    E = Wr.shape[1]
+    dev = X.device
+    dt = dtype_code(X.dtype)
+    wsb = lib.moe_router_workspace_bytes(d, E, dt)
+    if wsb and ws is None:
+        ws = _workspace(wsb, dev)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    _check(lib.moe_router(_dev(X, "X"), dt, T, d, E, _dev(Wr, "Wr", torch.float32),
+                          0 if bias is None else _dev(bias, "bias", torch.float32), logits.data_ptr(),
+                          0 if not wsb else ws.data_ptr(), wsb, _stream(dev)), "moe_router")
+    return logits
 
 
 def moe_route(logits: torch.Tensor, K: int):

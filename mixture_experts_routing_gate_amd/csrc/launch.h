@@ -49,6 +49,13 @@ hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void
                       int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
                       void* Act, void* Y, float* part, hipStream_t s);
 
+// Router projection upstream of step 1: logits = X Wr (+ bias).  `split` is a
+// workspace of router_split_bytes() bytes (0: none needed) for the bf16 split
+// of Wr.
+size_t router_split_bytes(int dtype, int d, int E);
+hipError_t launch_router(const void* X, int dtype, int T, int d, int E, const float* Wr, const float* bias,
+                         float* logits, void* split, hipStream_t s);
+
 // Step 5.
 hipError_t launch_combine(const void* Y, const float* w, const int32_t* inv, int dtype, int T, int d,
                           int K, void* out, hipStream_t s);

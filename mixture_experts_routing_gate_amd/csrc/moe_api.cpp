@@ -188,6 +188,11 @@ size_t moe_ffn_workspace_bytes(int d, int n, int dtype) {
     return ffn_split_bytes(dtype, d, n);
 }
 
+size_t moe_router_workspace_bytes(int d, int E, int dtype) {
+    if (check_dtype(dtype) != MOE_OK || d < 1 || E < 1 || E > kMaxE) return 0;
+    return router_split_bytes(dtype, d, E);
+}
+
 size_t moe_forward_workspace_bytes(int T, int d, int E, int K, int n, int dtype) {
     if (check_tek(T, E, K) != MOE_OK || check_dtype(dtype) != MOE_OK || check_dim("d", d, dtype) != MOE_OK ||
         check_dim("n", n, dtype) != MOE_OK)
@@ -311,6 +316,28 @@ int moe_ffn_down(const void* Act, const void* W2, int dtype, int T, int d, int E
     CHECK(ffn_split_arg(ws, ws_bytes, dtype, d, n, &part));
     HIPCHECK(launch_ffn_down(Act, W2, dtype, T * K, d, E, n, counts, offsets, Y, part,
                              static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_router(const void* X, int dtype, int T, int d, int E, const float* Wr, const float* bias,
+               float* logits, void* ws, size_t ws_bytes, void* stream) {
+    if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1 (got %d)", T);
+    if (d < 1) return fail(MOE_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+    if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1 (got %d)", E);
+    if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E=%d exceeds the supported maximum %d", E, kMaxE);
+    if ((long long)T * E >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*E must be < 2^31");
+    CHECK(check_dtype(dtype));
+    NONNULL(X);
+    NONNULL(Wr);
+    NONNULL(logits);
+    const size_t need = router_split_bytes(dtype, d, E);
+    if (need > 0) {
+        if (ws == nullptr || ws_bytes < need)
+            return fail(MOE_ERR_WORKSPACE, "moe_router needs %zu workspace bytes (got %zu)", need, ws_bytes);
+        if (!aligned16(ws) || !aligned16(X)) return fail(MOE_ERR_INVALID_ARG, "X and ws must be 16-byte aligned");
+    }
+    HIPCHECK(launch_router(X, dtype, T, d, E, Wr, bias, logits, need > 0 ? ws : nullptr,
+                           static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
 

@@ -1,0 +1,198 @@
+// Router projection, the step upstream of the gate: logits = X Wr (+ bias).
+//
+// Page [P1] "Optimising MoE with Triton: topk_gating operator fusion in
+// practice" section 2.1 starts its fused gating flow from the logit
+// computation, and page [P2] "SpMM in MoE: accelerating sparse experts with
+// Triton kernels" section 6 computes the gate logits with a linear layer over
+// the token's features.  Logits and Wr are fp32; X is the layer's dtype.
+//
+// bf16 X: a skinny GEMM (N = E <= 256) on bf16 MFMA.  Wr is fp32, so each
+// weight is split into two bf16 terms, hi = bf16(w) and lo = bf16(w - hi), and
+// both products are accumulated: |w - (hi + lo)| <= 2^-18 |w|, and the
+// products of bf16 X with either term are exact in the fp32 accumulator.
+// A prep kernel writes hi and lo transposed ([E_pad, d], k-contiguous) into the
+// workspace, so that both MFMA operands are 16-byte loads per lane.
+//
+// fp32 X, or d not a multiple of 256: one thread per output, fp32 fused
+// multiply-adds in index order.
+#include <algorithm>
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Wr [d, E] fp32 -> hi, lo [E_pad, d] bf16 (rows e >= E are zero).
+__global__ __launch_bounds__(kThreads) void router_split_kernel(const float* __restrict__ Wr, int d, int E,
+                                                                int E_pad, uint16_t* __restrict__ hi,
+                                                                uint16_t* __restrict__ lo) {
+    const size_t n = (size_t)E_pad * d;
+    for (size_t q = (size_t)blockIdx.x * kThreads + threadIdx.x; q < n; q += (size_t)gridDim.x * kThreads) {
+        const int e = (int)(q / d), i = (int)(q % d);
+        const float w = e < E ? Wr[(size_t)i * E + e] : 0.0f;
+        const uint16_t h = f32_to_bf16(w);
+        hi[q] = h;
+        lo[q] = f32_to_bf16(w - bf16_to_f32(h));
+    }
+}
+
+// Workgroup tile: 32*TG tokens x 32*NB experts; the four waves split d into
+// four quarters and their fp32 sums are added in wave order at the end (fixed
+// order: deterministic).  Each weight fragment a wave loads serves its TG
+// token groups, which cuts the L2 reads of the split weights by TG.  MFMA operands: a = 32 experts x 16 k of hi or lo,
+// b = 16 k x 32 tokens of X, both 8 consecutive k per lane; the accumulator
+// holds, in lane l, token l % 32 and experts (i/4)*8 + (l/32)*4 + i%4.
+// Workgroups of one XCD (blockIdx mod 8) take the expert groups of the same
+// token tile, so that they share its X rows in L2.
+template <int NB, int TG>
+__global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t* __restrict__ X, int T, int d,
+                                                               const uint16_t* __restrict__ hi,
+                                                               const uint16_t* __restrict__ lo,
+                                                               const float* __restrict__ bias, int E,
+                                                               int n_eg, float* __restrict__ logits) {
+    constexpr int U = TG > 1 ? 2 : 4;  // k-steps whose operands are loaded together
+    __shared__ f32x16 red[4][NB * TG][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int l32 = lane & 31, lh = lane >> 5;
+    // block b: XCD b % 8, expert group (b / 8) % n_eg, token tile from the rest
+    const int b = blockIdx.x;
+    const int eg = (b >> 3) % n_eg;
+    const int tt = (b & 7) + 8 * ((b >> 3) / n_eg);
+    const int t0 = tt * 32 * TG;
+    if (t0 >= T) return;
+    const int e0 = eg * 32 * NB;
+    const uint16_t* xr[TG];
+#pragma unroll
+    for (int g = 0; g < TG; ++g)  // rows past T are computed and discarded
+        xr[g] = X + (size_t)min(t0 + g * 32 + l32, T - 1) * d + lh * 8;
+    const size_t woff = (size_t)(e0 + l32) * d + lh * 8;
+    const int kq = d / 4;  // this wave's quarter of d
+    const int kb = wave * kq;
+
+    f32x16 acc[TG][NB];
+#pragma unroll
+    for (int g = 0; g < TG; ++g)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[g][j][i] = 0.0f;
+
+    for (int k0 = kb; k0 < kb + kq; k0 += 16 * U) {
+        bf16x8 xf[U][TG], hf[U][NB], lf[U][NB];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + u * 16;
+#pragma unroll
+            for (int g = 0; g < TG; ++g) xf[u][g] = *reinterpret_cast<const bf16x8*>(xr[g] + k);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                hf[u][j] = *reinterpret_cast<const bf16x8*>(hi + woff + (size_t)j * 32 * d + k);
+                lf[u][j] = *reinterpret_cast<const bf16x8*>(lo + woff + (size_t)j * 32 * d + k);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int g = 0; g < TG; ++g)
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf[u][j], xf[u][g], acc[g][j], 0, 0, 0);
+                    acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[u][j], xf[u][g], acc[g][j], 0, 0, 0);
+                }
+    }
+#pragma unroll
+    for (int g = 0; g < TG; ++g)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) red[wave][g * NB + j][lane] = acc[g][j];
+    __syncthreads();
+    // the NB*TG (token group, expert block) pieces are finished by the waves in turn
+    for (int pc = wave; pc < NB * TG; pc += 4) {
+        const int g = pc / NB, j = pc % NB;
+        f32x16 s = red[0][pc][lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) s += red[w][pc][lane];
+        const int t = t0 + g * 32 + l32;
+        if (t < T) {
+            float* orow = logits + (size_t)t * E;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int e = e0 + j * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+                if (e < E) orow[e] = s[i] + (bias != nullptr ? bias[e] : 0.0f);
+            }
+        }
+    }
+}
+
+// One thread per (token, expert), fp32 FMAs over d in index order.
+MOE_DEV float load_x(const float* p) { return *p; }
+MOE_DEV float load_x(const uint16_t* p) { return bf16_to_f32(*p); }
+template <typename XT>
+__global__ __launch_bounds__(kThreads) void router_fma_kernel(const XT* __restrict__ X, int T, int d,
+                                                              const float* __restrict__ Wr,
+                                                              const float* __restrict__ bias, int E,
+                                                              float* __restrict__ logits) {
+    const size_t q = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    if (q >= (size_t)T * E) return;
+    const int t = (int)(q / E), e = (int)(q % E);
+    const XT* xr = X + (size_t)t * d;
+    float s = 0.0f;
+    for (int i = 0; i < d; ++i) s = fmaf(load_x(xr + i), Wr[(size_t)i * E + e], s);
+    logits[q] = s + (bias != nullptr ? bias[e] : 0.0f);
+}
+
+int router_nb(int E) { return E <= 32 ? 1 : 2; }
+int router_tg(int E) { return E <= 32 ? 1 : 4; }  // token groups of 32 per workgroup
+
+// The MFMA kernel's four waves take d/4 each, 64 at a time.
+bool router_mfma_ok(int dtype, int d) { return dtype == 1 && d % 256 == 0; }
+
+}  // namespace
+
+size_t router_split_bytes(int dtype, int d, int E) {
+    if (!router_mfma_ok(dtype, d)) return 0;
+    const int eb = 32 * router_nb(E);
+    const size_t e_pad = (size_t)((E + eb - 1) / eb) * eb;
+    return 2 * e_pad * (size_t)d * sizeof(uint16_t);
+}
+
+hipError_t launch_router(const void* X, int dtype, int T, int d, int E, const float* Wr, const float* bias,
+                         float* logits, void* split, hipStream_t s) {
+    if (!router_mfma_ok(dtype, d)) {
+        const size_t n = (size_t)T * E;
+        const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
+        if (dtype == 1)
+            hipLaunchKernelGGL(router_fma_kernel<uint16_t>, grid, dim3(kThreads), 0, s,
+                               static_cast<const uint16_t*>(X), T, d, Wr, bias, E, logits);
+        else
+            hipLaunchKernelGGL(router_fma_kernel<float>, grid, dim3(kThreads), 0, s, static_cast<const float*>(X),
+                               T, d, Wr, bias, E, logits);
+        return hipGetLastError();
+    }
+    const int nb = router_nb(E);
+    const int eb = 32 * nb;
+    const int n_eg = (E + eb - 1) / eb;
+    const int e_pad = n_eg * eb;
+    uint16_t* hi = static_cast<uint16_t*>(split);
+    uint16_t* lo = hi + (size_t)e_pad * d;
+    const size_t n = (size_t)e_pad * d;
+    const unsigned sgrid = (unsigned)std::min<size_t>((n + kThreads - 1) / kThreads, 4096);
+    hipLaunchKernelGGL(router_split_kernel, dim3(sgrid), dim3(kThreads), 0, s, Wr, d, E, e_pad, hi, lo);
+    // token tiles rounded up to a multiple of 8 (one per XCD); blocks past T exit at once
+    const int tt = 32 * router_tg(E);
+    const int tiles = (((T + tt - 1) / tt) + 7) / 8 * 8;
+    const dim3 grid((unsigned)(tiles * n_eg));
+    if (nb == 1)
+        hipLaunchKernelGGL((router_mfma_kernel<1, 1>), grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(X), T,
+                           d, hi, lo, bias, E, n_eg, logits);
+    else
+        hipLaunchKernelGGL((router_mfma_kernel<2, 4>), grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(X), T,
+                           d, hi, lo, bias, E, n_eg, logits);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -82,16 +82,25 @@ def _normal(shape, var: float, dtype, device, g) -> torch.Tensor:
     return x.to(dtype)
 
 
+def make_router(cfg: MoEConfig, device="cpu", seed: int = 0):
+    """Router weights Wr [d, E] ~ N(0, 1/d) fp32 and the per-expert bias [E] ~ N(0, bias_var)
+    (None without one) -- the same draws make_logits uses."""
+    dev = torch.device(device)
+    Wr = _normal((cfg.d, cfg.E), 1.0 / cfg.d, torch.float32, dev, _gen(dev, seed, "Wr"))
+    b = _normal((cfg.E,), cfg.bias_var, torch.float32, dev, _gen(dev, seed, "b")) if cfg.bias_var else None
+    return Wr, b
+
+
 def make_logits(cfg: MoEConfig, device="cpu", seed: int = 0, X: torch.Tensor | None = None):
     dev = torch.device(device)
     if cfg.logits == "direct":
         return _normal((cfg.T, cfg.E), 1.0, torch.float32, dev, _gen(dev, seed, "logits"))
     if cfg.logits in ("proj", "proj_bias"):
         assert X is not None
-        Wr = _normal((cfg.d, cfg.E), 1.0 / cfg.d, torch.float32, dev, _gen(dev, seed, "Wr"))
+        Wr, b = make_router(cfg, dev, seed)
         lg = X.float() @ Wr
         if cfg.logits == "proj_bias":
-            lg += _normal((cfg.E,), cfg.bias_var, torch.float32, dev, _gen(dev, seed, "b"))
+            lg += b
         return lg.contiguous()
     if cfg.logits == "bias":
         z = _normal((cfg.T, cfg.E), 1.0, torch.float32, dev, _gen(dev, seed, "logits"))

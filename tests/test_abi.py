@@ -102,3 +102,23 @@ def test_combine_and_forward_reject(lib):
     bad = list(base)
     bad[1] = None
     assert lib.moe_forward(*bad, P, ws, None) == INVALID
+
+
+def test_router_workspace_and_rejections(lib):
+    assert lib.moe_router_workspace_bytes(4096, 8, 1) == 2 * 32 * 4096 * 2     # E padded to 32
+    assert lib.moe_router_workspace_bytes(7168, 256, 1) == 2 * 256 * 7168 * 2
+    assert lib.moe_router_workspace_bytes(1536, 40, 1) == 2 * 64 * 1536 * 2    # E padded to 64
+    assert lib.moe_router_workspace_bytes(128, 8, 0) == 0                      # fp32: no split
+    assert lib.moe_router_workspace_bytes(384, 8, 1) == 0                      # d % 256 != 0: no split
+    assert lib.moe_router_workspace_bytes(4096, 257, 1) == 0
+    wsb = lib.moe_router_workspace_bytes(4096, 8, 1)
+    assert lib.moe_router(P, 1, 0, 4096, 8, P, None, P, P, wsb, None) == INVALID      # T = 0
+    assert lib.moe_router(P, 1, 16, 4096, 0, P, None, P, P, wsb, None) == INVALID     # E = 0
+    assert lib.moe_router(P, 1, 16, 4096, 300, P, None, P, P, wsb, None) == UNSUPPORTED
+    assert lib.moe_router(None, 1, 16, 4096, 8, P, None, P, P, wsb, None) == INVALID  # X NULL
+    assert lib.moe_router(P, 1, 16, 4096, 8, None, None, P, P, wsb, None) == INVALID  # Wr NULL
+    assert lib.moe_router(P, 1, 16, 4096, 8, P, None, None, P, wsb, None) == INVALID  # logits NULL
+    assert lib.moe_router(P, 1, 16, 4096, 8, P, None, P, None, 0, None) == WORKSPACE
+    assert lib.moe_router(P, 1, 16, 4096, 8, P, None, P, P, wsb - 1, None) == WORKSPACE
+    assert lib.moe_router(P + 8, 1, 16, 4096, 8, P, None, P, P, wsb, None) == INVALID  # X misaligned
+    assert lib.moe_router(P, 7, 16, 4096, 8, P, None, P, P, wsb, None) == UNSUPPORTED  # dtype

@@ -1,0 +1,76 @@
+"""GPU parity of moe_router (the router projection upstream of the gate)
+against the oracle, and of the routing that follows it."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_routing_gate_amd as moe
+import oracle
+import synth
+from parity_util import check_equal, cuda, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_logits(lg_gpu, X_h, Wr_h, b_h, rows=None):
+    """|logit - oracle| <= 2^-16 * sum_i |X[t,i] Wr[i,e]| (+ a tiny floor), element by element."""
+    Xf = oracle.bf16_to_f32(X_h) if X_h.dtype == np.uint16 else X_h
+    if rows is not None:
+        X_h, Xf = X_h[rows], Xf[rows]
+    ref = oracle.router(X_h, Wr_h, b_h).astype(np.float64)
+    S = np.abs(Xf.astype(np.float64)) @ np.abs(Wr_h.astype(np.float64))
+    got = lg_gpu.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        got = got[rows]
+    err = np.abs(got - ref)
+    bound = 2.0 ** -16 * S + 2.0 ** -40
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, (f"{len(bad)} logits out of bound, first {bad[:3].tolist()}: "
+                           f"err {err[tuple(bad[0])]:.3e} bound {bound[tuple(bad[0])]:.3e}")
+    return float((err / np.maximum(S, 1e-30)).max())
+
+
+CASES = [
+    # (T, d, E, dtype, bias variance): E padded to 32 or 64, ragged token tiles,
+    # d not a multiple of 256 (the FMA path), fp32 X, a single token
+    (300, 512, 8, "bf16", 0.0),
+    (257, 768, 256, "bf16", 1.5),
+    (100, 1536, 128, "bf16", 2.0),
+    (65, 256, 40, "bf16", 1.0),
+    (33, 384, 8, "bf16", 0.0),
+    (256, 128, 8, "f32", 0.0),
+    (1, 1024, 64, "bf16", 0.5),
+]
+
+
+@pytest.mark.parametrize("T,d,E,dt,bv", CASES, ids=lambda v: str(v))
+def test_router_matches_oracle(T, d, E, dt, bv):
+    cfg = synth.MoEConfig("r", T=T, d=d, E=E, K=1, n=128, dtype=dt, logits="proj_bias" if bv else "proj",
+                          bias_var=bv)
+    X = synth._normal((T, d), 1.0, cfg.torch_dtype, torch.device("cpu"), synth._gen("cpu", 3, "X"))
+    Wr, b = synth.make_router(cfg, "cpu", 3)
+    lg = moe.moe_router(cuda(X), cuda(Wr), None if b is None else cuda(b))
+    torch.cuda.synchronize()
+    _check_logits(lg, to_np(X), Wr.numpy(), None if b is None else b.numpy())
+    # the same call twice gives the same bits
+    lg2 = moe.moe_router(cuda(X), cuda(Wr), None if b is None else cuda(b))
+    torch.cuda.synchronize()
+    assert torch.equal(lg, lg2)
+
+
+@pytest.mark.parametrize("name", ["mixtral", "dsv3"])
+def test_router_full_size_then_route(name):
+    """Full-size router on sampled rows, then the gate on the GPU logits matches
+    the oracle's gate on those same logits bit for bit."""
+    cfg = synth.CONFIGS[name]
+    X = synth._normal((cfg.T, cfg.d), 1.0, cfg.torch_dtype, torch.device("cuda"), synth._gen("cuda", 0, "X"))
+    Wr, b = synth.make_router(cfg, "cuda", 0)
+    lg = moe.moe_router(X, Wr, b)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[np.random.default_rng(1).choice(cfg.T, 48, replace=False), 0, cfg.T - 1])
+    _check_logits(lg, to_np(X), Wr.cpu().numpy(), None if b is None else b.cpu().numpy(), rows=rows)
+    idx, w, counts, offsets = moe.moe_route(lg, cfg.K)
+    torch.cuda.synchronize()
+    ridx, rw, rc, ro = oracle.route(lg.cpu().numpy(), cfg.K)
+    check_equal(idx, ridx, "topk_idx")
+    check_equal(counts, rc, "counts")
