@@ -100,18 +100,18 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_bf16_kernel(
         const uint16_t* Bp[2] = {B0 + (size_t)e * Kd * N, DUAL ? B1 + (size_t)e * Kd * N : nullptr};
 
         f32x16 acc[NB][2][2];
-#pragma unroll
+        #pragma unroll
         for (int m = 0; m < NB; ++m)
-#pragma unroll
+            #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
+                #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
+                    #pragma unroll
                     for (int i = 0; i < 16; ++i) acc[m][mi][ni][i] = 0.0f;
 
         for (int k0 = 0; k0 < Kd; k0 += BK) {
             __syncthreads();
-#pragma unroll
+            #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c = tid + kThreads * i;
                 const int r = c >> 3;
@@ -120,47 +120,47 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_bf16_kernel(
                 if (r < rows_valid) val = *reinterpret_cast<const u32x4*>(A + (row0 + r) * Kd + k0 + kc);
                 *reinterpret_cast<u32x4*>(As + r * LDK + kc) = val;
             }
-#pragma unroll
+            #pragma unroll
             for (int m = 0; m < NB; ++m) {
-#pragma unroll
+                #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int c = tid + kThreads * i;
                     const int kr = c >> 4;
                     const int nc = (c & 15) << 3;
                     const u32x4 val =
                         *reinterpret_cast<const u32x4*>(Bp[m] + (size_t)(k0 + kr) * N + n0 + nc);
-#pragma unroll
+                    #pragma unroll
                     for (int j = 0; j < 8; ++j)
                         Bs[m][(nc + j) * LDK + kr] = (uint16_t)(val[j >> 1] >> (16 * (j & 1)));
                 }
             }
             __syncthreads();
-#pragma unroll
+            #pragma unroll
             for (int ks = 0; ks < BK / 16; ++ks) {
                 bf16x8 a[2], b[NB][2];
-#pragma unroll
+                #pragma unroll
                 for (int mi = 0; mi < 2; ++mi)
                     a[mi] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + mi * 32 + l32) * LDK + ks * 16 + lh * 8);
-#pragma unroll
+                #pragma unroll
                 for (int m = 0; m < NB; ++m)
-#pragma unroll
+                    #pragma unroll
                     for (int ni = 0; ni < 2; ++ni)
                         b[m][ni] = *reinterpret_cast<const bf16x8*>(Bs[m] + (wn * 64 + ni * 32 + l32) * LDK + ks * 16 + lh * 8);
-#pragma unroll
+                #pragma unroll
                 for (int m = 0; m < NB; ++m)
-#pragma unroll
+                    #pragma unroll
                     for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
+                        #pragma unroll
                         for (int ni = 0; ni < 2; ++ni)
                             acc[m][mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[m][ni], acc[m][mi][ni], 0, 0, 0);
             }
         }
         // 32x32 accumulator layout: element i of lane l is row (i/4)*8 + (l/32)*4 + i%4, column l%32.
-#pragma unroll
+        #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
+            #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
+                #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int row = wm * 64 + mi * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
                     const int col = n0 + wn * 64 + ni * 32 + l32;
@@ -221,7 +221,7 @@ constexpr int kTicketInts = 8 * 16;
 MOE_DEV int sched_lookup(const int32_t* __restrict__ counts, int E, int NT, int rows, int lane, int tile,
                          int* start, int* total) {
     int v[4];
-#pragma unroll
+    #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = lane * 4 + j;
         const int c = e < E ? min(max(counts[e], 0), rows) : 0;
@@ -229,7 +229,7 @@ MOE_DEV int sched_lookup(const int32_t* __restrict__ counts, int E, int NT, int 
     }
     const int p0 = v[0], p1 = p0 + v[1], p2 = p1 + v[2], p3 = p2 + v[3];
     int x = p3;  // inclusive scan of the per-lane totals
-#pragma unroll
+    #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
         const int y = __shfl_up(x, o, kWave);
         if (lane >= o) x += y;
@@ -253,14 +253,14 @@ MOE_DEV int sched_lookup(const int32_t* __restrict__ counts, int E, int NT, int 
 // (the short-tile layouts).  All lanes of the wave must call it.
 MOE_DEV int count_short_tiles(const int32_t* __restrict__ counts, int E, int NT, int rows, int lane) {
     int n = 0;
-#pragma unroll
+    #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = lane * 4 + j;
         const int c = e < E ? min(max(counts[e], 0), rows) : 0;
         const int rem = c % kBM256;
         n += (rem > 0 && rem <= 128) ? NT : 0;
     }
-#pragma unroll
+    #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) n += __shfl_xor(n, o, kWave);
     return uniform(n);
 }
@@ -319,12 +319,12 @@ MOE_DEV void store_rows(const f32x16 (&a)[4], int mi, uint16_t* __restrict__ C, 
     const int m = wm * 128 + mi * 32 + l32;
     if (m < rows_valid) {
         uint16_t* crow = C + (size_t)(r0 + m) * N;
-#pragma unroll
+        #pragma unroll
         for (int ni = 0; ni < (DUAL ? 2 : 4); ++ni) {
-#pragma unroll
+            #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 float v[4];
-#pragma unroll
+                #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     v[j] = a[ni][q * 4 + j];
                     if (DUAL) v[j] = silu_mul(v[j], a[ni + 2][q * 4 + j]);
@@ -364,12 +364,12 @@ MOE_DEV void store_rows_lds(const f32x16 (&a)[4], int mi, char* smem, uint16_t* 
     };
     auto swz = [](int r, int c) { return DUAL ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15)); };
     char* wr = row_at(l32);
-#pragma unroll
+    #pragma unroll
     for (int ni = 0; ni < (DUAL ? 2 : 4); ++ni) {
-#pragma unroll
+        #pragma unroll
         for (int q = 0; q < 4; ++q) {
             float v[4];
-#pragma unroll
+            #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 v[j] = a[ni][q * 4 + j];
                 if (DUAL) v[j] = silu_mul(v[j], a[ni + 2][q * 4 + j]);
@@ -385,12 +385,12 @@ MOE_DEV void store_rows_lds(const f32x16 (&a)[4], int mi, char* smem, uint16_t* 
     const int c = lane % CH;
     const int colb = n0 + (DUAL ? wn * 64 : wn * 128) + c * 8;
     u32x4 val[32 / RPI];
-#pragma unroll
+    #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
         const int r = i * RPI + lane / CH;
         val[i] = *reinterpret_cast<const u32x4*>(row_at(r) + swz(r, c) * 16);
     }
-#pragma unroll
+    #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
         const int r = i * RPI + lane / CH;
         const int m = wm * 128 + mi * 32 + r;
@@ -410,12 +410,12 @@ MOE_DEV void store_rows_short(const f32x16 (&a)[2], int mi, uint16_t* __restrict
     const int m = mi * 32 + l32;
     if (m < rows_valid) {
         uint16_t* crow = C + (size_t)(r0 + m) * N;
-#pragma unroll
+        #pragma unroll
         for (int ni = 0; ni < (DUAL ? 1 : 2); ++ni) {
-#pragma unroll
+            #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 float v[4];
-#pragma unroll
+                #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     v[j] = a[ni][q * 4 + j];
                     if (DUAL) v[j] = silu_mul(v[j], a[1][q * 4 + j]);
@@ -466,14 +466,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     // A row r, k-chunk c of 8 elements sits at r*64 + ((c ^ ((r/4)%4)) * 16).
     const int arow = wm * 128 + l32;
     int a_rd[2];
-#pragma unroll
+    #pragma unroll
     for (int ks = 0; ks < 2; ++ks) a_rd[ks] = arow * 64 + (((ks * 2 + lh) ^ ((arow >> 2) & 3)) << 4);
     // B k-row k, column n of half h sits at 16K + h*8K + k*256 + (((n/8) ^ 4*(k%4)) * 16) + (n%8)*2.
     const int b_x = (s16 >> 2) << 2;
     const int b_c = (g16 & 1) * 2 + ((s16 & 3) >> 1);
     const int b_lane = 16384 + ((g16 >> 1) * 8 + (s16 >> 2)) * 256 + (s16 & 1) * 8;
     int b_rd[4];
-#pragma unroll
+    #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
         const int half = DUAL ? (ni >> 1) : wn;
         const int nn = DUAL ? (wn * 64 + (ni & 1) * 32) : ni * 32;
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
             const uint16_t* bmat = (DUAL && half) ? B1 : B0;
             const rsrc_t rb = make_rsrc(bmat + (size_t)e * Kd * N);
             uint32_t a_vo[4], b_vo[4];
-    #pragma unroll
+            #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = (wave * 4 + i) * 16 + (lane >> 2);
                 const int ch = (lane & 3) ^ ((r >> 2) & 3);
@@ -571,184 +571,184 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                 else dma16(rb, dst + 16384 + (i - 4) * 1024, b_vo[i - 4], ka * b_step);
             };
             auto issue = [&](int kt, int soff) {
-    #pragma unroll
+                #pragma unroll
                 for (int i = 0; i < 8; ++i) issue_one(kt, soff, i);
             };
 
             if constexpr (MI == 0) {
-            f32x16 acc[4][4];
-    #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-    #pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-    #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+                f32x16 acc[4][4];
+                #pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+                    #pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+                        #pragma unroll
+                        for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
 
-            bf16x8 af[2][4], bfr[2][4];
-            auto load_frags = [&](int soff, int ks, int buf) {
-                const char* sa = smem + soff + a_rd[ks];
-    #pragma unroll
-                for (int mi = 0; mi < 4; ++mi) af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * 64);
-    #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const char* pb = smem + soff + b_rd[ni] + ks * 16 * 256;
-                    const bf16x4 h0 = lds_read_tr(pb);
-                    const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
-                    bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+                bf16x8 af[2][4], bfr[2][4];
+                auto load_frags = [&](int soff, int ks, int buf) {
+                    const char* sa = smem + soff + a_rd[ks];
+                    #pragma unroll
+                    for (int mi = 0; mi < 4; ++mi) af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * 64);
+                    #pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) {
+                        const char* pb = smem + soff + b_rd[ni] + ks * 16 * 256;
+                        const bf16x4 h0 = lds_read_tr(pb);
+                        const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
+                        bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    }
+                };
+                auto mfma = [&](int buf, int lo, int hi) {
+                    #pragma unroll
+                    for (int q = lo; q < hi; ++q) {
+                        const int mi = q >> 2, ni = q & 3;
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
+                    }
+                };
+
+                // Prologue (ksn is a multiple of 4 here): K-steps 0..3 in flight, wait for step 0.
+                issue(0, 0);
+                issue(1, kP4Stage);
+                issue(2, 2 * kP4Stage);
+                issue(3, 3 * kP4Stage);
+                __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
+                __syncthreads();
+                load_frags(0, 0, 0);
+
+                int s_cur = 0;  // byte offset of step kt's stage
+                for (int kt0 = 0; kt0 < ksn; kt0 += 4) {
+                    #pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int kt = kt0 + u;
+                        const int s_nxt = s_cur == (kP4Stages - 1) * kP4Stage ? 0 : s_cur + kP4Stage;
+                        const int s_old = s_cur == 0 ? (kP4Stages - 1) * kP4Stage : s_cur - kP4Stage;
+                        // Step boundary: own DMA of step kt+1 done (16 younger ones may fly).
+                        __builtin_amdgcn_sched_barrier(0);
+                        __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+                        __syncthreads();
+                        // Refill the stage of step kt-1 with step kt+4, one DMA per MFMA.
+                        const int kn = min(kt + 4, ksn - 1);
+                        #pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            issue_one(kn, s_old, i);
+                            mfma(0, i, i + 1);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        // Rest of sub-step 0 while sub-step 1's fragments are read.
+                        load_frags(s_cur, 1, 1);
+                        mfma(0, 8, 16);
+                        #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        }
+                        #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        // Sub-step 1 while the next step's sub-step-0 fragments are read.
+                        load_frags(s_nxt, 0, 0);
+                        mfma(1, 0, 16);
+                        #pragma unroll
+                        for (int i = 0; i < 12; ++i) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        }
+                        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                        s_cur = s_nxt;
+                    }
                 }
-            };
-            auto mfma = [&](int buf, int lo, int hi) {
-    #pragma unroll
-                for (int q = lo; q < hi; ++q) {
-                    const int mi = q >> 2, ni = q & 3;
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
+                // The clamped refills of the last steps are still in flight.
+                __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                // Every wave is done reading the stages (the staged epilogue below
+                // reuses them).
+                if (tickets != nullptr) j_next = take();
+                else __syncthreads();
+
+                #pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    if constexpr (PART) {
+                        f32x4* dst =
+                            reinterpret_cast<f32x4*>(part + (size_t)pslot * kPartFloats) + part_index(wave, mi * 4, 0, __lane_id());
+                        #pragma unroll
+                        for (int ni = 0; ni < 4; ++ni)
+                            #pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const f32x16& av = acc[mi][ni];
+                                dst[(ni * 4 + q) * kWave] = f32x4{av[q * 4], av[q * 4 + 1], av[q * 4 + 2], av[q * 4 + 3]};
+                            }
+                    } else {
+                        store_rows_lds<DUAL>(acc[mi], mi, smem, C, r0, rows_valid, n0, N, wave, wm, wn);
+                    }
                 }
-            };
-
-            // Prologue (ksn is a multiple of 4 here): K-steps 0..3 in flight, wait for step 0.
-            issue(0, 0);
-            issue(1, kP4Stage);
-            issue(2, 2 * kP4Stage);
-            issue(3, 3 * kP4Stage);
-            __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
-            __syncthreads();
-            load_frags(0, 0, 0);
-
-            int s_cur = 0;  // byte offset of step kt's stage
-            for (int kt0 = 0; kt0 < ksn; kt0 += 4) {
-    #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int kt = kt0 + u;
+            } else {
+                // Short tile: every row sits in the first 32 * MI.  The four waves
+                // share those rows and each takes a quarter of the columns (the W1
+                // and W3 halves of 32 output columns for the SwiGLU GEMM, 64
+                // columns otherwise), so only row slices that hold rows are
+                // multiplied.  Stages, DMA, waits and barriers are the full tile's.
+                int sa_rd[2], sb_rd[2];
+                #pragma unroll
+                for (int ks = 0; ks < 2; ++ks) sa_rd[ks] = l32 * 64 + (((ks * 2 + lh) ^ ((l32 >> 2) & 3)) << 4);
+                #pragma unroll
+                for (int ni = 0; ni < 2; ++ni) {
+                    const int sh = DUAL ? ni : (wave >> 1);
+                    const int nn = DUAL ? wave * 32 : (wave & 1) * 64 + ni * 32;
+                    sb_rd[ni] = b_lane + sh * 8192 + ((((nn >> 3) ^ b_x) + b_c) << 4);
+                }
+                f32x16 acc[MI][2];
+                #pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+                    #pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+                        #pragma unroll
+                        for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+                bf16x8 af[2][MI], bfr[2][2];
+                auto load_frags = [&](int soff, int ks, int buf) {
+                    const char* sa = smem + soff + sa_rd[ks];
+                    #pragma unroll
+                    for (int mi = 0; mi < MI; ++mi) af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * 64);
+                    #pragma unroll
+                    for (int ni = 0; ni < 2; ++ni) {
+                        const char* pb = smem + soff + sb_rd[ni] + ks * 16 * 256;
+                        const bf16x4 h0 = lds_read_tr(pb);
+                        const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
+                        bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    }
+                };
+                auto mfma = [&](int buf) {
+                    #pragma unroll
+                    for (int mi = 0; mi < MI; ++mi)
+                        #pragma unroll
+                        for (int ni = 0; ni < 2; ++ni)
+                            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
+                };
+                issue(0, 0);
+                issue(1, kP4Stage);
+                issue(2, 2 * kP4Stage);
+                issue(3, 3 * kP4Stage);
+                __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
+                __syncthreads();
+                load_frags(0, 0, 0);
+                int s_cur = 0;
+                for (int kt = 0; kt < ksn; ++kt) {
                     const int s_nxt = s_cur == (kP4Stages - 1) * kP4Stage ? 0 : s_cur + kP4Stage;
                     const int s_old = s_cur == 0 ? (kP4Stages - 1) * kP4Stage : s_cur - kP4Stage;
-                    // Step boundary: own DMA of step kt+1 done (16 younger ones may fly).
                     __builtin_amdgcn_sched_barrier(0);
                     __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
                     __syncthreads();
-                    // Refill the stage of step kt-1 with step kt+4, one DMA per MFMA.
-                    const int kn = min(kt + 4, ksn - 1);
-    #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        issue_one(kn, s_old, i);
-                        mfma(0, i, i + 1);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                    // Rest of sub-step 0 while sub-step 1's fragments are read.
+                    issue(min(kt + 4, ksn - 1), s_old);
                     load_frags(s_cur, 1, 1);
-                    mfma(0, 8, 16);
-    #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    }
-    #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    // Sub-step 1 while the next step's sub-step-0 fragments are read.
+                    mfma(0);
                     load_frags(s_nxt, 0, 0);
-                    mfma(1, 0, 16);
-    #pragma unroll
-                    for (int i = 0; i < 12; ++i) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                    mfma(1);
                     s_cur = s_nxt;
                 }
-            }
-            // The clamped refills of the last steps are still in flight.
-            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            // Every wave is done reading the stages (the staged epilogue below
-            // reuses them).
-            if (tickets != nullptr) j_next = take();
-            else __syncthreads();
-
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                if constexpr (PART) {
-                    f32x4* dst =
-                        reinterpret_cast<f32x4*>(part + (size_t)pslot * kPartFloats) + part_index(wave, mi * 4, 0, __lane_id());
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const f32x16& av = acc[mi][ni];
-                            dst[(ni * 4 + q) * kWave] = f32x4{av[q * 4], av[q * 4 + 1], av[q * 4 + 2], av[q * 4 + 3]};
-                        }
-                } else {
-                    store_rows_lds<DUAL>(acc[mi], mi, smem, C, r0, rows_valid, n0, N, wave, wm, wn);
-                }
-            }
-            } else {
-            // Short tile: every row sits in the first 32 * MI.  The four waves
-            // share those rows and each takes a quarter of the columns (the W1
-            // and W3 halves of 32 output columns for the SwiGLU GEMM, 64
-            // columns otherwise), so only row slices that hold rows are
-            // multiplied.  Stages, DMA, waits and barriers are the full tile's.
-            int sa_rd[2], sb_rd[2];
-    #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) sa_rd[ks] = l32 * 64 + (((ks * 2 + lh) ^ ((l32 >> 2) & 3)) << 4);
-    #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int sh = DUAL ? ni : (wave >> 1);
-                const int nn = DUAL ? wave * 32 : (wave & 1) * 64 + ni * 32;
-                sb_rd[ni] = b_lane + sh * 8192 + ((((nn >> 3) ^ b_x) + b_c) << 4);
-            }
-            f32x16 acc[MI][2];
-    #pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-    #pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-    #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
-            bf16x8 af[2][MI], bfr[2][2];
-            auto load_frags = [&](int soff, int ks, int buf) {
-                const char* sa = smem + soff + sa_rd[ks];
-    #pragma unroll
-                for (int mi = 0; mi < MI; ++mi) af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * 64);
-    #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const char* pb = smem + soff + sb_rd[ni] + ks * 16 * 256;
-                    const bf16x4 h0 = lds_read_tr(pb);
-                    const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
-                    bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
-            };
-            auto mfma = [&](int buf) {
-    #pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
-    #pragma unroll
-                    for (int ni = 0; ni < 2; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
-            };
-            issue(0, 0);
-            issue(1, kP4Stage);
-            issue(2, 2 * kP4Stage);
-            issue(3, 3 * kP4Stage);
-            __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
-            __syncthreads();
-            load_frags(0, 0, 0);
-            int s_cur = 0;
-            for (int kt = 0; kt < ksn; ++kt) {
-                const int s_nxt = s_cur == (kP4Stages - 1) * kP4Stage ? 0 : s_cur + kP4Stage;
-                const int s_old = s_cur == 0 ? (kP4Stages - 1) * kP4Stage : s_cur - kP4Stage;
-                __builtin_amdgcn_sched_barrier(0);
-                __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
-                __syncthreads();
-                issue(min(kt + 4, ksn - 1), s_old);
-                load_frags(s_cur, 1, 1);
-                mfma(0);
-                load_frags(s_nxt, 0, 0);
-                mfma(1);
-                s_cur = s_nxt;
-            }
-            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (tickets != nullptr) j_next = take();
-    #pragma unroll
-            for (int mi = 0; mi < MI; ++mi) store_rows_short<DUAL>(acc[mi], mi, C, r0, rows_valid, n0, N, wave);
+                __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (tickets != nullptr) j_next = take();
+                #pragma unroll
+                for (int mi = 0; mi < MI; ++mi) store_rows_short<DUAL>(acc[mi], mi, C, r0, rows_valid, n0, N, wave);
             }
         };
         using Full = std::integral_constant<int, 0>;
@@ -787,22 +787,22 @@ __global__ __launch_bounds__(kThreads) void ffn_split_fixup(const float* __restr
         if (tg.rows_valid <= 0) continue;
         const f32x4* src = reinterpret_cast<const f32x4*>(part + (size_t)i * sp.S * kPartFloats);
         f32x16 acc[4];
-#pragma unroll
+        #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
+            #pragma unroll
             for (int c = 0; c < 16; ++c) acc[ni][c] = 0.0f;
         for (int j = 0; j < sp.S; ++j) {  // parts in slot order
             f32x4 v[16];
-#pragma unroll
+            #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
+                #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     v[ni * 4 + q] = src[(size_t)j * (kPartFloats / 4) + part_index(wave, mi * 4 + ni, q, lane)];
-#pragma unroll
+            #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
+                #pragma unroll
                 for (int q = 0; q < 4; ++q)
-#pragma unroll
+                    #pragma unroll
                     for (int c = 0; c < 4; ++c) acc[ni][q * 4 + c] += v[ni * 4 + q][c];
         }
         store_rows<DUAL>(acc, mi, C, tg.r0, tg.rows_valid, tg.n0, N, wm, wn);
@@ -849,49 +849,49 @@ __global__ __launch_bounds__(kThreads) void ffn_f32_kernel(const float* __restri
         const int n0 = n_tile * BN;
         const float* Bp[2] = {B0 + (size_t)e * Kd * N, DUAL ? B1 + (size_t)e * Kd * N : nullptr};
         float acc[NB][4][4];
-#pragma unroll
+        #pragma unroll
         for (int m = 0; m < NB; ++m)
-#pragma unroll
+            #pragma unroll
             for (int i = 0; i < 4; ++i)
-#pragma unroll
+                #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[m][i][j] = 0.0f;
         for (int k0 = 0; k0 < Kd; k0 += BK) {
             __syncthreads();
-#pragma unroll
+            #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c = tid + kThreads * i;
                 const int r = c >> 4, kk = c & 15;
                 As[kk][r] = (r < rows_valid) ? A[(row0 + r) * Kd + k0 + kk] : 0.0f;
             }
-#pragma unroll
+            #pragma unroll
             for (int m = 0; m < NB; ++m)
-#pragma unroll
+                #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int c = tid + kThreads * i;
                     const int kk = c >> 6, nn = c & 63;
                     Bs[m][kk][nn] = Bp[m][(size_t)(k0 + kk) * N + n0 + nn];
                 }
             __syncthreads();
-#pragma unroll
+            #pragma unroll
             for (int kk = 0; kk < BK; ++kk) {
                 float a[4], b[NB][4];
-#pragma unroll
+                #pragma unroll
                 for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
-#pragma unroll
+                #pragma unroll
                 for (int m = 0; m < NB; ++m)
-#pragma unroll
+                    #pragma unroll
                     for (int j = 0; j < 4; ++j) b[m][j] = Bs[m][kk][tx + 16 * j];
-#pragma unroll
+                #pragma unroll
                 for (int m = 0; m < NB; ++m)
-#pragma unroll
+                    #pragma unroll
                     for (int i = 0; i < 4; ++i)
-#pragma unroll
+                        #pragma unroll
                         for (int j = 0; j < 4; ++j) acc[m][i][j] = fmaf(a[i], b[m][j], acc[m][i][j]);
             }
         }
-#pragma unroll
+        #pragma unroll
         for (int i = 0; i < 4; ++i)
-#pragma unroll
+            #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = ty + 16 * i;
                 if (row < rows_valid) {
