@@ -914,24 +914,29 @@ static bool ffn_pipelined_ok(int d, int n) { return d % 256 == 0 && n % 128 == 0
 
 static int ffn_grid() { return (device_cu_count() / 8) * 8; }
 
-// Split slots for every workgroup, then the claim counters.
+// Split slots for every workgroup, then two sets of claim counters (the
+// SwiGLU GEMM's, then the down GEMM's).
 size_t ffn_split_bytes(int dtype, int d, int n) {
     return (dtype == 1 && ffn_pipelined_ok(d, n))
-               ? (size_t)ffn_grid() * kPartFloats * sizeof(float) + kTicketInts * sizeof(int)
+               ? (size_t)ffn_grid() * kPartFloats * sizeof(float) + 2 * kTicketInts * sizeof(int)
                : 0;
 }
+
+int* ffn_tickets(float* part) { return part ? reinterpret_cast<int*>(part + (size_t)ffn_grid() * kPartFloats) : nullptr; }
+int ffn_ticket_ints() { return 2 * kTicketInts; }
 
 // One pipelined GEMM (SwiGLU or plain), then the fixup of its split tail.
 template <bool DUAL>
 static hipError_t launch_pipelined(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                                    const int32_t* counts, const int32_t* offsets, int E, int Kd, int N, int rows,
-                                   float* part, hipStream_t s) {
+                                   float* part, bool tickets_zeroed, hipStream_t s) {
     const hipError_t aerr =
         hipFuncSetAttribute((const void*)ffn_p4_kernel<DUAL>, hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
     if (aerr != hipSuccess) return aerr;
     const int G = ffn_grid();
-    int* tickets = part != nullptr ? reinterpret_cast<int*>(part + (size_t)G * kPartFloats) : nullptr;
-    if (tickets != nullptr) hipLaunchKernelGGL(zero_ints, dim3(1), dim3(kTicketInts), 0, s, tickets, kTicketInts);
+    int* tickets = part != nullptr ? ffn_tickets(part) + (DUAL ? 0 : kTicketInts) : nullptr;
+    if (tickets != nullptr && !tickets_zeroed)
+        hipLaunchKernelGGL(zero_ints, dim3(1), dim3(kTicketInts), 0, s, tickets, kTicketInts);
     hipLaunchKernelGGL(ffn_p4_kernel<DUAL>, dim3(G), dim3(kThreads), kP4Lds, s, A, B0, B1, C, counts, offsets, E, Kd,
                        N, rows, part, tickets);
     if (part != nullptr)
@@ -943,12 +948,12 @@ static hipError_t launch_pipelined(const uint16_t* A, const uint16_t* B0, const 
 // Step 4a: Act = SiLU(Xp W1) * (Xp W3).
 hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int rows, int d, int E,
                          int n, const int32_t* counts, const int32_t* offsets, void* Act, float* part,
-                         hipStream_t s) {
+                         bool tickets_zeroed, hipStream_t s) {
     const int cus = device_cu_count();
     if (dtype == 1 && ffn_pipelined_ok(d, n))
         return launch_pipelined<true>(static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
                                       static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(Act), counts,
-                                      offsets, E, d, n, rows, part, s);
+                                      offsets, E, d, n, rows, part, tickets_zeroed, s);
     if (dtype == 1) {
         hipLaunchKernelGGL(ffn_bf16_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s,
                            static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
@@ -965,12 +970,13 @@ hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dty
 
 // Step 4b: Y = Act W2.
 hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows, int d, int E, int n,
-                           const int32_t* counts, const int32_t* offsets, void* Y, float* part, hipStream_t s) {
+                           const int32_t* counts, const int32_t* offsets, void* Y, float* part,
+                           bool tickets_zeroed, hipStream_t s) {
     const int cus = device_cu_count();
     if (dtype == 1 && ffn_pipelined_ok(d, n))
         return launch_pipelined<false>(static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
                                        static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(Y), counts,
-                                       offsets, E, n, d, rows, part, s);
+                                       offsets, E, n, d, rows, part, tickets_zeroed, s);
     if (dtype == 1) {
         hipLaunchKernelGGL(ffn_bf16_kernel<false>, dim3(cus * 2), dim3(kThreads), 0, s,
                            static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
@@ -987,10 +993,11 @@ hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows,
 
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
                       int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
-                      void* Act, void* Y, float* part, hipStream_t s) {
-    const hipError_t err = launch_ffn_up(Xp, W1, W3, dtype, rows, d, E, n, counts, offsets, Act, part, s);
+                      void* Act, void* Y, float* part, bool tickets_zeroed, hipStream_t s) {
+    const hipError_t err =
+        launch_ffn_up(Xp, W1, W3, dtype, rows, d, E, n, counts, offsets, Act, part, tickets_zeroed, s);
     if (err != hipSuccess) return err;
-    return launch_ffn_down(Act, W2, dtype, rows, d, E, n, counts, offsets, Y, part, s);
+    return launch_ffn_down(Act, W2, dtype, rows, d, E, n, counts, offsets, Y, part, tickets_zeroed, s);
 }
 
 }  // namespace moe

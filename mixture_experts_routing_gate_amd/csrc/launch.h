@@ -19,8 +19,10 @@ int device_cu_count();
 // Steps 1-2.
 hipError_t launch_gate(const float* logits, int T, int E, int K, int32_t* idx, float* w,
                        int32_t* blk, hipStream_t s);
+// `zero` (nullable): nzero ints the scan also clears (state for later kernels
+// on the stream, such as the grouped GEMMs' claim counters).
 hipError_t launch_scan(const int32_t* blk, int B, int E, int32_t* counts, int32_t* offsets,
-                       int32_t* blkbase, hipStream_t s);
+                       int32_t* blkbase, hipStream_t s, int* zero = nullptr, int nzero = 0);
 
 // Step 3.
 hipError_t launch_chunk_hist(const int32_t* idx, int T, int E, int K, int32_t* blk, hipStream_t s);
@@ -30,7 +32,8 @@ hipError_t launch_rank(const int32_t* idx, int T, int E, int K, const int32_t* b
 // (worth it while B*E is small, see scan_rank_fused()); counts and offsets are
 // written when not null.
 hipError_t launch_scan_rank(const int32_t* idx, int T, int E, int K, const int32_t* blk, int32_t* counts,
-                            int32_t* offsets, int32_t* sorted_pair, int32_t* inv, hipStream_t s);
+                            int32_t* offsets, int32_t* sorted_pair, int32_t* inv, int* zero, int nzero,
+                            hipStream_t s);
 inline bool scan_rank_fused(int T, int E) { return (long long)num_chunks(T) * E <= 16384; }
 hipError_t launch_copy_rows(const void* X, size_t row_bytes, int T, int K, const int32_t* inv,
                             void* Xp, hipStream_t s);
@@ -38,16 +41,22 @@ hipError_t launch_copy_rows(const void* X, size_t row_bytes, int T, int K, const
 // Step 4.  dtype: 0 = fp32, 1 = bf16.  4a (SwiGLU GEMM), 4b (down GEMM), both.
 // `part` (nullable) is the split workspace of ffn_split_bytes() bytes: with it,
 // the last partial round of tiles is split over the idle workgroups along K,
-// and tiles are claimed from per-XCD counters kept at its end.
+// and tiles are claimed from per-XCD counters kept at its end
+// (ffn_ticket_ints() ints at ffn_tickets(part)).  They must be zero when a GEMM
+// starts: each launch clears its own set first unless `tickets_zeroed` says an
+// earlier kernel on the stream already did.
 size_t ffn_split_bytes(int dtype, int d, int n);
+int* ffn_tickets(float* part);
+int ffn_ticket_ints();
 hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int rows, int d, int E,
                          int n, const int32_t* counts, const int32_t* offsets, void* Act, float* part,
-                         hipStream_t s);
+                         bool tickets_zeroed, hipStream_t s);
 hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows, int d, int E, int n,
-                           const int32_t* counts, const int32_t* offsets, void* Y, float* part, hipStream_t s);
+                           const int32_t* counts, const int32_t* offsets, void* Y, float* part,
+                           bool tickets_zeroed, hipStream_t s);
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
                       int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
-                      void* Act, void* Y, float* part, hipStream_t s);
+                      void* Act, void* Y, float* part, bool tickets_zeroed, hipStream_t s);
 
 // Router projection upstream of step 1: logits = X Wr (+ bias).  `split` is a
 // workspace of router_split_bytes() bytes (0: none needed) for the bf16 split

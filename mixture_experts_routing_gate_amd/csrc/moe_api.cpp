@@ -243,7 +243,7 @@ int moe_permute(const void* X, int dtype, int T, int d, int E, int K, const int3
     int32_t* off = c.take<int32_t>(E + 1);
     HIPCHECK(launch_chunk_hist(topk_idx, T, E, K, blk, s));
     if (scan_rank_fused(T, E)) {
-        HIPCHECK(launch_scan_rank(topk_idx, T, E, K, blk, nullptr, nullptr, sorted_pair, inv, s));
+        HIPCHECK(launch_scan_rank(topk_idx, T, E, K, blk, nullptr, nullptr, sorted_pair, inv, nullptr, 0, s));
     } else {
         HIPCHECK(launch_scan(blk, B, E, cnt, off, blkbase, s));
         HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s));
@@ -271,7 +271,7 @@ int moe_grouped_ffn(const void* Xp, const void* W1, const void* W3, const void* 
         return fail(MOE_ERR_UNSUPPORTED, "T*K*max(d,n) must be < 2^40");
     float* part = nullptr;
     CHECK(ffn_split_arg(ws, ws_bytes, dtype, d, n, &part));
-    HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, T * K, d, E, n, counts, offsets, Act, Y, part,
+    HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, T * K, d, E, n, counts, offsets, Act, Y, part, false,
                         static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
@@ -293,7 +293,7 @@ int moe_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int T,
         return fail(MOE_ERR_UNSUPPORTED, "T*K*max(d,n) must be < 2^40");
     float* part = nullptr;
     CHECK(ffn_split_arg(ws, ws_bytes, dtype, d, n, &part));
-    HIPCHECK(launch_ffn_up(Xp, W1, W3, dtype, T * K, d, E, n, counts, offsets, Act, part,
+    HIPCHECK(launch_ffn_up(Xp, W1, W3, dtype, T * K, d, E, n, counts, offsets, Act, part, false,
                            static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
@@ -314,7 +314,7 @@ int moe_ffn_down(const void* Act, const void* W2, int dtype, int T, int d, int E
         return fail(MOE_ERR_UNSUPPORTED, "T*K*max(d,n) must be < 2^40");
     float* part = nullptr;
     CHECK(ffn_split_arg(ws, ws_bytes, dtype, d, n, &part));
-    HIPCHECK(launch_ffn_down(Act, W2, dtype, T * K, d, E, n, counts, offsets, Y, part,
+    HIPCHECK(launch_ffn_down(Act, W2, dtype, T * K, d, E, n, counts, offsets, Y, part, false,
                              static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
@@ -408,14 +408,17 @@ int moe_forward(const void* X, const float* logits, const void* W1, const void* 
     if (!inv) inv = ws_inv;
 
     HIPCHECK(launch_gate(logits, T, E, K, topk_idx, topk_w, blk, s));
+    // the scan also clears the grouped GEMMs' claim counters (no launches of their own)
+    int* tickets = ffn_tickets(part);
+    const int nt = tickets != nullptr ? ffn_ticket_ints() : 0;
     if (scan_rank_fused(T, E)) {
-        HIPCHECK(launch_scan_rank(topk_idx, T, E, K, blk, counts, offsets, sorted_pair, inv, s));
+        HIPCHECK(launch_scan_rank(topk_idx, T, E, K, blk, counts, offsets, sorted_pair, inv, tickets, nt, s));
     } else {
-        HIPCHECK(launch_scan(blk, B, E, counts, offsets, blkbase, s));
+        HIPCHECK(launch_scan(blk, B, E, counts, offsets, blkbase, s, tickets, nt));
         HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s));
     }
     HIPCHECK(launch_copy_rows(X, (size_t)d * sz, T, K, inv, Xp, s));
-    HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, (int)A, d, E, n, counts, offsets, Act, Yb, part, s));
+    HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, (int)A, d, E, n, counts, offsets, Act, Yb, part, true, s));
     HIPCHECK(launch_combine(Yb, topk_w, inv, dtype, T, d, K, out, s));
     return MOE_OK;
 }

@@ -54,7 +54,8 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ counts,
                                                         int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ sorted_pair,
-                                                        int32_t* __restrict__ inv) {
+                                                        int32_t* __restrict__ inv,
+                                                        int* __restrict__ zero, int nzero) {
     __shared__ unsigned long long mask[kWaves][256];
     __shared__ int pre[kWaves][256];
     __shared__ int run[256];
@@ -62,6 +63,8 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int chunk = blockIdx.x;
+    if (chunk == 0)  // state for later kernels on the stream
+        for (int i = tid; i < nzero; i += kThreads) zero[i] = 0;
     if (blkbase != nullptr) {
         for (int e = tid; e < E; e += kThreads) run[e] = blkbase[(size_t)chunk * E + e];
     } else {  // E <= 256 == kThreads: thread e owns expert e
@@ -207,15 +210,17 @@ hipError_t launch_rank(const int32_t* idx, int T, int E, int K, const int32_t* b
                        int32_t* sorted_pair, int32_t* inv, hipStream_t s) {
     hipLaunchKernelGGL(rank_kernel, dim3(num_chunks(T)), dim3(kThreads), 0, s, idx, T, E, K,
                        chunk_tokens(T), blkbase, static_cast<const int32_t*>(nullptr), 0,
-                       static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr), sorted_pair, inv);
+                       static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr), sorted_pair, inv,
+                       static_cast<int*>(nullptr), 0);
     return hipGetLastError();
 }
 
 hipError_t launch_scan_rank(const int32_t* idx, int T, int E, int K, const int32_t* blk, int32_t* counts,
-                            int32_t* offsets, int32_t* sorted_pair, int32_t* inv, hipStream_t s) {
+                            int32_t* offsets, int32_t* sorted_pair, int32_t* inv, int* zero, int nzero,
+                            hipStream_t s) {
     hipLaunchKernelGGL(rank_kernel, dim3(num_chunks(T)), dim3(kThreads), 0, s, idx, T, E, K,
                        chunk_tokens(T), static_cast<const int32_t*>(nullptr), blk, num_chunks(T), counts,
-                       offsets, sorted_pair, inv);
+                       offsets, sorted_pair, inv, zero, zero != nullptr ? nzero : 0);
     return hipGetLastError();
 }
 

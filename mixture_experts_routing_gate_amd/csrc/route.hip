@@ -491,10 +491,12 @@ constexpr int kScanBatch = 32;
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ blk, int B,
                                                             int E, int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ blkbase) {
+                                                            int32_t* __restrict__ blkbase,
+                                                            int* __restrict__ zero, int nzero) {
     __shared__ int part[kScanThreads];  // [Q][E]: chunk-group sums, then their exclusive prefix
     __shared__ int sc[2][256];          // scan buffers over experts
     const int tid = threadIdx.x;
+    for (int i = tid; i < nzero; i += kScanThreads) zero[i] = 0;
     const int Q = kScanThreads / E;  // chunk groups (>= 4 since E <= 256)
     const int e = tid % E;
     const int q = tid / E;
@@ -600,9 +602,9 @@ hipError_t launch_gate(const float* logits, int T, int E, int K, int32_t* idx, f
 }
 
 hipError_t launch_scan(const int32_t* blk, int B, int E, int32_t* counts, int32_t* offsets,
-                       int32_t* blkbase, hipStream_t s) {
+                       int32_t* blkbase, hipStream_t s, int* zero, int nzero) {
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk, B, E, counts, offsets,
-                       blkbase);
+                       blkbase, zero, zero != nullptr ? nzero : 0);
     return hipGetLastError();
 }
 
