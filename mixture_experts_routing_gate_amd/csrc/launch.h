@@ -50,13 +50,18 @@ int* ffn_tickets(float* part);
 int ffn_ticket_ints();
 hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int rows, int d, int E,
                          int n, const int32_t* counts, const int32_t* offsets, void* Act, float* part,
-                         bool tickets_zeroed, hipStream_t s);
+                         bool tickets_zeroed, hipStream_t s, const int32_t* gather = nullptr, int gK = 1);
 hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows, int d, int E, int n,
                            const int32_t* counts, const int32_t* offsets, void* Y, float* part,
                            bool tickets_zeroed, hipStream_t s);
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
                       int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
-                      void* Act, void* Y, float* part, bool tickets_zeroed, hipStream_t s);
+                      void* Act, void* Y, float* part, bool tickets_zeroed, hipStream_t s,
+                      const int32_t* gather = nullptr, int gK = 1);
+// With `gather` (sorted_pair) the SwiGLU GEMM reads its rows straight from the
+// token-ordered X (passed as Xp): row p of the expert-sorted order is X row
+// gather[p] / gK.  Only where ffn_gather_ok().
+bool ffn_gather_ok(int dtype, int T, int d, int n);
 
 // Router projection upstream of step 1: logits = X Wr (+ bias).  `split` is a
 // workspace of router_split_bytes() bytes (0: none needed) for the bf16 split

@@ -417,8 +417,14 @@ int moe_forward(const void* X, const float* logits, const void* W1, const void* 
         HIPCHECK(launch_scan(blk, B, E, counts, offsets, blkbase, s, tickets, nt));
         HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s));
     }
-    HIPCHECK(launch_copy_rows(X, (size_t)d * sz, T, K, inv, Xp, s));
-    HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, (int)A, d, E, n, counts, offsets, Act, Yb, part, true, s));
+    if (ffn_gather_ok(dtype, T, d, n)) {
+        // no permuted copy of X: the SwiGLU GEMM gathers its rows through sorted_pair
+        HIPCHECK(launch_ffn(X, W1, W3, W2, dtype, (int)A, d, E, n, counts, offsets, Act, Yb, part, true, s,
+                            sorted_pair, K));
+    } else {
+        HIPCHECK(launch_copy_rows(X, (size_t)d * sz, T, K, inv, Xp, s));
+        HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, (int)A, d, E, n, counts, offsets, Act, Yb, part, true, s));
+    }
     HIPCHECK(launch_combine(Yb, topk_w, inv, dtype, T, d, K, out, s));
     return MOE_OK;
 }
