@@ -964,7 +964,11 @@ hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dty
                          int n, const int32_t* counts, const int32_t* offsets, void* Act, float* part,
                          bool tickets_zeroed, hipStream_t s, const int32_t* gather, int gK) {
     const int cus = device_cu_count();
-    if (dtype == 1 && ffn_pipelined_ok(d, n))
+    const bool pipelined = dtype == 1 && ffn_pipelined_ok(d, n);
+    // Only the pipelined kernel gathers; the others would index the
+    // token-ordered X by expert-sorted row, past its end.
+    if (gather != nullptr && !(pipelined && ffn_gather_ok(dtype, rows / gK, d, n))) return hipErrorInvalidValue;
+    if (pipelined)
         return launch_pipelined<true>(static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
                                       static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(Act), counts,
                                       offsets, E, d, n, rows, part, tickets_zeroed, gather, gK, s);
