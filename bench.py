@@ -102,9 +102,10 @@ def kernel_traffic(workload, kernel):
 
 
 def traffic_probe(moe, synth, torch, dev):
-    """A plain copy of known size, then each step of the layer once on the
-    mixtral-shaped workload and the gate on the large gate workload (each after
-    one warm-up call), for FETCH_SIZE / WRITE_SIZE counter runs."""
+    """A plain copy of known size, then the router projection and each step of
+    the layer once on the mixtral-shaped workload and the gate on the large gate
+    workload (each after one warm-up call), for FETCH_SIZE / WRITE_SIZE counter
+    runs."""
     n = 256 << 20  # 512 MiB of bf16
     src = torch.ones(n, dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
@@ -112,7 +113,9 @@ def traffic_probe(moe, synth, torch, dev):
     torch.cuda.synchronize()
     cfg = synth.CONFIGS["mixtral"]
     g = synth.make_inputs(cfg, dev, seed=0)
+    Wr, rb = synth.make_router(cfg, dev, seed=0)
     for _ in range(2):
+        moe.moe_router(g["X"], Wr, rb)
         idx, w, counts, offsets = moe.moe_route(g["logits"], cfg.K)
         sp, inv, Xp = moe.moe_permute(g["X"], idx, cfg.E)
         Act = moe.moe_ffn_up(Xp, g["W1"], g["W3"], counts, offsets, cfg.K)
