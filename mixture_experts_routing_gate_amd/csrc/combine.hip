@@ -19,8 +19,9 @@ constexpr int kWaves = kThreads / kWave;
 
 // One wave per token; each lane owns 16-byte chunks of the row (8 bf16 or 4 fp32).
 // K <= KC; each lane keeps U * KC row loads in flight (U chunks of each of the
-// K source rows) before the first multiply-add: 8 for K <= 4, 16 for K <= 8
-// (measured best on the Mixtral-, fine- and DeepSeek-V3-shaped layers).  The
+// K source rows) before the first multiply-add: 4 for K = 2, 8 for K = 1 and
+// K <= 4, 16 for K <= 8 (measured best on the Mixtral-, fine- and
+// DeepSeek-V3-shaped layers).  The
 // output row is written with streaming stores: it is not read again here.
 template <bool BF16, int KC>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const u32x4* __restrict__ Y,
@@ -28,7 +29,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const u32x4* __restri
                                                            const int32_t* __restrict__ inv, int T,
                                                            int row_chunks, int K,
                                                            u32x4* __restrict__ out) {
-    constexpr int U = KC == 8 ? 2 : 8 / KC;
+    constexpr int U = KC == 8 ? 2 : KC == 2 ? 2 : 8 / KC;
     constexpr int NV = BF16 ? 8 : 4;
     const int lane = threadIdx.x & (kWave - 1);
     const int t = blockIdx.x * kWaves + threadIdx.x / kWave;
