@@ -22,6 +22,8 @@ CASES = [
     synth.MoEConfig("min_dims", T=257, d=128, E=4, K=2, n=128),
     synth.MoEConfig("fine_small", T=2048, d=256, E=128, K=4, n=128, logits="bias", bias_var=2.0),
     synth.MoEConfig("f32_e256", T=300, d=64, E=256, K=8, n=64, dtype="f32"),
+    # every expert short (a few rows each): short tiles, tile claiming, gathered loads
+    synth.MoEConfig("bf16_e256_k8", T=600, d=256, E=256, K=8, n=128, logits="bias", bias_var=1.5),
 ]
 
 
