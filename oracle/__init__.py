@@ -54,9 +54,15 @@ def _load():
         lib.oracle_expert_down.argtypes = [P, I, I, P, P, I, I, I, P]
         lib.oracle_layer.argtypes = [P, I, P, P, P, P, I, I, I, I, I, P, I, P]
         lib.oracle_router.argtypes = [P, I, P, P, I, I, I, P]
+        L = ctypes.c_int64
+        lib.oracle_tr_target.argtypes = [ctypes.c_int32, I, I, I]
+        lib.oracle_tr_target.restype = ctypes.c_int32
+        lib.oracle_token_round.argtypes = [P, I, I, I, I, I, P, P, P, L, P, P]
+        lib.oracle_tr_combine.argtypes = [P, P, P, I, I, I, L, P]
+        lib.oracle_tr_layer.argtypes = [P, I, P, P, P, P, P, I, I, I, I, P, I, P]
         for f in (lib.oracle_softmax, lib.oracle_route, lib.oracle_permute, lib.oracle_gather_rows,
                   lib.oracle_expert_ffn, lib.oracle_combine, lib.oracle_layer, lib.oracle_expert_down,
-                  lib.oracle_router):
+                  lib.oracle_router, lib.oracle_token_round, lib.oracle_tr_combine, lib.oracle_tr_layer):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -208,6 +214,65 @@ def layer(X, logits, W1, W3, W2, K: int, tokens=None) -> np.ndarray:
     out = np.empty((ntok, d), np.float32)
     _check(_load().oracle_layer(_ptr(Xs), dt, _ptr(lg), _ptr(W1s), _ptr(W3s), _ptr(W2s), T, d, E, K, n,
                                 tp, ntok, _ptr(out)), "oracle_layer")
+    return out
+
+
+def tr_target(f: int, M: int, T: int, cap_tiles: int = 0) -> int:
+    """Rows an expert with f routed tokens keeps under Token Rounding."""
+    return int(_load().oracle_tr_target(int(f), int(M), int(T), int(cap_tiles)))
+
+
+def token_round(logits: np.ndarray, K: int, M: int, cap_tiles: int = 0):
+    """Token Rounding plan.  -> dict with counts_r int32 [E], offsets_r int32 [E+1],
+    row_tok int32 [rows], slot_row int32 [T,E] (-1 where not kept), slot_w float32 [T,E]."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    cap = T * E
+    counts_r = np.empty(E, np.int32)
+    offsets_r = np.empty(E + 1, np.int32)
+    row_tok = np.empty(max(cap, 1), np.int32)
+    slot_row = np.empty((T, E), np.int32)
+    slot_w = np.empty((T, E), np.float32)
+    _check(_load().oracle_token_round(_ptr(lg), T, E, K, M, cap_tiles, _ptr(counts_r), _ptr(offsets_r),
+                                      _ptr(row_tok), cap, _ptr(slot_row), _ptr(slot_w)), "oracle_token_round")
+    return {"counts_r": counts_r, "offsets_r": offsets_r, "row_tok": row_tok[: int(offsets_r[E])].copy(),
+            "slot_row": slot_row, "slot_w": slot_w}
+
+
+def tr_combine(Y: np.ndarray, slot_row: np.ndarray, slot_w: np.ndarray) -> np.ndarray:
+    """out[t] = sum over kept experts e (ascending) of slot_w[t,e] * Y[slot_row[t,e]] (fp64)."""
+    Yc = _c(Y, np.float32)
+    sr = _c(slot_row, np.int32)
+    sw = _c(slot_w, np.float32)
+    T, E = sr.shape
+    nrows, d = Yc.shape
+    out = np.empty((T, d), np.float32)
+    _check(_load().oracle_tr_combine(_ptr(Yc), _ptr(sr), _ptr(sw), T, E, d, nrows, _ptr(out)),
+           "oracle_tr_combine")
+    return out
+
+
+def tr_layer(X, slot_row, slot_w, W1, W3, W2, tokens=None) -> np.ndarray:
+    """Layer after Token Rounding, per-token loop over the kept experts.  -> float32 [ntok, d]."""
+    Xs, dt = _storage(X)
+    W1s, d1 = _storage(W1)
+    W3s, d3 = _storage(W3)
+    W2s, d2 = _storage(W2)
+    if not (dt == d1 == d3 == d2):
+        raise ValueError("X and the expert weights must share one storage dtype")
+    sr = _c(slot_row, np.int32)
+    sw = _c(slot_w, np.float32)
+    T, d = Xs.shape
+    E, _, n = W1s.shape
+    assert sr.shape == (T, E) and sw.shape == (T, E)
+    if tokens is None:
+        ntok, tp = T, None
+    else:
+        tk = _c(tokens, np.int32)
+        ntok, tp = tk.size, _ptr(tk)
+    out = np.empty((ntok, d), np.float32)
+    _check(_load().oracle_tr_layer(_ptr(Xs), dt, _ptr(sr), _ptr(sw), _ptr(W1s), _ptr(W3s), _ptr(W2s), T, d, E,
+                                   n, tp, ntok, _ptr(out)), "oracle_tr_layer")
     return out
 
 

@@ -27,6 +27,12 @@
  *                  from library matmuls; identical experts reduce to that MLP
  *                  for any routing; zero row; exact scaling by 2
  *   expert down  - reproduces expert FFN's y from its act; library matmul
+ *   token rounding - hand-worked examples (tests/golden); the rounding rule's
+ *                  nearest-multiple property; brute force that each expert
+ *                  keeps its best-ranked candidates; M = 1 equals top-K;
+ *                  weights sum to 1 with the logit ratios; the combine on
+ *                  one-hot and token-index rows; identical experts give the
+ *                  dense MLP built from library matmuls
  * Every function here is pinned; none is "parity unpinned".
  *
  * Errors: every entry point returns 0 on success and a negative value on a
@@ -306,4 +312,174 @@ int oracle_router(const void* X, int dtype, const float* Wr, const float* bias, 
         }
     }
     return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Token Rounding, the routing variant of [P4] section 3.  Section 3.1: the
+ * per-expert token counts of ordinary top-K routing are rounded to a multiple
+ * of the tile size M, up or down, and a second sort by score decides which
+ * tokens an expert drops or takes on, so that every expert's row count is a
+ * whole number of tiles.  Section 3.2: the rounding goes to the nearest
+ * multiple (a remainder of exactly M/2 rounds up), the routing weights are
+ * renormalised by a softmax over what each token keeps, and one expert may be
+ * limited to a number of tiles (that section names 2M tokens).
+ *
+ * Readings taken where the pages leave a step open:
+ *   - the counts rounded are those of oracle_route's top-K;
+ *   - a target above T (an expert cannot take a token twice) rounds down;
+ *   - cap_tiles > 0 limits a target to cap_tiles * M rows; 0 means no limit;
+ *   - the second sort ranks tokens for expert e by logit[t,e] descending,
+ *     then token index ascending.  An expert whose target is below its count
+ *     keeps its best routed tokens; one whose target is above keeps all of
+ *     them and takes on the best tokens not routed to it;
+ *   - a token left with no expert contributes a zero output row;
+ *   - rows are laid out expert by expert, tokens ascending inside an expert.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    float l;
+    int32_t t;
+} tr_cand;
+
+/* Better candidate first: larger logit, then lower token index. */
+static int tr_cand_cmp(const void* a, const void* b) {
+    const tr_cand* x = (const tr_cand*)a;
+    const tr_cand* y = (const tr_cand*)b;
+    if (x->l > y->l) return -1;
+    if (x->l < y->l) return 1;
+    return (x->t > y->t) - (x->t < y->t);
+}
+
+/* Rows an expert with f routed tokens ends up with. */
+int32_t oracle_tr_target(int32_t f, int M, int T, int cap_tiles) {
+    int64_t r = (((int64_t)f + M / 2) / M) * M;
+    if (r > T) r -= M;
+    if (cap_tiles > 0 && r > (int64_t)cap_tiles * M) r = (int64_t)cap_tiles * M;
+    return (int32_t)r;
+}
+
+/* Outputs: counts_r[E], offsets_r[E+1] (exclusive sums, offsets_r[E] = rows),
+ * row_tok[rows] (token of each row), slot_row[T,E] (row of (t,e) or -1) and
+ * slot_w[T,E] (weight of (t,e), 0 where not kept):
+ *   w[t,e] = exp(l[t,e] - m) / sum_{e' kept by t} exp(l[t,e'] - m),
+ * m the largest kept logit of t, in fp64, rounded once.  rows_cap is the room
+ * in row_tok; more rows than that is an error (-4). */
+int oracle_token_round(const float* logits, int T, int E, int K, int M, int cap_tiles,
+                       int32_t* counts_r, int32_t* offsets_r, int32_t* row_tok, int64_t rows_cap,
+                       int32_t* slot_row, float* slot_w) {
+    if (!logits || !counts_r || !offsets_r || !row_tok || !slot_row || !slot_w) return -1;
+    if (T < 0 || E < 1 || K < 1 || K > E || M < 1 || cap_tiles < 0 || rows_cap < 0) return -1;
+    const size_t TE = (size_t)T * E;
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * ((size_t)T * K + 1));
+    float* w = (float*)malloc(sizeof(float) * ((size_t)T * K + 1));
+    int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+    char* routed = (char*)calloc(TE + 1, 1);
+    char* kept = (char*)calloc(TE + 1, 1);
+    tr_cand* cand = (tr_cand*)malloc(sizeof(tr_cand) * ((size_t)T + 1));
+    int rc = (idx && w && counts && offsets && routed && kept && cand) ? 0 : -3;
+    if (rc == 0) rc = oracle_route(logits, T, E, K, idx, w, counts, offsets);
+    if (rc == 0) {
+        for (size_t q = 0; q < (size_t)T * K; ++q) routed[(q / K) * E + idx[q]] = 1;
+        int64_t run = 0;
+        for (int e = 0; e < E; ++e) {
+            const int32_t f = counts[e];
+            const int32_t r = oracle_tr_target(f, M, T, cap_tiles);
+            int n = 0;
+            if (r <= f) {
+                /* keep the r best routed tokens */
+                for (int t = 0; t < T; ++t)
+                    if (routed[(size_t)t * E + e]) { cand[n].l = logits[(size_t)t * E + e]; cand[n].t = t; ++n; }
+                qsort(cand, (size_t)n, sizeof(tr_cand), tr_cand_cmp);
+                for (int j = 0; j < r; ++j) kept[(size_t)cand[j].t * E + e] = 1;
+            } else {
+                /* keep every routed token and take on the r - f best others */
+                for (int t = 0; t < T; ++t) {
+                    if (routed[(size_t)t * E + e]) kept[(size_t)t * E + e] = 1;
+                    else { cand[n].l = logits[(size_t)t * E + e]; cand[n].t = t; ++n; }
+                }
+                qsort(cand, (size_t)n, sizeof(tr_cand), tr_cand_cmp);
+                for (int j = 0; j < r - f; ++j) kept[(size_t)cand[j].t * E + e] = 1;
+            }
+            counts_r[e] = r;
+            offsets_r[e] = (int32_t)run;
+            run += r;
+        }
+        offsets_r[E] = (int32_t)run;
+        if (run > rows_cap) rc = -4;
+    }
+    if (rc == 0) {
+        int32_t p = 0;
+        for (int e = 0; e < E; ++e)
+            for (int t = 0; t < T; ++t) {
+                if (kept[(size_t)t * E + e]) { row_tok[p] = t; slot_row[(size_t)t * E + e] = p; ++p; }
+                else slot_row[(size_t)t * E + e] = -1;
+            }
+        for (int t = 0; t < T; ++t) {
+            const float* l = logits + (size_t)t * E;
+            double m = -INFINITY;
+            for (int e = 0; e < E; ++e)
+                if (kept[(size_t)t * E + e] && (double)l[e] > m) m = (double)l[e];
+            double s = 0.0;
+            for (int e = 0; e < E; ++e)
+                if (kept[(size_t)t * E + e]) s += exp((double)l[e] - m);
+            for (int e = 0; e < E; ++e)
+                slot_w[(size_t)t * E + e] = kept[(size_t)t * E + e] ? (float)(exp((double)l[e] - m) / s) : 0.0f;
+        }
+    }
+    free(idx); free(w); free(counts); free(offsets); free(routed); free(kept); free(cand);
+    return rc;
+}
+
+/* Combine after Token Rounding: the aggregation of [P4] section 1 over the
+ * experts a token kept, in ascending expert order, in fp64:
+ *   out[t,c] = sum_{e: slot_row[t,e] >= 0} slot_w[t,e] * Y[slot_row[t,e], c]. */
+int oracle_tr_combine(const float* Y, const int32_t* slot_row, const float* slot_w, int T, int E, int d,
+                      int64_t nrows, float* out) {
+    if (!Y || !slot_row || !slot_w || !out || T < 0 || E < 1 || d < 0 || nrows < 0) return -1;
+    for (int t = 0; t < T; ++t)
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int e = 0; e < E; ++e) {
+                const int32_t r = slot_row[(size_t)t * E + e];
+                if (r < 0) continue;
+                if (r >= nrows) return -1;
+                acc += (double)slot_w[(size_t)t * E + e] * (double)Y[(size_t)r * d + c];
+            }
+            out[(size_t)t * d + c] = (float)acc;
+        }
+    return 0;
+}
+
+/* The layer after Token Rounding, per token: each expert the token kept runs
+ * its MLP on the token row and the outputs are summed with the kept weights,
+ * in ascending expert order ([P4] section 1, Router -> Experts -> Aggregator,
+ * with the routing of section 3).  Only slot_row's sign is used: the rows
+ * themselves play no part.  tokens == NULL means all T tokens. */
+int oracle_tr_layer(const void* X, int dtype, const int32_t* slot_row, const float* slot_w, const void* W1,
+                    const void* W3, const void* W2, int T, int d, int E, int n, const int32_t* tokens, int ntok,
+                    float* out) {
+    if (!X || !slot_row || !slot_w || !W1 || !W3 || !W2 || !out) return -1;
+    if (T < 0 || d < 1 || E < 1 || n < 1 || ntok < 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int s = 0; s < ntok; ++s) {
+        const int t = tokens ? tokens[s] : s;
+        if (t < 0 || t >= T) { bad |= 1; continue; }
+        double* h1 = (double*)malloc(sizeof(double) * (size_t)n);
+        double* h3 = (double*)malloc(sizeof(double) * (size_t)n);
+        float* a = (float*)malloc(sizeof(float) * (size_t)n);
+        float* y = (float*)malloc(sizeof(float) * (size_t)d);
+        double* acc = (double*)calloc((size_t)d, sizeof(double));
+        for (int e = 0; e < E; ++e) {
+            if (slot_row[(size_t)t * E + e] < 0) continue;
+            expert_row(X, (size_t)t * d, dtype, W1, W3, W2, (size_t)e * d * n, (size_t)e * n * d, d, n, h1, h3,
+                       a, y);
+            const double we = (double)slot_w[(size_t)t * E + e];
+            for (int c = 0; c < d; ++c) acc[c] += we * (double)y[c];
+        }
+        for (int c = 0; c < d; ++c) out[(size_t)s * d + c] = (float)acc[c];
+        free(h1); free(h3); free(a); free(y); free(acc);
+    }
+    return bad ? -1 : 0;
 }
