@@ -222,6 +222,77 @@ int moe_forward(const void* X, const float* logits, const void* W1, const void* 
                 int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
                 int32_t* sorted_pair, int32_t* inv, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Token Rounding -- the routing variant of [P4] section 3.  Section 3.1: the
+ * per-expert counts of top-K routing are rounded to whole tiles of M rows and
+ * a second sort by score picks which tokens each expert drops or takes on.
+ * Section 3.2: rounding to the nearest multiple (a remainder of exactly M/2
+ * rounds up), a per-expert limit (cap_tiles tiles; 0 = none; the page names
+ * 2M tokens) and the weights renormalised by a softmax over what each token
+ * keeps.  Readings where the pages leave a step open:
+ *   - f_e = rows of expert e under top-K (the `counts` of moe_route);
+ *     r_e = M*floor((f_e + floor(M/2)) / M), less M if that exceeds T, then
+ *     at most cap_tiles*M when cap_tiles > 0;
+ *   - tokens are ranked for expert e by logits[t,e] descending, then t
+ *     ascending; if r_e <= f_e the expert keeps its r_e best routed tokens,
+ *     else all its routed tokens plus the r_e - f_e best others;
+ *   - w[t,e] = exp(l[t,e] - m) / sum over the experts t kept of exp(l - m),
+ *     m the largest kept logit (fp32); a token that kept none gets a zero row.
+ * Plan layout: rows expert by expert (offsets_r), tokens ascending inside an
+ * expert; row_tok[row] = token; slot_row[t,e] = the row of (t,e) or -1;
+ * slot_w[t,e] = its weight or 0.  Every row count is a multiple of M, so the
+ * grouped GEMM runs whole tiles when M is its tile height (256).
+ * At most moe_token_round_max_rows(T,E,K,M) = min(T*E, T*K + E*floor(M/2))
+ * rows; the size functions return 0 for invalid sizes.  1 <= M <= 65536,
+ * T*E < 2^31.
+ */
+long long moe_token_round_max_rows(int T, int E, int K, int M);
+size_t moe_token_round_workspace_bytes(int T, int E, int K, int M);
+
+/*
+ * moe_token_round -- the plan from router logits and moe_route's routing.
+ * In:  logits [T,E] fp32, topk_idx [T,K] int32 and counts [E] int32 as
+ *      moe_route writes them (counts must be the histogram of topk_idx;
+ *      otherwise the plan is unspecified, but nothing is written past
+ *      rows_cap rows).
+ * Out: counts_r [E], offsets_r [E+1], row_tok [rows_cap] (the first
+ *      offsets_r[E] entries are written), slot_row [T,E] int32, slot_w [T,E]
+ *      fp32.  rows_cap must be at least moe_token_round_max_rows(T,E,K,M).
+ * Workspace: moe_token_round_workspace_bytes(T,E,K,M) bytes.
+ */
+int moe_token_round(const float* logits, const int32_t* topk_idx, const int32_t* counts, int T, int E, int K,
+                    int M, int cap_tiles, int32_t* counts_r, int32_t* offsets_r, int32_t* row_tok,
+                    long long rows_cap, int32_t* slot_row, float* slot_w, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * moe_tr_combine -- step 5 after Token Rounding: a gather-sum by token over
+ * the experts it kept, in ascending expert order, no atomics:
+ *   out[t] = sum_{e: 0 <= slot_row[t,e] < rows} slot_w[t,e] * Y[slot_row[t,e]]
+ * in fp32, rounded once to dtype (a token with no row gets zeros).
+ * In:  Y [rows,d] (dtype), slot_row [T,E] int32, slot_w [T,E] fp32.
+ * Out: out [T,d] (dtype).
+ */
+int moe_tr_combine(const void* Y, const int32_t* slot_row, const float* slot_w, int dtype, int T, int E, int d,
+                   long long rows, void* out, void* stream);
+
+/*
+ * moe_forward_tr -- the whole layer with Token Rounding: moe_route,
+ * moe_token_round, the grouped SwiGLU and down GEMMs over the plan's rows
+ * (gathering X rows through row_tok where the tile kernel can) and
+ * moe_tr_combine, on one stream.
+ * In:  as moe_forward, plus M and cap_tiles.  Out: out [T,d].
+ * Optional outputs (may be NULL, then they live in the workspace):
+ *      counts_r [E], offsets_r [E+1], row_tok [moe_token_round_max_rows],
+ *      slot_row [T,E], slot_w [T,E].
+ * Workspace: moe_forward_tr_workspace_bytes(T,d,E,K,n,M,dtype) bytes.
+ */
+size_t moe_forward_tr_workspace_bytes(int T, int d, int E, int K, int n, int M, int dtype);
+int moe_forward_tr(const void* X, const float* logits, const void* W1, const void* W3, const void* W2, int dtype,
+                   int T, int d, int E, int K, int n, int M, int cap_tiles, void* out, int32_t* counts_r,
+                   int32_t* offsets_r, int32_t* row_tok, int32_t* slot_row, float* slot_w, void* ws,
+                   size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

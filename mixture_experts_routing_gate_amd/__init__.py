@@ -41,7 +41,7 @@ def load_library() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
     lib = ctypes.CDLL(LIB_PATH)
-    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    P, I, Z, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_longlong
     sig = {
         "moe_status_string": ([I], ctypes.c_char_p),
         "moe_last_error": ([], ctypes.c_char_p),
@@ -58,6 +58,12 @@ def load_library() -> ctypes.CDLL:
         "moe_ffn_down": ([P, P, I, I, I, I, I, I, P, P, P, P, Z, P], I),
         "moe_combine": ([P, P, P, I, I, I, I, P, P], I),
         "moe_forward": ([P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P], I),
+        "moe_token_round_max_rows": ([I, I, I, I], L),
+        "moe_token_round_workspace_bytes": ([I, I, I, I], Z),
+        "moe_token_round": ([P, P, P, I, I, I, I, I, P, P, P, L, P, P, P, Z, P], I),
+        "moe_tr_combine": ([P, P, P, I, I, I, I, L, P, P], I),
+        "moe_forward_tr_workspace_bytes": ([I, I, I, I, I, I, I], Z),
+        "moe_forward_tr": ([P, P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, Z, P], I),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -273,5 +279,91 @@ def moe_forward(X: torch.Tensor, logits: torch.Tensor, W1: torch.Tensor, W3: tor
     T, d = X.shape
     E, _, n = W1.shape
     plan = ForwardPlan(T, d, E, K, n, X.dtype, X.device)
+    plan(X, logits, W1, W3, W2)
+    return plan.out, plan
+
+
+def moe_token_round(logits: torch.Tensor, topk_idx: torch.Tensor, counts: torch.Tensor, M: int,
+                    cap_tiles: int = 0):
+    """Token Rounding plan from logits [T,E] f32 and moe_route's topk_idx [T,K] / counts [E].
+    Returns a dict: counts_r [E], offsets_r [E+1], row_tok [max rows] (the first offsets_r[E]
+    entries are the plan's), slot_row [T,E] i32, slot_w [T,E] f32."""
+    lib = load_library()
+    T, E = logits.shape
+    K = topk_idx.shape[1]
+    dev = logits.device
+    R = lib.moe_token_round_max_rows(T, E, K, M)
+    nws = lib.moe_token_round_workspace_bytes(T, E, K, M)
+    if R <= 0 or nws == 0:
+        raise MoEError(MOE_ERR_UNSUPPORTED, "moe_token_round_max_rows", lib.moe_last_error().decode())
+    ws = _workspace(nws, dev)
+    plan = {
+        "counts_r": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets_r": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "row_tok": torch.empty(R, dtype=torch.int32, device=dev),
+        "slot_row": torch.empty((T, E), dtype=torch.int32, device=dev),
+        "slot_w": torch.empty((T, E), dtype=torch.float32, device=dev),
+    }
+    _check(lib.moe_token_round(_dev(logits, "logits", torch.float32), _dev(topk_idx, "topk_idx", torch.int32),
+                               _dev(counts, "counts", torch.int32), T, E, K, M, cap_tiles,
+                               plan["counts_r"].data_ptr(), plan["offsets_r"].data_ptr(), plan["row_tok"].data_ptr(),
+                               R, plan["slot_row"].data_ptr(), plan["slot_w"].data_ptr(), ws.data_ptr(), nws,
+                               _stream(dev)), "moe_token_round")
+    return plan
+
+
+def moe_tr_combine(Y: torch.Tensor, slot_row: torch.Tensor, slot_w: torch.Tensor):
+    """Combine after Token Rounding.  Y [rows,d], slot_row [T,E] i32, slot_w [T,E] f32 -> out [T,d]."""
+    lib = load_library()
+    T, E = slot_row.shape
+    rows, d = Y.shape
+    dev = Y.device
+    out = torch.empty((T, d), dtype=Y.dtype, device=dev)
+    _check(lib.moe_tr_combine(_dev(Y, "Y"), _dev(slot_row, "slot_row", torch.int32),
+                              _dev(slot_w, "slot_w", torch.float32), dtype_code(Y.dtype), T, E, d, rows,
+                              out.data_ptr(), _stream(dev)), "moe_tr_combine")
+    return out
+
+
+class ForwardTRPlan:
+    """Preallocated outputs and workspace for repeated moe_forward_tr calls on one shape."""
+
+    def __init__(self, T: int, d: int, E: int, K: int, n: int, M: int, dtype: torch.dtype, device,
+                 cap_tiles: int = 0):
+        lib = load_library()
+        self.T, self.d, self.E, self.K, self.n, self.M, self.cap_tiles = T, d, E, K, n, M, cap_tiles
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.ws_bytes = lib.moe_forward_tr_workspace_bytes(T, d, E, K, n, M, dtype_code(dtype))
+        self.max_rows = lib.moe_token_round_max_rows(T, E, K, M)
+        if self.ws_bytes == 0 or self.max_rows <= 0:
+            raise MoEError(MOE_ERR_UNSUPPORTED, "moe_forward_tr_workspace_bytes", lib.moe_last_error().decode())
+        dev = self.device
+        self.ws = _workspace(self.ws_bytes, dev)
+        self.out = torch.empty((T, d), dtype=dtype, device=dev)
+        self.counts_r = torch.empty(E, dtype=torch.int32, device=dev)
+        self.offsets_r = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.row_tok = torch.empty(self.max_rows, dtype=torch.int32, device=dev)
+        self.slot_row = torch.empty((T, E), dtype=torch.int32, device=dev)
+        self.slot_w = torch.empty((T, E), dtype=torch.float32, device=dev)
+
+    def __call__(self, X, logits, W1, W3, W2):
+        lib = load_library()
+        dt = self.dtype
+        _check(lib.moe_forward_tr(_dev(X, "X", dt), _dev(logits, "logits", torch.float32), _dev(W1, "W1", dt),
+                                  _dev(W3, "W3", dt), _dev(W2, "W2", dt), dtype_code(dt), self.T, self.d, self.E,
+                                  self.K, self.n, self.M, self.cap_tiles, self.out.data_ptr(),
+                                  self.counts_r.data_ptr(), self.offsets_r.data_ptr(), self.row_tok.data_ptr(),
+                                  self.slot_row.data_ptr(), self.slot_w.data_ptr(), self.ws.data_ptr(),
+                                  self.ws_bytes, _stream(self.device)), "moe_forward_tr")
+        return self.out
+
+
+def moe_forward_tr(X: torch.Tensor, logits: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, W2: torch.Tensor,
+                   K: int, M: int = 256, cap_tiles: int = 0):
+    """Whole layer with Token Rounding.  Returns (out [T,d], plan)."""
+    T, d = X.shape
+    E, _, n = W1.shape
+    plan = ForwardTRPlan(T, d, E, K, n, M, X.dtype, X.device, cap_tiles)
     plan(X, logits, W1, W3, W2)
     return plan.out, plan

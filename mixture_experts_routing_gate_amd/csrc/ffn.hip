@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     int E, int Kd, int N, int rows, float* __restrict__ part, int* __restrict__ ticket_ctr,
-    const int32_t* __restrict__ gather, int gK) {
+    const int32_t* __restrict__ gather, int gK, int xrows) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     constexpr int OUTW = DUAL ? 128 : 256;
@@ -547,10 +547,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
             constexpr int MI = decltype(mi_tag)::value;
             // DMA sources.  A: 16 rows of 64 bytes per KB; rows past the segment are
             // clamped to its last row.  B: 4 k-rows of one 128-column half per KB.
-            // With `gather`, A is the token-ordered X and expert-sorted row p is
-            // read from X row gather[p] / gK (page [P4] section 1: the gather
-            // fused into the GEMM's loads, so the permuted copy of X is never
-            // written).
+            // With `gather`, A is the token-ordered X (xrows rows) and
+            // expert-sorted row p is read from X row gather[p] / gK, clamped
+            // into [0, xrows) (page [P4] section 1: the gather fused into the
+            // GEMM's loads, so the permuted copy of X is never written).
             const rsrc_t ra = make_rsrc(gather != nullptr ? A : A + (size_t)r0 * Kd);
             const int half = wave >> 1;
             const uint16_t* bmat = (DUAL && half) ? B1 : B0;
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                 const int ch = (lane & 3) ^ ((r >> 2) & 3);
                 const int rr = min(r, rows_valid - 1);
                 const uint32_t arow =
-                    gather != nullptr ? (uint32_t)min(max(gather[r0 + rr], 0) / gK, rows / gK - 1) : (uint32_t)rr;
+                    gather != nullptr ? (uint32_t)min(max(gather[r0 + rr], 0) / gK, xrows - 1) : (uint32_t)rr;
                 a_vo[i] = (arow * (uint32_t)Kd + ch * 8) * 2u;
                 const int kr = (wave & 1) * 16 + i * 4 + (lane >> 4);
                 const int bc = (lane & 15) ^ ((kr & 3) << 2);
@@ -942,7 +942,7 @@ int ffn_ticket_ints() { return 2 * kTicketInts; }
 template <bool DUAL>
 static hipError_t launch_pipelined(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                                    const int32_t* counts, const int32_t* offsets, int E, int Kd, int N, int rows,
-                                   float* part, bool tickets_zeroed, const int32_t* gather, int gK,
+                                   float* part, bool tickets_zeroed, const int32_t* gather, int gK, int xrows,
                                    hipStream_t s) {
     const hipError_t aerr =
         hipFuncSetAttribute((const void*)ffn_p4_kernel<DUAL>, hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
@@ -952,7 +952,7 @@ static hipError_t launch_pipelined(const uint16_t* A, const uint16_t* B0, const 
     if (tickets != nullptr && !tickets_zeroed)
         hipLaunchKernelGGL(zero_ints, dim3(1), dim3(kTicketInts), 0, s, tickets, kTicketInts);
     hipLaunchKernelGGL(ffn_p4_kernel<DUAL>, dim3(G), dim3(kThreads), kP4Lds, s, A, B0, B1, C, counts, offsets, E, Kd,
-                       N, rows, part, tickets, gather, gK);
+                       N, rows, part, tickets, gather, gK, xrows);
     if (part != nullptr)
         hipLaunchKernelGGL(ffn_split_fixup<DUAL>, dim3(G), dim3(kThreads), 0, s, part, C, counts, offsets, E, Kd, N,
                            rows, G);
@@ -962,16 +962,17 @@ static hipError_t launch_pipelined(const uint16_t* A, const uint16_t* B0, const 
 // Step 4a: Act = SiLU(Xp W1) * (Xp W3).
 hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int rows, int d, int E,
                          int n, const int32_t* counts, const int32_t* offsets, void* Act, float* part,
-                         bool tickets_zeroed, hipStream_t s, const int32_t* gather, int gK) {
+                         bool tickets_zeroed, hipStream_t s, const int32_t* gather, int gK, int xrows) {
     const int cus = device_cu_count();
     const bool pipelined = dtype == 1 && ffn_pipelined_ok(d, n);
     // Only the pipelined kernel gathers; the others would index the
     // token-ordered X by expert-sorted row, past its end.
-    if (gather != nullptr && !(pipelined && ffn_gather_ok(dtype, rows / gK, d, n))) return hipErrorInvalidValue;
+    if (gather != nullptr && !(pipelined && gK >= 1 && xrows >= 1 && ffn_gather_ok(dtype, xrows, d, n)))
+        return hipErrorInvalidValue;
     if (pipelined)
         return launch_pipelined<true>(static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
                                       static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(Act), counts,
-                                      offsets, E, d, n, rows, part, tickets_zeroed, gather, gK, s);
+                                      offsets, E, d, n, rows, part, tickets_zeroed, gather, gK, xrows, s);
     if (dtype == 1) {
         hipLaunchKernelGGL(ffn_bf16_kernel<true>, dim3(cus * 2), dim3(kThreads), 0, s,
                            static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
@@ -994,7 +995,7 @@ hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows,
     if (dtype == 1 && ffn_pipelined_ok(d, n))
         return launch_pipelined<false>(static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
                                        static_cast<const uint16_t*>(nullptr), static_cast<uint16_t*>(Y), counts,
-                                       offsets, E, n, d, rows, part, tickets_zeroed, nullptr, 1, s);
+                                       offsets, E, n, d, rows, part, tickets_zeroed, nullptr, 1, 1, s);
     if (dtype == 1) {
         hipLaunchKernelGGL(ffn_bf16_kernel<false>, dim3(cus * 2), dim3(kThreads), 0, s,
                            static_cast<const uint16_t*>(Act), static_cast<const uint16_t*>(W2),
@@ -1012,9 +1013,9 @@ hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows,
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
                       int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
                       void* Act, void* Y, float* part, bool tickets_zeroed, hipStream_t s,
-                      const int32_t* gather, int gK) {
-    const hipError_t err =
-        launch_ffn_up(Xp, W1, W3, dtype, rows, d, E, n, counts, offsets, Act, part, tickets_zeroed, s, gather, gK);
+                      const int32_t* gather, int gK, int xrows) {
+    const hipError_t err = launch_ffn_up(Xp, W1, W3, dtype, rows, d, E, n, counts, offsets, Act, part,
+                                         tickets_zeroed, s, gather, gK, xrows);
     if (err != hipSuccess) return err;
     return launch_ffn_down(Act, W2, dtype, rows, d, E, n, counts, offsets, Y, part, tickets_zeroed, s);
 }

@@ -50,17 +50,19 @@ int* ffn_tickets(float* part);
 int ffn_ticket_ints();
 hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dtype, int rows, int d, int E,
                          int n, const int32_t* counts, const int32_t* offsets, void* Act, float* part,
-                         bool tickets_zeroed, hipStream_t s, const int32_t* gather = nullptr, int gK = 1);
+                         bool tickets_zeroed, hipStream_t s, const int32_t* gather = nullptr, int gK = 1,
+                         int xrows = 0);
 hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows, int d, int E, int n,
                            const int32_t* counts, const int32_t* offsets, void* Y, float* part,
                            bool tickets_zeroed, hipStream_t s);
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
                       int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
                       void* Act, void* Y, float* part, bool tickets_zeroed, hipStream_t s,
-                      const int32_t* gather = nullptr, int gK = 1);
-// With `gather` (sorted_pair) the SwiGLU GEMM reads its rows straight from the
-// token-ordered X (passed as Xp): row p of the expert-sorted order is X row
-// gather[p] / gK.  Only where ffn_gather_ok().
+                      const int32_t* gather = nullptr, int gK = 1, int xrows = 0);
+// With `gather` the SwiGLU GEMM reads its rows straight from the token-ordered
+// X (passed as Xp, xrows rows): row p of the expert-sorted order is X row
+// gather[p] / gK, clamped into [0, xrows) (sorted_pair with gK = K, or a
+// Token Rounding plan's row_tok with gK = 1).  Only where ffn_gather_ok().
 bool ffn_gather_ok(int dtype, int T, int d, int n);
 
 // Router projection upstream of step 1: logits = X Wr (+ bias).  `split` is a
@@ -73,5 +75,17 @@ hipError_t launch_router(const void* X, int dtype, int T, int d, int E, const fl
 // Step 5.
 hipError_t launch_combine(const void* Y, const float* w, const int32_t* inv, int dtype, int T, int d,
                           int K, void* out, hipStream_t s);
+
+// Token Rounding (routing variant).  tr_target: rows kept by an expert with f
+// routed tokens.  launch_token_round needs tr_keys_bytes(T, E) bytes of `ws`.
+long long tr_target(int f, int M, int T, int cap_tiles);
+size_t tr_keys_bytes(int T, int E);
+hipError_t launch_token_round(const float* logits, const int32_t* idx, const int32_t* counts, int T, int E, int K,
+                              int M, int cap_tiles, int32_t* counts_r, int32_t* offsets_r, int32_t* row_tok,
+                              long long rows_cap, int32_t* slot_row, float* slot_w, void* ws, hipStream_t s);
+hipError_t launch_tr_combine(const void* Y, const int32_t* slot_row, const float* slot_w, int dtype, int T, int E,
+                             int d, long long nrows, void* out, hipStream_t s);
+hipError_t launch_tr_gather_rows(const void* X, size_t row_bytes, int T, const int32_t* row_tok,
+                                 const int32_t* offsets_r, int E, long long rows_cap, void* Xp, hipStream_t s);
 
 }  // namespace moe

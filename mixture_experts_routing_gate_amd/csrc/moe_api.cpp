@@ -135,6 +135,41 @@ int ffn_split_arg(void* ws, size_t ws_bytes, int dtype, int d, int n, float** pa
     return MOE_OK;
 }
 
+// Token Rounding arguments: (T, E, K) as for routing, tile rows M, limit in tiles.
+int check_tr(int T, int E, int K, int M, int cap_tiles) {
+    CHECK(check_tek(T, E, K));
+    if (M < 1) return fail(MOE_ERR_INVALID_ARG, "M must be >= 1 (got %d)", M);
+    if (M > 65536) return fail(MOE_ERR_UNSUPPORTED, "M=%d exceeds the supported maximum 65536", M);
+    if (cap_tiles < 0) return fail(MOE_ERR_INVALID_ARG, "cap_tiles must be >= 0 (got %d)", cap_tiles);
+    if ((long long)T * E >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*E must be < 2^31");
+    return MOE_OK;
+}
+
+// Most rows a Token Rounding plan can have: an expert rounds up by at most
+// floor(M/2) rows and never holds a token twice.
+long long tr_max_rows(int T, int E, int K, int M) {
+    const long long a = (long long)T * K + (long long)E * (M / 2);
+    const long long b = (long long)T * E;
+    return a < b ? a : b;
+}
+
+size_t forward_tr_ws(int T, int d, int E, int K, int n, int M, int dtype) {
+    const size_t A = (size_t)T * K;
+    const size_t R = (size_t)tr_max_rows(T, E, K, M);
+    const size_t s = elem_bytes(dtype);
+    size_t b = 0;
+    b += 2 * align_up((size_t)num_chunks(T) * E * 4);  // blk, blkbase
+    b += align_up(A * 4) * 2;                          // topk_idx, topk_w
+    b += align_up(E * 4) + align_up((E + 1) * 4);      // counts, offsets
+    b += align_up(tr_keys_bytes(T, E));                // keys, flags and rows by expert
+    b += align_up(E * 4) + align_up((E + 1) * 4);      // counts_r, offsets_r
+    b += align_up(R * 4);                              // row_tok
+    b += align_up((size_t)T * E * 4) * 2;              // slot_row, slot_w
+    b += (ffn_gather_ok(dtype, T, d, n) ? 0 : align_up(R * d * s)) + align_up(R * d * s) + align_up(R * n * s);
+    b += align_up(ffn_split_bytes(dtype, d, n));
+    return b;
+}
+
 std::atomic<int> g_cu_count[64];
 
 }  // namespace
@@ -420,12 +455,144 @@ int moe_forward(const void* X, const float* logits, const void* W1, const void* 
     if (ffn_gather_ok(dtype, T, d, n)) {
         // no permuted copy of X: the SwiGLU GEMM gathers its rows through sorted_pair
         HIPCHECK(launch_ffn(X, W1, W3, W2, dtype, (int)A, d, E, n, counts, offsets, Act, Yb, part, true, s,
-                            sorted_pair, K));
+                            sorted_pair, K, T));
     } else {
         HIPCHECK(launch_copy_rows(X, (size_t)d * sz, T, K, inv, Xp, s));
         HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, (int)A, d, E, n, counts, offsets, Act, Yb, part, true, s));
     }
     HIPCHECK(launch_combine(Yb, topk_w, inv, dtype, T, d, K, out, s));
+    return MOE_OK;
+}
+
+long long moe_token_round_max_rows(int T, int E, int K, int M) {
+    if (check_tr(T, E, K, M, 0) != MOE_OK) return 0;
+    return tr_max_rows(T, E, K, M);
+}
+
+size_t moe_token_round_workspace_bytes(int T, int E, int K, int M) {
+    if (check_tr(T, E, K, M, 0) != MOE_OK) return 0;
+    return align_up(tr_keys_bytes(T, E));
+}
+
+int moe_token_round(const float* logits, const int32_t* topk_idx, const int32_t* counts, int T, int E, int K,
+                    int M, int cap_tiles, int32_t* counts_r, int32_t* offsets_r, int32_t* row_tok,
+                    long long rows_cap, int32_t* slot_row, float* slot_w, void* ws, size_t ws_bytes,
+                    void* stream) {
+    CHECK(check_tr(T, E, K, M, cap_tiles));
+    NONNULL(logits);
+    NONNULL(topk_idx);
+    NONNULL(counts);
+    NONNULL(counts_r);
+    NONNULL(offsets_r);
+    NONNULL(row_tok);
+    NONNULL(slot_row);
+    NONNULL(slot_w);
+    const long long need_rows = tr_max_rows(T, E, K, M);
+    if (rows_cap < need_rows)
+        return fail(MOE_ERR_INVALID_ARG, "row_tok needs room for %lld rows (got %lld)", need_rows, rows_cap);
+    const size_t need = align_up(tr_keys_bytes(T, E));
+    if (ws == nullptr || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "moe_token_round needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+    HIPCHECK(launch_token_round(logits, topk_idx, counts, T, E, K, M, cap_tiles, counts_r, offsets_r, row_tok,
+                                need_rows, slot_row, slot_w, ws, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+int moe_tr_combine(const void* Y, const int32_t* slot_row, const float* slot_w, int dtype, int T, int E, int d,
+                   long long rows, void* out, void* stream) {
+    if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1 (got %d)", T);
+    if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1 (got %d)", E);
+    if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E=%d exceeds the supported maximum %d", E, kMaxE);
+    if ((long long)T * E >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*E must be < 2^31");
+    if (rows < 0 || rows >= (1LL << 31)) return fail(MOE_ERR_INVALID_ARG, "rows must be in [0, 2^31)");
+    CHECK(check_dtype(dtype));
+    CHECK(check_row(d, dtype));
+    NONNULL(Y);
+    NONNULL(slot_row);
+    NONNULL(slot_w);
+    NONNULL(out);
+    HIPCHECK(launch_tr_combine(Y, slot_row, slot_w, dtype, T, E, d, rows, out, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+size_t moe_forward_tr_workspace_bytes(int T, int d, int E, int K, int n, int M, int dtype) {
+    if (check_tr(T, E, K, M, 0) != MOE_OK || check_dtype(dtype) != MOE_OK || check_dim("d", d, dtype) != MOE_OK ||
+        check_dim("n", n, dtype) != MOE_OK)
+        return 0;
+    return forward_tr_ws(T, d, E, K, n, M, dtype);
+}
+
+int moe_forward_tr(const void* X, const float* logits, const void* W1, const void* W3, const void* W2, int dtype,
+                   int T, int d, int E, int K, int n, int M, int cap_tiles, void* out, int32_t* counts_r,
+                   int32_t* offsets_r, int32_t* row_tok, int32_t* slot_row, float* slot_w, void* ws,
+                   size_t ws_bytes, void* stream) {
+    CHECK(check_tr(T, E, K, M, cap_tiles));
+    CHECK(check_dtype(dtype));
+    CHECK(check_dim("d", d, dtype));
+    CHECK(check_dim("n", n, dtype));
+    NONNULL(X);
+    NONNULL(logits);
+    NONNULL(W1);
+    NONNULL(W3);
+    NONNULL(W2);
+    NONNULL(out);
+    for (const void* p : {(const void*)counts_r, (const void*)offsets_r, (const void*)row_tok,
+                          (const void*)slot_row, (const void*)slot_w})
+        if (p != nullptr && !aligned16(p))
+            return fail(MOE_ERR_INVALID_ARG, "optional outputs must be 16-byte aligned");
+    const long long R = tr_max_rows(T, E, K, M);
+    if (R >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "the plan's row bound must be < 2^31");
+    if (R * (long long)(d > n ? d : n) >= (1LL << 40))
+        return fail(MOE_ERR_UNSUPPORTED, "rows*max(d,n) must be < 2^40");
+    const size_t need = forward_tr_ws(T, d, E, K, n, M, dtype);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "moe_forward_tr needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t A = (size_t)T * K;
+    const size_t sz = elem_bytes(dtype);
+    const int B = num_chunks(T);
+    const bool gather = ffn_gather_ok(dtype, T, d, n);
+    Carver c(ws);
+    int32_t* blk = c.take<int32_t>((size_t)B * E);
+    int32_t* blkbase = c.take<int32_t>((size_t)B * E);
+    int32_t* idx = c.take<int32_t>(A);
+    float* w = c.take<float>(A);
+    int32_t* counts = c.take<int32_t>(E);
+    int32_t* offsets = c.take<int32_t>(E + 1);
+    void* keys = c.take<char>(tr_keys_bytes(T, E));
+    int32_t* ws_cr = c.take<int32_t>(E);
+    int32_t* ws_or = c.take<int32_t>(E + 1);
+    int32_t* ws_rt = c.take<int32_t>((size_t)R);
+    int32_t* ws_sr = c.take<int32_t>((size_t)T * E);
+    float* ws_sw = c.take<float>((size_t)T * E);
+    void* Xp = gather ? nullptr : c.take<char>((size_t)R * d * sz);
+    void* Yb = c.take<char>((size_t)R * d * sz);
+    void* Act = c.take<char>((size_t)R * n * sz);
+    const size_t split_bytes = ffn_split_bytes(dtype, d, n);
+    float* part = split_bytes ? c.take<float>(split_bytes / sizeof(float)) : nullptr;
+    if (!counts_r) counts_r = ws_cr;
+    if (!offsets_r) offsets_r = ws_or;
+    if (!row_tok) row_tok = ws_rt;
+    if (!slot_row) slot_row = ws_sr;
+    if (!slot_w) slot_w = ws_sw;
+
+    HIPCHECK(launch_gate(logits, T, E, K, idx, w, blk, s));
+    // the scan also clears the grouped GEMMs' claim counters
+    int* tickets = ffn_tickets(part);
+    HIPCHECK(launch_scan(blk, B, E, counts, offsets, blkbase, s, tickets, tickets != nullptr ? ffn_ticket_ints() : 0));
+    HIPCHECK(launch_token_round(logits, idx, counts, T, E, K, M, cap_tiles, counts_r, offsets_r, row_tok, R, slot_row,
+                                slot_w, keys, s));
+    if (gather) {
+        HIPCHECK(launch_ffn(X, W1, W3, W2, dtype, (int)R, d, E, n, counts_r, offsets_r, Act, Yb, part, true, s,
+                            row_tok, 1, T));
+    } else {
+        HIPCHECK(launch_tr_gather_rows(X, (size_t)d * sz, T, row_tok, offsets_r, E, R, Xp, s));
+        HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, (int)R, d, E, n, counts_r, offsets_r, Act, Yb, part, true, s));
+    }
+    HIPCHECK(launch_tr_combine(Yb, slot_row, slot_w, dtype, T, E, d, R, out, s));
     return MOE_OK;
 }
 

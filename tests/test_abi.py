@@ -122,3 +122,47 @@ def test_router_workspace_and_rejections(lib):
     assert lib.moe_router(P, 1, 16, 4096, 8, P, None, P, P, wsb - 1, None) == WORKSPACE
     assert lib.moe_router(P + 8, 1, 16, 4096, 8, P, None, P, P, wsb, None) == INVALID  # X misaligned
     assert lib.moe_router(P, 7, 16, 4096, 8, P, None, P, P, wsb, None) == UNSUPPORTED  # dtype
+
+
+def test_token_round_sizes_and_rejections(lib):
+    # an expert rounds up by at most floor(M/2) rows and holds a token at most once
+    assert lib.moe_token_round_max_rows(8192, 8, 2, 256) == 8192 * 2 + 8 * 128
+    assert lib.moe_token_round_max_rows(100, 4, 2, 256) == 100 * 4
+    assert lib.moe_token_round_max_rows(16, 8, 2, 0) == 0
+    assert lib.moe_token_round_workspace_bytes(8192, 8, 2, 256) >= 8192 * 8 * 9
+    assert lib.moe_token_round_workspace_bytes(16, 8, 9, 4) == 0
+    R = lib.moe_token_round_max_rows(16, 8, 2, 4)
+    good = [P, P, P, 16, 8, 2, 4, 0, P, P, P, R, P, P, P, 1 << 20, None]
+
+    def call(**kw):
+        a = list(good)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.moe_token_round(*a)
+
+    assert call(a6=0) == INVALID            # M
+    assert call(a6=70000) == UNSUPPORTED
+    assert call(a7=-1) == INVALID           # cap_tiles
+    assert call(a11=R - 1) == INVALID       # row_tok too small
+    assert call(a0=None) == INVALID
+    assert call(a2=None) == INVALID         # counts
+    assert call(a13=P + 4) == INVALID       # misaligned slot_row
+    assert call(a15=0) == WORKSPACE
+    assert call(a4=300) == UNSUPPORTED      # E
+    assert lib.moe_last_error()
+
+
+def test_tr_combine_and_forward_tr_reject(lib):
+    assert lib.moe_tr_combine(P, P, P, moe.MOE_BF16, 0, 8, 128, 10, P, None) == INVALID
+    assert lib.moe_tr_combine(P, P, P, moe.MOE_BF16, 16, 300, 128, 10, P, None) == UNSUPPORTED
+    assert lib.moe_tr_combine(P, P, P, moe.MOE_BF16, 16, 8, 100, 10, P, None) == UNSUPPORTED  # row of 200 bytes
+    assert lib.moe_tr_combine(P, P, P, moe.MOE_BF16, 16, 8, 128, -1, P, None) == INVALID
+    assert lib.moe_tr_combine(P, None, P, moe.MOE_BF16, 16, 8, 128, 10, P, None) == INVALID
+    T, d, E, K, n, M = 8192, 4096, 8, 2, 14336, 256
+    R = lib.moe_token_round_max_rows(T, E, K, M)
+    assert lib.moe_forward_tr_workspace_bytes(T, d, E, K, n, M, moe.MOE_BF16) >= R * (d + n) * 2
+    assert lib.moe_forward_tr_workspace_bytes(T, d, E, K, n, 0, moe.MOE_BF16) == 0
+    args = [P, P, P, P, P, moe.MOE_BF16, T, d, E, K, n, M, 0, P, None, None, None, None, None, P, 0, None]
+    assert lib.moe_forward_tr(*args) == WORKSPACE
+    args[11] = 0
+    assert lib.moe_forward_tr(*args) == INVALID
