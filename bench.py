@@ -11,6 +11,9 @@ n=14336, bf16, fp32 accumulation), inputs resident in HBM.  Prints ONE JSON line
                 of the pipelined MFMA kernel), MFMA-bound, against 2.5 PFLOP/s
                 dense bf16; its HBM traffic comes from the committed rocprofv3
                 counter table (profiles/traffic.json) when it matches ffn.hip
+  token_rounding = the layer with Token Rounding at tile height 256 beside
+                plain top-K on the same inputs (mixtral here; the other shapes
+                under other_workloads), with its plan and combine back to back
   cpu_baseline= the CPU oracle (per-token loop, fp64 accumulation) on a bounded
                 sample of the same layer, on this host's cores
 Inputs are seeded synthetic tensors (see synth/); nothing is read from disk
@@ -274,6 +277,8 @@ def main():
                      "algorithmic_flops_per_launch": up_flops, "us_per_launch": up_ms * 1e3},
     }
 
+    if not args.no_other_workloads:
+        out["token_rounding"] = {"mixtral": token_rounding(cfg, g, plan, moe, torch, np, dev)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, g, args.cpu_seconds, np, torch, synth)
     if not args.no_other_workloads:
@@ -336,8 +341,59 @@ def other_workload(name, moe, synth, torch, np, dev, steps=5):
            "ms_per_step": round(ms, 4), "TFLOPS": 6.0 * A * d * n / (ms * 1e-3) / 1e12,
            "roofline_ms": round(roof_s * 1e3, 4), "frac_of_roofline": roof_s * 1e3 / ms,
            "experts_nonempty": e_act, "max_count": int(counts.max()), "steps_back_to_back": steps,
-           "tile_padding": padded / A - 1.0}
+           "tile_padding": padded / A - 1.0,
+           "token_rounding": token_rounding(c, g, plan, moe, torch, np, dev)}
     del g, plan, Yc, Wr, rb, rws
+    torch.cuda.empty_cache()
+    return res
+
+
+def token_rounding(c, g, plan_topk, moe, torch, np, dev, steps=5, M=256):
+    """The layer with Token Rounding (page "MoE architecture optimisation and
+    SonicMoE practice", section 3) at tile height M, timed beside plain top-K
+    routing on the same inputs in the same run: time per step, rows the grouped
+    GEMMs compute, and the plan and its combine on their own, back to back,
+    against their algorithmic bytes."""
+    T, d, E, K, n, s = c.T, c.d, c.E, c.K, c.n, 2
+    trp = moe.ForwardTRPlan(T, d, E, K, n, M, c.torch_dtype, dev)
+
+    def run_tr():
+        trp(g["X"], g["logits"], g["W1"], g["W3"], g["W2"])
+
+    def run_topk():
+        plan_topk(g["X"], g["logits"], g["W1"], g["W3"], g["W2"])
+
+    def per_step(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    ms_tr = per_step(run_tr)
+    ms_topk = per_step(run_topk)
+    R = int(trp.offsets_r[-1].item())
+    counts_r = trp.counts_r.cpu().numpy().astype(np.int64)
+    counts = plan_topk.counts.cpu().numpy().astype(np.int64)
+    kept_routed = int(np.minimum(counts, counts_r).sum())  # routed pairs an expert keeps
+    idx, _, cnt, _ = moe.moe_route(g["logits"], K)
+    plan_ms = b2b_time_ms(torch, lambda: moe.moe_token_round(g["logits"], idx, cnt, M))
+    Yr = torch.zeros((max(R, 1), d), dtype=c.torch_dtype, device=dev)
+    comb_ms = b2b_time_ms(torch, lambda: moe.moe_tr_combine(Yr, trp.slot_row, trp.slot_w))
+    BW = PEAK_HBM_GBS * 1e9
+    plan_bytes = 12 * T * E + 4 * T * K + 4 * R
+    comb_bytes = 8 * T * E + (R + T) * d * s
+    res = {"M": M, "ms_per_step": round(ms_tr, 4), "ms_per_step_topk_same_run": round(ms_topk, 4),
+           "rows": R, "rows_topk": T * K, "routed_pairs_dropped": T * K - kept_routed,
+           "pairs_added": R - kept_routed, "tile_padding": 0.0 if R == 0 else float(
+               sum(-(-int(x) // 256) * 256 for x in counts_r) / R - 1.0),
+           "TFLOPS_of_rows": 6.0 * R * d * n / (ms_tr * 1e-3) / 1e12,
+           "plan_us_back_to_back": round(plan_ms * 1e3, 2), "plan_frac_hbm": plan_bytes / BW * 1e3 / plan_ms,
+           "combine_us_back_to_back": round(comb_ms * 1e3, 2), "combine_frac_hbm": comb_bytes / BW * 1e3 / comb_ms}
+    del trp, Yr
     torch.cuda.empty_cache()
     return res
 
