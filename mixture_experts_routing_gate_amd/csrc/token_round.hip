@@ -91,25 +91,47 @@ __global__ __launch_bounds__(256) void tr_keys_kernel(const float* __restrict__ 
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kBins = 256;  // radix digit of 8 bits
+constexpr int kSelBatch = 16;  // tokens a thread loads at once (kept for every pass when T <= 16384)
 
-// Exclusive prefix count of `flag` over the workgroup in thread order; *total
-// gets the workgroup's count.  Every thread must call it.
-MOE_DEV int block_excl_count(bool flag, int* s_wave, int* total) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const unsigned long long b = __ballot(flag);
-    const int in_wave = __popcll(b & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wave[wave] = __popcll(b);
-    __syncthreads();
-    int before = 0, tot = 0;
+// Flags and keys of tokens [b0, b0 + kSelBatch) that lie below t_hi; flag 0xFF
+// (neither routed nor not routed) past t_hi.  All loads are issued together.
+MOE_DEV void sel_load(const uint8_t* __restrict__ mem, const uint32_t* __restrict__ key, int b0, int t_hi,
+                      uint8_t (&mm)[kSelBatch], uint32_t (&kk)[kSelBatch]) {
 #pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) {
-        const int v = s_wave[w];
-        before += w < wave ? v : 0;
-        tot += v;
+    for (int j = 0; j < kSelBatch; ++j) {
+        const int t = b0 + j;
+        const bool v = t < t_hi;
+        mm[j] = v ? mem[t] : (uint8_t)0xFF;
+        kk[j] = v ? key[t] : 0u;
     }
+}
+
+// Exclusive prefix sum of a 64-bit value over the workgroup in thread order;
+// *total gets the workgroup's sum.  Every thread must call it.
+MOE_DEV long long block_excl_scan_ll(long long v, long long* s_ll, long long* total) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    long long x = v;
+#pragma unroll
+    for (int s = 1; s < kWave; s <<= 1) {
+        const long long y = __shfl_up(x, s, kWave);
+        if (lane >= s) x += y;
+    }
+    if (lane == kWave - 1) s_ll[wave] = x;
+    __syncthreads();
+    // lanes 0..15 hold the wave totals; sum those before this wave, and all
+    const long long wt = lane < kSelWaves ? s_ll[lane] : 0;
+    long long before = lane < wave ? wt : 0, tot = wt;
+#pragma unroll
+    for (int s = 1; s < kSelWaves; s <<= 1) {
+        before += __shfl_xor(before, s, kWave);
+        tot += __shfl_xor(tot, s, kWave);
+    }
+    before = __shfl(before, 0, kWave);
+    tot = __shfl(tot, 0, kWave);
     __syncthreads();
     *total = tot;
-    return before + in_wave;
+    return before + x - v;
 }
 
 // Workgroup sum of a 64-bit value (fixed order: deterministic).
@@ -131,19 +153,29 @@ MOE_DEV long long block_sum_ll(long long v, long long* s_ll) {
 // of the experts before e.  Writes counts_r[e], offsets_r[e] (and offsets_r[E]
 // from the last expert), row_tok[o .. o+r) and slotT[e*T + t] for every t.
 // Nothing is written past rows_cap rows, whatever counts holds.
+// Thread i owns the contiguous tokens [i*c, (i+1)*c), c = ceil(T / 1024), so
+// thread order is token order and one scan over threads ranks the kept tokens.
 __global__ __launch_bounds__(kSelThreads) void tr_select_kernel(
     const uint32_t* __restrict__ keyT, const uint8_t* __restrict__ memT, int T, int E, int M, int cap_tiles,
     const int32_t* __restrict__ counts, int32_t* __restrict__ counts_r, int32_t* __restrict__ offsets_r,
     int32_t* __restrict__ row_tok, long long rows_cap, int32_t* __restrict__ slotT) {
-    __shared__ int s_hist[256];
-    __shared__ int s_wave[kSelWaves];
+    __shared__ int s_hist[2][kBins];
+    __shared__ int s_scan[kBins];
     __shared__ long long s_ll[kSelWaves];
     __shared__ int s_digit, s_above, s_total;
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
     const int e = blockIdx.x;
     const uint32_t* key = keyT + (size_t)e * T;
     const uint8_t* mem = memT + (size_t)e * T;
     int32_t* srow = slotT + (size_t)e * T;
+    const int c = (T + kSelThreads - 1) / kSelThreads;
+    const int t_lo = min(tid * c, T), t_hi = min(t_lo + c, T);
+    // Each thread's tokens, loaded once when they fit one batch (c is uniform).
+    const bool cached = c <= kSelBatch;
+    uint8_t mm[kSelBatch];
+    uint32_t kk[kSelBatch];
+    if (cached) sel_load(mem, key, t_lo, t_hi, mm, kk);
 
     long long part = 0;
     for (int q = tid; q < e; q += kSelThreads) part += tr_target_dev(min(max(counts[q], 0), T), M, T, cap_tiles);
@@ -172,27 +204,43 @@ __global__ __launch_bounds__(kSelThreads) void tr_select_kernel(
     if (m > 0) {
         uint32_t prefix = 0, hmask = 0;
         need = m;
+        if (tid < kBins) s_hist[0][tid] = 0;
+        __syncthreads();
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass;
-            if (tid < 256) s_hist[tid] = 0;
-            __syncthreads();
-            for (int t = tid; t < T; t += kSelThreads) {
-                if (mem[t] == want) {
-                    const uint32_t k = key[t];
-                    if ((k & hmask) == prefix) atomicAdd(&s_hist[(k >> shift) & 255u], 1);
-                }
+            int* hist = s_hist[pass & 1];
+            if (tid < kBins) s_hist[(pass + 1) & 1][tid] = 0;  // the next pass's bins
+            for (int b0 = t_lo; b0 < t_hi; b0 += kSelBatch) {
+                if (!cached) sel_load(mem, key, b0, t_hi, mm, kk);
+#pragma unroll
+                for (int j = 0; j < kSelBatch; ++j)
+                    if (mm[j] == want && (kk[j] & hmask) == prefix)
+                        atomicAdd(&hist[(kk[j] >> shift) & (kBins - 1)], 1);
             }
             __syncthreads();
-            // above(b) = candidates in bins above b: a suffix sum, one bin per thread
-            if (tid < 256) {
-                int above = 0;
-                for (int b = 255; b > tid; --b) above += s_hist[b];
-                const int v = s_hist[tid];
-                if (above < need && need <= above + v) {
-                    s_digit = tid;
+            // above(b) = candidates in bins above b: an inclusive scan from the
+            // top bin down, 64 bins per wave, then the totals of the waves before.
+            if (tid < kBins) {
+                const int v = hist[kBins - 1 - tid];
+                int x = v;
+#pragma unroll
+                for (int s = 1; s < kWave; s <<= 1) {
+                    const int y = __shfl_up(x, s, kWave);
+                    if (lane >= s) x += y;
+                }
+                s_scan[tid] = x;
+            }
+            __syncthreads();
+            if (tid < kBins) {
+                int incl = s_scan[tid];
+                for (int w = 0; w < wave; ++w) incl += s_scan[w * kWave + kWave - 1];
+                const int v = hist[kBins - 1 - tid];
+                const int above = incl - v;
+                if (above < need && need <= incl) {
+                    s_digit = kBins - 1 - tid;
                     s_above = above;
                 }
-                if (tid == 0) s_total = above + v;
+                if (tid == kBins - 1) s_total = incl;
             }
             __syncthreads();
             if (pass == 0 && s_total <= need) {
@@ -202,73 +250,130 @@ __global__ __launch_bounds__(kSelThreads) void tr_select_kernel(
             prefix |= (uint32_t)s_digit << shift;
             hmask |= 0xFFu << shift;
             need -= s_above;
-            __syncthreads();
         }
         tau = prefix;
     }
 
-    // Kept tokens in ascending order.
-    int base_sel = 0, base_tie = 0;
-    for (int t0 = 0; t0 < T; t0 += kSelThreads) {
-        const int t = t0 + tid;
-        const bool valid = t < T;
-        const uint8_t mb = valid ? mem[t] : 0;
-        const uint32_t k = valid ? key[t] : 0u;
-        const bool cand = valid && m > 0 && mb == want;
-        const bool always = valid && !down && mb == 1;
-        const bool tie = cand && !take_all && k == tau;
-        int tie_total;
-        const int tie_rank = base_tie + block_excl_count(tie, s_wave, &tie_total);
-        const bool sel = always || (cand && (take_all || k > tau)) || (tie && tie_rank < need);
-        int sel_total;
-        const int pos = base_sel + block_excl_count(sel, s_wave, &sel_total);
-        if (valid) {
+    // Kept tokens in ascending order.  Per thread: ties with tau (taken in
+    // token order while fewer than `need` came before) and the other kept
+    // tokens; one scan of both counts gives each thread its first tie rank and
+    // its first row.
+    int n_tie = 0, n_sel = 0;
+    for (int b0 = t_lo; b0 < t_hi; b0 += kSelBatch) {
+        if (!cached) sel_load(mem, key, b0, t_hi, mm, kk);
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+            const bool cand = m > 0 && mm[j] == want;
+            const bool always = !down && mm[j] == 1;
+            if (cand && !take_all) {
+                n_tie += kk[j] == tau;
+                n_sel += kk[j] > tau;
+            } else {
+                n_sel += always || cand;
+            }
+        }
+    }
+    long long tot2;
+    const long long base2 = block_excl_scan_ll(((long long)n_tie << 32) | (long long)n_sel, s_ll, &tot2);
+    int tie_rank = (int)(base2 >> 32);
+    int pos = (int)(base2 & 0xFFFFFFFFll) + min(tie_rank, need);
+    for (int b0 = t_lo; b0 < t_hi; b0 += kSelBatch) {
+        if (!cached) sel_load(mem, key, b0, t_hi, mm, kk);
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+            const int t = b0 + j;
+            if (t >= t_hi) break;
+            const bool cand = m > 0 && mm[j] == want;
+            const bool always = !down && mm[j] == 1;
+            bool sel;
+            if (cand && !take_all) {
+                const bool tie = kk[j] == tau;
+                sel = kk[j] > tau || (tie && tie_rank < need);
+                tie_rank += tie;
+            } else {
+                sel = always || cand;
+            }
             int32_t row = -1;
-            if (sel && room && pos < r) {
-                row = (int32_t)(o + pos);
-                row_tok[row] = t;
+            if (sel) {
+                if (room && pos < r) {
+                    row = (int32_t)(o + pos);
+                    row_tok[row] = t;
+                }
+                ++pos;
             }
             srow[t] = row;
         }
-        base_sel += sel_total;
-        base_tie += tie_total;
     }
 }
 
-constexpr int kSlotTokens = 32;  // tokens per workgroup of tr_slots_kernel
+constexpr int kSlotTokens = 32;                 // tokens per workgroup of tr_slots_kernel
+constexpr int kSlotPerWave = kSlotTokens / 4;   // tokens per wave
+constexpr int kSlotMaxE = 256;                  // experts per token held in registers (4 per lane)
 
 // slot_row[t,e] from slotT[e,t] (through LDS), and slot_w[t,e] = softmax of
 // logits[t,:] over the kept experts: exp(l - m) / sum, m the largest kept
-// logit, fp32; 0 where not kept.  One wave per token.
+// logit, fp32; 0 where not kept.  One wave per token, 8 tokens per wave; the
+// logits of all 8 are loaded before the first is reduced.  E <= 256.
 __global__ __launch_bounds__(256) void tr_slots_kernel(const float* __restrict__ logits,
                                                        const int32_t* __restrict__ slotT, int T, int E,
                                                        int32_t* __restrict__ slot_row, float* __restrict__ slot_w) {
+    constexpr int NE = kSlotMaxE / kWave;
     extern __shared__ int32_t s_rows[];  // [kSlotTokens][E + 1]
     const int t0 = blockIdx.x * kSlotTokens;
     const int ld = E + 1;
-    for (int q = threadIdx.x; q < kSlotTokens * E; q += 256) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    float lv[kSlotPerWave][NE];
+#pragma unroll
+    for (int j = 0; j < kSlotPerWave; ++j) {
+        const int t = t0 + wave * kSlotPerWave + j;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int e = lane + i * kWave;
+            lv[j][i] = (t < T && e < E) ? logits[(size_t)t * E + e] : 0.0f;
+        }
+    }
+    // slotT entries of the 32 tokens (at most 32 per thread), all loads issued together
+    constexpr int NQ = kSlotTokens * kSlotMaxE / 256;
+    int32_t rv[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const int q = threadIdx.x + 256 * i;
+        const int e = q / kSlotTokens, t = t0 + q % kSlotTokens;
+        rv[i] = (e < E && t < T) ? slotT[(size_t)e * T + t] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const int q = threadIdx.x + 256 * i;
         const int e = q / kSlotTokens, tt = q % kSlotTokens;
-        const int t = t0 + tt;
-        s_rows[tt * ld + e] = t < T ? slotT[(size_t)e * T + t] : -1;
+        if (e < E) s_rows[tt * ld + e] = rv[i];
     }
     __syncthreads();
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    for (int tt = wave; tt < kSlotTokens; tt += 4) {
+#pragma unroll
+    for (int j = 0; j < kSlotPerWave; ++j) {
+        const int tt = wave * kSlotPerWave + j;
         const int t = t0 + tt;
         if (t >= T) break;
-        const float* l = logits + (size_t)t * E;
+        int32_t row[NE];
         float mx = -INFINITY;
-        for (int e = lane; e < E; e += kWave)
-            if (s_rows[tt * ld + e] >= 0) mx = fmaxf(mx, l[e]);
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int e = lane + i * kWave;
+            row[i] = e < E ? s_rows[tt * ld + e] : -1;
+            if (row[i] >= 0) mx = fmaxf(mx, lv[j][i]);
+        }
         mx = group_max<kWave>(mx);
         float sum = 0.0f;
-        for (int e = lane; e < E; e += kWave)
-            if (s_rows[tt * ld + e] >= 0) sum += expf(l[e] - mx);
+#pragma unroll
+        for (int i = 0; i < NE; ++i)
+            if (row[i] >= 0) sum += expf(lv[j][i] - mx);
         sum = group_sum<kWave>(sum);
-        for (int e = lane; e < E; e += kWave) {
-            const int32_t row = s_rows[tt * ld + e];
-            slot_row[(size_t)t * E + e] = row;
-            slot_w[(size_t)t * E + e] = row >= 0 ? expf(l[e] - mx) / sum : 0.0f;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int e = lane + i * kWave;
+            if (e < E) {
+                slot_row[(size_t)t * E + e] = row[i];
+                slot_w[(size_t)t * E + e] = row[i] >= 0 ? expf(lv[j][i] - mx) / sum : 0.0f;
+            }
         }
     }
 }
