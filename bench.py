@@ -238,6 +238,16 @@ def main():
                          "traffic": kernel_traffic("gate_l", "gate_kernel")}}
     del flush_buf, flush_out
 
+    # Practical HBM ceiling: a plain 1 GiB device-to-device copy (torch copy_),
+    # 20 copies back to back, best of 3; bytes = read + write.
+    cp_src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    cp_ms = b2b_time_ms(torch, lambda: cp_dst.copy_(cp_src))
+    hbm_copy = {"what": "torch copy_ of 1 GiB, device to device, 20 back to back, best of 3; read + write bytes",
+                "GB/s": 2 * cp_src.numel() * 4 / (cp_ms * 1e-3) / 1e9}
+    hbm_copy["frac_of_8TBs"] = hbm_copy["GB/s"] / PEAK_HBM_GBS
+    del cp_src, cp_dst
+
     out = {
         "metric": "MoE layer fwd active TFLOPS + gate Gtokens/s on 1 MI355X (vs roofline)",
         "value": round(tflops, 2),
@@ -254,6 +264,7 @@ def main():
         "config": {"workload": "mixtral-shaped MoE layer forward", "T": T, "d": d, "E": E, "K": K, "n": n,
                    "active_flops_per_step": flops, "expert_counts": counts_h.tolist()},
         "gate": gate,
+        "hbm_copy": hbm_copy,
         "steps_us": {
             "router": {"us": rt_ms * 1e3, "us_back_to_back": rt_b2b * 1e3,
                        "frac_hbm_back_to_back": router_bytes / (rt_b2b * 1e-3) / 1e9 / PEAK_HBM_GBS},
