@@ -92,6 +92,11 @@ __global__ __launch_bounds__(256) void tr_keys_kernel(const float* __restrict__ 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kBins = 256;  // radix digit of 8 bits
+// Lanes count into kSub copies of the histogram (lane % kSub), each padded by
+// one word so that the copies of a bin sit in different banks: normal logits
+// put nearly every key's top byte into a few bins, and lanes adding to one
+// LDS word serialise.
+constexpr int kSub = 16, kSubLd = kBins + 1, kHistWords = kSub * kSubLd;
 constexpr int kSelBatch = 16;  // tokens a thread loads at once (kept for every pass when T <= 16384)
 
 // Flags and keys of tokens [b0, b0 + kSelBatch) that lie below t_hi; flag 0xFF
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(kSelThreads) void tr_select_kernel(
     const uint32_t* __restrict__ keyT, const uint8_t* __restrict__ memT, int T, int E, int M, int cap_tiles,
     const int32_t* __restrict__ counts, int32_t* __restrict__ counts_r, int32_t* __restrict__ offsets_r,
     int32_t* __restrict__ row_tok, long long rows_cap, int32_t* __restrict__ slotT) {
-    __shared__ int s_hist[2][kBins];
+    __shared__ int s_hist[2][kHistWords];
     __shared__ int s_scan[kBins];
     __shared__ long long s_ll[kSelWaves];
     __shared__ int s_digit, s_above, s_total;
@@ -204,24 +209,27 @@ __global__ __launch_bounds__(kSelThreads) void tr_select_kernel(
     if (m > 0) {
         uint32_t prefix = 0, hmask = 0;
         need = m;
-        if (tid < kBins) s_hist[0][tid] = 0;
+        for (int q = tid; q < kHistWords; q += kSelThreads) s_hist[0][q] = 0;
         __syncthreads();
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass;
             int* hist = s_hist[pass & 1];
-            if (tid < kBins) s_hist[(pass + 1) & 1][tid] = 0;  // the next pass's bins
+            int* my_hist = hist + (lane & (kSub - 1)) * kSubLd;
+            for (int q = tid; q < kHistWords; q += kSelThreads) s_hist[(pass + 1) & 1][q] = 0;  // next pass
             for (int b0 = t_lo; b0 < t_hi; b0 += kSelBatch) {
                 if (!cached) sel_load(mem, key, b0, t_hi, mm, kk);
 #pragma unroll
                 for (int j = 0; j < kSelBatch; ++j)
                     if (mm[j] == want && (kk[j] & hmask) == prefix)
-                        atomicAdd(&hist[(kk[j] >> shift) & (kBins - 1)], 1);
+                        atomicAdd(&my_hist[(kk[j] >> shift) & (kBins - 1)], 1);
             }
             __syncthreads();
             // above(b) = candidates in bins above b: an inclusive scan from the
             // top bin down, 64 bins per wave, then the totals of the waves before.
+            int v = 0;
             if (tid < kBins) {
-                const int v = hist[kBins - 1 - tid];
+#pragma unroll
+                for (int u = 0; u < kSub; ++u) v += hist[u * kSubLd + kBins - 1 - tid];
                 int x = v;
 #pragma unroll
                 for (int s = 1; s < kWave; s <<= 1) {
@@ -234,7 +242,6 @@ __global__ __launch_bounds__(kSelThreads) void tr_select_kernel(
             if (tid < kBins) {
                 int incl = s_scan[tid];
                 for (int w = 0; w < wave; ++w) incl += s_scan[w * kWave + kWave - 1];
-                const int v = hist[kBins - 1 - tid];
                 const int above = incl - v;
                 if (above < need && need <= incl) {
                     s_digit = kBins - 1 - tid;
