@@ -153,6 +153,18 @@ MOE_DEV long long block_sum_ll(long long v, long long* s_ll) {
     return tot;
 }
 
+// LDS staging of an expert's keys and flags when T <= 16384 (one batch per
+// thread): global memory is read and written in token order across threads
+// (coalesced), and each thread reads its own run of tokens from LDS.  One pad
+// word (keys) or 4 pad bytes (flags) after every 16 tokens spread a thread's
+// run over distinct banks.
+constexpr int kSelStageT = kSelThreads * kSelBatch;
+constexpr int kStageKeyWords = kSelStageT + kSelStageT / 16;
+constexpr int kStageMemBytes = kSelStageT + kSelStageT / 4;
+constexpr size_t kSelLds = (size_t)kStageKeyWords * 4 + kStageMemBytes;
+MOE_DEV int skw(int t) { return t + (t >> 4); }
+MOE_DEV int skb(int t) { return t + ((t >> 4) << 2); }
+
 // One workgroup per expert e.  counts[] is the histogram of topk_idx (as
 // moe_route writes it); rows of e are [o, o + r) with o the sum of the targets
 // of the experts before e.  Writes counts_r[e], offsets_r[e] (and offsets_r[E]
@@ -164,6 +176,7 @@ __global__ __launch_bounds__(kSelThreads) void tr_select_kernel(
     const uint32_t* __restrict__ keyT, const uint8_t* __restrict__ memT, int T, int E, int M, int cap_tiles,
     const int32_t* __restrict__ counts, int32_t* __restrict__ counts_r, int32_t* __restrict__ offsets_r,
     int32_t* __restrict__ row_tok, long long rows_cap, int32_t* __restrict__ slotT) {
+    extern __shared__ __attribute__((aligned(16))) char sel_stage[];  // kSelLds bytes when T <= kSelStageT
     __shared__ int s_hist[2][kHistWords];
     __shared__ int s_scan[kBins];
     __shared__ long long s_ll[kSelWaves];
@@ -176,11 +189,38 @@ __global__ __launch_bounds__(kSelThreads) void tr_select_kernel(
     int32_t* srow = slotT + (size_t)e * T;
     const int c = (T + kSelThreads - 1) / kSelThreads;
     const int t_lo = min(tid * c, T), t_hi = min(t_lo + c, T);
-    // Each thread's tokens, loaded once when they fit one batch (c is uniform).
+    // Each thread's tokens, loaded once when they fit one batch (c is uniform),
+    // through LDS: coalesced global loads, then each thread's run.
     const bool cached = c <= kSelBatch;
+    uint32_t* s_key = reinterpret_cast<uint32_t*>(sel_stage);
+    uint8_t* s_mem = reinterpret_cast<uint8_t*>(sel_stage + (size_t)kStageKeyWords * 4);
     uint8_t mm[kSelBatch];
     uint32_t kk[kSelBatch];
-    if (cached) sel_load(mem, key, t_lo, t_hi, mm, kk);
+    if (cached) {
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+            const int q = j * kSelThreads + tid;
+            const bool v = q < T;
+            kk[j] = v ? key[q] : 0u;
+            mm[j] = v ? mem[q] : (uint8_t)0xFF;
+        }
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+            const int q = j * kSelThreads + tid;
+            if (q < T) {
+                s_key[skw(q)] = kk[j];
+                s_mem[skb(q)] = mm[j];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+            const int t = t_lo + j;
+            const bool v = t < t_hi;
+            kk[j] = v ? s_key[skw(t)] : 0u;
+            mm[j] = v ? s_mem[skb(t)] : (uint8_t)0xFF;
+        }
+    }
 
     long long part = 0;
     for (int q = tid; q < e; q += kSelThreads) part += tr_target_dev(min(max(counts[q], 0), T), M, T, cap_tiles);
@@ -308,7 +348,16 @@ __global__ __launch_bounds__(kSelThreads) void tr_select_kernel(
                 }
                 ++pos;
             }
-            srow[t] = row;
+            if (cached) s_key[skw(t)] = (uint32_t)row;  // every read of s_key was before the scan's barriers
+            else srow[t] = row;
+        }
+    }
+    if (cached) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+            const int q = j * kSelThreads + tid;
+            if (q < T) srow[q] = (int32_t)s_key[skw(q)];
         }
     }
 }
@@ -512,7 +561,13 @@ hipError_t launch_token_round(const float* logits, const int32_t* idx, const int
     uint8_t* memT = reinterpret_cast<uint8_t*>(slotT + (size_t)T * E);
     const dim3 kgrid((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile));
     hipLaunchKernelGGL(tr_keys_kernel, kgrid, dim3(256), 0, s, logits, idx, T, E, K, keyT, memT);
-    hipLaunchKernelGGL(tr_select_kernel, dim3((unsigned)E), dim3(kSelThreads), 0, s, keyT, memT, T, E, M,
+    const size_t sel_lds = T <= kSelStageT ? kSelLds : 0;
+    if (sel_lds != 0) {
+        const hipError_t aerr =
+            hipFuncSetAttribute((const void*)tr_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSelLds);
+        if (aerr != hipSuccess) return aerr;
+    }
+    hipLaunchKernelGGL(tr_select_kernel, dim3((unsigned)E), dim3(kSelThreads), sel_lds, s, keyT, memT, T, E, M,
                        cap_tiles, counts, counts_r, offsets_r, row_tok, rows_cap, slotT);
     const size_t lds = (size_t)kSlotTokens * (E + 1) * sizeof(int32_t);
     hipLaunchKernelGGL(tr_slots_kernel, dim3((unsigned)((T + kSlotTokens - 1) / kSlotTokens)), dim3(256), lds, s,

@@ -121,7 +121,7 @@ def test_forward_tr_matches_oracle(cfg, M, cap):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["mixtral", "dsv3"])
+@pytest.mark.parametrize("name", ["mixtral", "dsv3", "fine"])
 def test_forward_tr_full_size(name):
     cfg = synth.CONFIGS[name]
     print(f"[tr] full {name}: generating inputs", flush=True)
