@@ -45,6 +45,8 @@ PLAN_CASES = [
     ("k_eq_e", 300, 4, 4, 64, 0, 0, 0.0),          # every token routed to every expert
     ("t_below_m", 5, 4, 2, 8, 0, 0, 0.0),          # rounding up past T rounds down
     ("skewed_e64", 70001, 64, 4, 128, 0, 0, 2.0),  # many select blocks, ragged last block
+    ("t_16384", 16384, 16, 2, 256, 0, 5, 1.0),     # largest T whose tokens the select stages in LDS
+    ("t_16385", 16385, 16, 2, 256, 0, 5, 1.0),     # one past it: 17 tokens a thread, read from global memory
     ("mixtral_routing", 8192, 8, 2, 256, 0, 0, 0.0),
     ("dsv3_routing", 8192, 256, 8, 256, 0, 0, 1.5),
 ]
