@@ -262,7 +262,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; X~N(0,1), logits=X@Wr, Wr~N(0,1/d), W1,W3~N(0,1/d), W2~N(0,1/n))",
         "config": {"workload": "mixtral-shaped MoE layer forward", "T": T, "d": d, "E": E, "K": K, "n": n,
-                   "active_flops_per_step": flops, "expert_counts": counts_h.tolist()},
+                   "active_flops_per_step": flops, "expert_counts": counts_h.tolist(),
+                   "load": load_stats(counts_h, A, E)},
         "gate": gate,
         "hbm_copy": hbm_copy,
         "steps_us": {
@@ -351,12 +352,21 @@ def other_workload(name, moe, synth, torch, np, dev, steps=5):
                        + (f" (per-expert bias variance {c.bias_var})" if c.bias_var else ""),
            "ms_per_step": round(ms, 4), "TFLOPS": 6.0 * A * d * n / (ms * 1e-3) / 1e12,
            "roofline_ms": round(roof_s * 1e3, 4), "frac_of_roofline": roof_s * 1e3 / ms,
-           "experts_nonempty": e_act, "max_count": int(counts.max()), "steps_back_to_back": steps,
+           "experts_nonempty": e_act, "max_count": int(counts.max()), "load": load_stats(counts, A, E),
+           "steps_back_to_back": steps,
            "tile_padding": padded / A - 1.0,
            "token_rounding": token_rounding(c, g, plan, moe, torch, np, dev)}
     del g, plan, Yc, Wr, rb, rws
     torch.cuda.empty_cache()
     return res
+
+
+def load_stats(counts, A, E):
+    """Expert load of the routing: smallest and largest count, empty experts,
+    and the variance of the load fractions f_e = count_e / (T*K) around 1/E."""
+    f = [int(x) / A for x in counts]
+    return {"min": int(min(counts)), "max": int(max(counts)), "empty": int(sum(1 for x in counts if int(x) == 0)),
+            "var_f": sum((x - 1.0 / E) ** 2 for x in f) / E}
 
 
 def token_rounding(c, g, plan_topk, moe, torch, np, dev, steps=5, M=256):
