@@ -1,4 +1,4 @@
-"""CPU oracle for the MoE layer forward pass -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the MoE layer forward pass and its backward -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
@@ -60,9 +60,11 @@ def _load():
         lib.oracle_token_round.argtypes = [P, I, I, I, I, I, P, P, P, L, P, P]
         lib.oracle_tr_combine.argtypes = [P, P, P, I, I, I, L, P]
         lib.oracle_tr_layer.argtypes = [P, I, P, P, P, P, P, I, I, I, I, P, I, P]
+        lib.oracle_layer_backward.argtypes = [P, I, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P]
         for f in (lib.oracle_softmax, lib.oracle_route, lib.oracle_permute, lib.oracle_gather_rows,
                   lib.oracle_expert_ffn, lib.oracle_combine, lib.oracle_layer, lib.oracle_expert_down,
-                  lib.oracle_router, lib.oracle_token_round, lib.oracle_tr_combine, lib.oracle_tr_layer):
+                  lib.oracle_router, lib.oracle_token_round, lib.oracle_tr_combine, lib.oracle_tr_layer,
+                  lib.oracle_layer_backward):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -215,6 +217,30 @@ def layer(X, logits, W1, W3, W2, K: int, tokens=None) -> np.ndarray:
     _check(_load().oracle_layer(_ptr(Xs), dt, _ptr(lg), _ptr(W1s), _ptr(W3s), _ptr(W2s), T, d, E, K, n,
                                 tp, ntok, _ptr(out)), "oracle_layer")
     return out
+
+
+def layer_backward(X, logits, W1, W3, W2, K: int, dout):
+    """Gradient of layer() given dout [T, d]: a dict of float32 arrays dX [T, d],
+    dlogits [T, E], dW1, dW3 [E, d, n], dW2 [E, n, d] and dw [T, K] (the
+    gradient of the renormalised routing weights)."""
+    Xs, dt = _storage(X)
+    W1s, d1 = _storage(W1)
+    W3s, d3 = _storage(W3)
+    W2s, d2 = _storage(W2)
+    if not (dt == d1 == d3 == d2):
+        raise ValueError("X and the expert weights must share one storage dtype")
+    lg = _c(logits, np.float32)
+    g = _c(dout, np.float32)
+    T, d = Xs.shape
+    E, _, n = W1s.shape
+    assert g.shape == (T, d) and lg.shape == (T, E)
+    r = {"dX": np.empty((T, d), np.float32), "dlogits": np.empty((T, E), np.float32),
+         "dW1": np.empty((E, d, n), np.float32), "dW3": np.empty((E, d, n), np.float32),
+         "dW2": np.empty((E, n, d), np.float32), "dw": np.empty((T, K), np.float32)}
+    _check(_load().oracle_layer_backward(_ptr(Xs), dt, _ptr(lg), _ptr(W1s), _ptr(W3s), _ptr(W2s), T, d, E, K, n,
+                                         _ptr(g), _ptr(r["dX"]), _ptr(r["dlogits"]), _ptr(r["dW1"]), _ptr(r["dW3"]),
+                                         _ptr(r["dW2"]), _ptr(r["dw"])), "oracle_layer_backward")
+    return r
 
 
 def tr_target(f: int, M: int, T: int, cap_tiles: int = 0) -> int:

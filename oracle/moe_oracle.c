@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the MoE layer forward pass.  TEST INFRASTRUCTURE ONLY.
+ * CPU oracle for the MoE layer forward pass and its backward.  TEST
+ * INFRASTRUCTURE ONLY.
  *
  * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
  * load this library.  The HIP library never links, includes or calls it, and
@@ -33,6 +34,12 @@
  *                  weights sum to 1 with the logit ratios; the combine on
  *                  one-hot and token-index rows; identical experts give the
  *                  dense MLP built from library matmuls
+ *   layer backward - central finite differences of oracle_layer for every
+ *                  element of X, the logits and the three weight tensors; the
+ *                  dS identity against the forward's act and a library matmul;
+ *                  logit gradients sum to zero per token, zero for experts not
+ *                  chosen, zero at K = 1 and for identical experts; exact
+ *                  linearity in dout; exact bf16 widening
  * Every function here is pinned; none is "parity unpinned".
  *
  * Errors: every entry point returns 0 on success and a negative value on a
@@ -482,4 +489,129 @@ int oracle_tr_layer(const void* X, int dtype, const int32_t* slot_row, const flo
         free(h1); free(h3); free(a); free(y); free(acc);
     }
     return bad ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward of the layer: the gradient of oracle_layer's output with respect
+ * to X, the router logits and the expert weights, given dout = dL/d(out).
+ * [P4] section 2.2 names the two products the backward needs beside the
+ * weight gradients, dH (through the SwiGLU) and dS, the gradient of the
+ * routing scores; [P4] section 5 measures the backward pass.  Per token t and
+ * slot k with expert e, weight w_k, and g = dout[t]:
+ *   h1 = x W1[e], h3 = x W3[e], s1 = SiLU(h1), a = s1 * h3, y = a W2[e]
+ *   dw[t,k]  = <g, y>                      (dS; equals <g W2[e]^T, a>, the
+ *                                            form [P4] section 2.2 uses)
+ *   da       = w_k (g W2[e]^T)
+ *   dW2[e]  += w_k a^T g
+ *   dh3      = da * s1,   dh1 = da * h3 * SiLU'(h1),
+ *              SiLU'(z) = sig(z) (1 + z (1 - sig(z))),  sig(z) = 1 / (1 + e^-z)
+ *   dX[t]   += dh1 W1[e]^T + dh3 W3[e]^T
+ *   dW1[e]  += x^T dh1,   dW3[e] += x^T dh3
+ * The weights are the softmax of the K chosen logits renormalised over them,
+ * so for a chosen expert j
+ *   dlogits[t, idx_j] = w_j (dw_j - sum_k w_k dw_k)
+ * and 0 for the others (the top-K choice itself is piecewise constant).
+ * The routing is oracle_route's.  Everything is summed in fp64 in index order
+ * (tokens ascending for the weight gradients) and rounded once to fp32; the
+ * activations are not rounded to fp32 in between, so this is the gradient of
+ * the real-valued function that oracle_layer evaluates.  Sized for small
+ * inputs: it holds fp64 copies of the three weight gradients.
+ * dw may be NULL. */
+int oracle_layer_backward(const void* X, int dtype, const float* logits, const void* W1, const void* W3,
+                          const void* W2, int T, int d, int E, int K, int n, const float* dout, float* dX,
+                          float* dlogits, float* dW1, float* dW3, float* dW2, float* dw) {
+    if (!X || !logits || !W1 || !W3 || !W2 || !dout || !dX || !dlogits || !dW1 || !dW3 || !dW2) return -1;
+    if (T < 0 || d < 1 || E < 1 || K < 1 || K > E || n < 1) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    const size_t wn = (size_t)E * d * n;
+    double* gW1 = (double*)calloc(wn, sizeof(double));
+    double* gW3 = (double*)calloc(wn, sizeof(double));
+    double* gW2 = (double*)calloc(wn, sizeof(double));
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
+    float* w = (float*)malloc(sizeof(float) * (size_t)K);
+    int32_t* cnt = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    int32_t* off = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+    double* h1 = (double*)malloc(sizeof(double) * (size_t)n);
+    double* h3 = (double*)malloc(sizeof(double) * (size_t)n);
+    double* a = (double*)malloc(sizeof(double) * (size_t)n);
+    double* ga = (double*)malloc(sizeof(double) * (size_t)n);
+    double* dh1 = (double*)malloc(sizeof(double) * (size_t)n);
+    double* dh3 = (double*)malloc(sizeof(double) * (size_t)n);
+    double* gx = (double*)malloc(sizeof(double) * (size_t)d);
+    double* dwk = (double*)malloc(sizeof(double) * (size_t)K);
+    int rc = 0;
+    if (!gW1 || !gW3 || !gW2 || !idx || !w || !cnt || !off || !h1 || !h3 || !a || !ga || !dh1 || !dh3 || !gx ||
+        !dwk)
+        rc = -3;
+    for (int t = 0; t < T && rc == 0; ++t) {
+        rc = oracle_route(logits + (size_t)t * E, 1, E, K, idx, w, cnt, off);
+        if (rc) break;
+        const float* g = dout + (size_t)t * d;
+        const size_t xoff = (size_t)t * d;
+        for (int i = 0; i < d; ++i) gx[i] = 0.0;
+        for (int k = 0; k < K; ++k) {
+            const int e = idx[k];
+            const size_t o13 = (size_t)e * d * n, o2 = (size_t)e * n * d;
+            const double wk = (double)w[k];
+            for (int j = 0; j < n; ++j) { h1[j] = 0.0; h3[j] = 0.0; }
+            for (int i = 0; i < d; ++i) {
+                const double xi = load_elem(X, dtype, xoff + i);
+                for (int j = 0; j < n; ++j) {
+                    h1[j] += xi * load_elem(W1, dtype, o13 + (size_t)i * n + j);
+                    h3[j] += xi * load_elem(W3, dtype, o13 + (size_t)i * n + j);
+                }
+            }
+            double dws = 0.0;
+            for (int j = 0; j < n; ++j) {
+                a[j] = h1[j] / (1.0 + exp(-h1[j])) * h3[j];
+                double s = 0.0;
+                for (int c = 0; c < d; ++c) s += (double)g[c] * load_elem(W2, dtype, o2 + (size_t)j * d + c);
+                ga[j] = s;  /* (g W2[e]^T)[j] */
+            }
+            /* dS = <g, y> with y = a W2[e], summed over the output columns */
+            for (int c = 0; c < d; ++c) {
+                double yc = 0.0;
+                for (int j = 0; j < n; ++j) yc += a[j] * load_elem(W2, dtype, o2 + (size_t)j * d + c);
+                dws += (double)g[c] * yc;
+            }
+            dwk[k] = dws;
+            for (int j = 0; j < n; ++j)
+                for (int c = 0; c < d; ++c) gW2[o2 + (size_t)j * d + c] += wk * a[j] * (double)g[c];
+            for (int j = 0; j < n; ++j) {
+                const double sig = 1.0 / (1.0 + exp(-h1[j]));
+                const double s1 = h1[j] * sig;
+                const double da = wk * ga[j];
+                dh3[j] = da * s1;
+                dh1[j] = da * h3[j] * sig * (1.0 + h1[j] * (1.0 - sig));
+            }
+            for (int i = 0; i < d; ++i) {
+                const double xi = load_elem(X, dtype, xoff + i);
+                double s = 0.0;
+                for (int j = 0; j < n; ++j) {
+                    s += dh1[j] * load_elem(W1, dtype, o13 + (size_t)i * n + j) +
+                         dh3[j] * load_elem(W3, dtype, o13 + (size_t)i * n + j);
+                    gW1[o13 + (size_t)i * n + j] += xi * dh1[j];
+                    gW3[o13 + (size_t)i * n + j] += xi * dh3[j];
+                }
+                gx[i] += s;
+            }
+        }
+        for (int i = 0; i < d; ++i) dX[xoff + i] = (float)gx[i];
+        double mean = 0.0;
+        for (int k = 0; k < K; ++k) mean += (double)w[k] * dwk[k];
+        for (int e = 0; e < E; ++e) dlogits[(size_t)t * E + e] = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            dlogits[(size_t)t * E + idx[k]] = (float)((double)w[k] * (dwk[k] - mean));
+            if (dw) dw[(size_t)t * K + k] = (float)dwk[k];
+        }
+    }
+    if (rc == 0)
+        for (size_t q = 0; q < wn; ++q) {
+            dW1[q] = (float)gW1[q];
+            dW3[q] = (float)gW3[q];
+            dW2[q] = (float)gW2[q];
+        }
+    free(gW1); free(gW3); free(gW2); free(idx); free(w); free(cnt); free(off); free(h1); free(h3); free(a);
+    free(ga); free(dh1); free(dh3); free(gx); free(dwk);
+    return rc;
 }
