@@ -293,6 +293,34 @@ int moe_forward_tr(const void* X, const float* logits, const void* W1, const voi
                    int32_t* offsets_r, int32_t* row_tok, int32_t* slot_row, float* slot_w, void* ws,
                    size_t ws_bytes, void* stream);
 
+/*
+ * moe_backward_data -- the data gradients of the layer that moe_forward
+ * computes: dX and the router-logit gradient, given dout = dL/d(out).
+ * [P4] section 2.2 names the backward's dH (through the SwiGLU) and dS (the
+ * routing-score gradient, taken as <dA, A> so that the expert outputs need
+ * not be kept); section 5 measures the backward.  Per assignment (t, k) with
+ * expert e and weight w_k (moe_route's routing of `logits`), g = dout[t]:
+ *   dA = g W2[e]^T, a = SiLU(h1) h3 with h1 = x W1[e], h3 = x W3[e] recomputed,
+ *   dw[t,k] = <dA, a>, dh1 = w_k dA h3 SiLU'(h1), dh3 = w_k dA SiLU(h1),
+ *   dX[t] = sum_k dh1 W1[e]^T + dh3 W3[e]^T,
+ *   dlogits[t, idx_k] = w_k (dw[t,k] - sum_j w_j dw[t,j]), 0 for other experts.
+ * The expert-weight gradients are not computed.
+ * In:  X [T,d], W1/W3 [E,d,n], W2 [E,n,d] and dout [T,d] in dtype; logits
+ *      [T,E] fp32.  Sizes and limits as moe_forward.
+ * Out: dX [T,d] (dtype), dlogits [T,E] fp32, dw [T,K] fp32 (may be NULL).
+ *      bf16 intermediates (h1, h3, dA, dh) are stored rounded to bf16; the
+ *      sums are fp32.
+ * Workspace: moe_backward_data_workspace_bytes(T,d,E,K,n,dtype) bytes, 16-byte
+ *      aligned; it holds the routing, expert-sorted copies of X and dout, the
+ *      intermediates and transposed copies of the weights, all rewritten on
+ *      every call.  The caller owns every buffer.  Errors as moe_forward:
+ *      nothing is launched when an argument is rejected.
+ */
+size_t moe_backward_data_workspace_bytes(int T, int d, int E, int K, int n, int dtype);
+int moe_backward_data(const void* X, const float* logits, const void* W1, const void* W3, const void* W2, int dtype,
+                      int T, int d, int E, int K, int n, const void* dout, void* dX, float* dlogits, float* dw,
+                      void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,8 @@ def load_library() -> ctypes.CDLL:
         "moe_tr_combine": ([P, P, P, I, I, I, I, L, P, P], I),
         "moe_forward_tr_workspace_bytes": ([I, I, I, I, I, I, I], Z),
         "moe_forward_tr": ([P, P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, Z, P], I),
+        "moe_backward_data_workspace_bytes": ([I, I, I, I, I, I], Z),
+        "moe_backward_data": ([P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -367,3 +369,27 @@ def moe_forward_tr(X: torch.Tensor, logits: torch.Tensor, W1: torch.Tensor, W3: 
     plan = ForwardTRPlan(T, d, E, K, n, M, X.dtype, X.device, cap_tiles)
     plan(X, logits, W1, W3, W2)
     return plan.out, plan
+
+
+def moe_backward_data(X: torch.Tensor, logits: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, W2: torch.Tensor,
+                      K: int, dout: torch.Tensor, ws: torch.Tensor | None = None):
+    """Data gradients of the layer: dX [T,d] (dtype of X) and dlogits [T,E] f32 given dout [T,d];
+    also dw [T,K] f32, the gradient of the renormalised routing weights.  Returns a dict."""
+    lib = load_library()
+    T, d = X.shape
+    E, _, n = W1.shape
+    dt = X.dtype
+    dev = X.device
+    nws = lib.moe_backward_data_workspace_bytes(T, d, E, K, n, dtype_code(dt))
+    if nws == 0:
+        raise MoEError(MOE_ERR_UNSUPPORTED, "moe_backward_data_workspace_bytes", lib.moe_last_error().decode())
+    if ws is None:
+        ws = _workspace(nws, dev)
+    r = {"dX": torch.empty((T, d), dtype=dt, device=dev),
+         "dlogits": torch.empty((T, E), dtype=torch.float32, device=dev),
+         "dw": torch.empty((T, K), dtype=torch.float32, device=dev)}
+    _check(lib.moe_backward_data(_dev(X, "X", dt), _dev(logits, "logits", torch.float32), _dev(W1, "W1", dt),
+                                 _dev(W3, "W3", dt), _dev(W2, "W2", dt), dtype_code(dt), T, d, E, K, n,
+                                 _dev(dout, "dout", dt), r["dX"].data_ptr(), r["dlogits"].data_ptr(),
+                                 r["dw"].data_ptr(), _dev(ws, "ws"), ws.numel(), _stream(dev)), "moe_backward_data")
+    return r

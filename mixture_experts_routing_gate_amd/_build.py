@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["router.hip", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "token_round.hip", "moe_api.cpp"]
+SOURCES = ["router.hip", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "token_round.hip", "backward.hip", "moe_api.cpp"]
 HEADERS = ["common.h", "launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,151 @@
+// Backward of the MoE layer, data gradients: dX and the router-logit gradient
+// from dout = dL/d(out).  Page [P4] "MoE architecture optimisation and
+// SonicMoE practice" section 2.2 names the products the backward needs beside
+// the weight gradients: dH through the SwiGLU and dS, the gradient of the
+// routing scores, taken as <dA, A> (the activation gradient before the score
+// scaling against the activation) so that the expert outputs Y need not be
+// kept; section 5 measures the backward.  Per assignment (t, k) with expert e
+// and weight w, row p of the expert-sorted order, g = dout[t]:
+//   dA  = g W2[e]^T                    (grouped GEMM over the rows)
+//   dS  = <dA, SiLU(h1) * h3>          (h1, h3 recomputed by grouped GEMMs)
+//   dh1 = w dA h3 SiLU'(h1),  dh3 = w dA SiLU(h1)
+//   dXp = [dh1 | dh3] [W1[e]^T ; W3[e]^T]   (grouped GEMM, K = 2n)
+//   dX[t] = sum_k dXp[row of (t, k)]   (the combine with unit weights)
+//   dlogits[t, idx_k] = w_k (dS_k - sum_j w_j dS_j), 0 for experts not chosen.
+// The GEMMs are the forward's grouped kernels on transposed weight copies;
+// this file holds the kernels that are new: the weight transpose, the SwiGLU
+// backward with dS, the logit gradient and a fill.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTr = 32;  // transpose tile
+
+// out[e*oes + c*ors + r] = in[e][r][c] for in [E][R][C]; one 32 x 32 tile per
+// workgroup (256 threads), through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_experts_kernel(const T* __restrict__ in, int R, int C,
+                                                                T* __restrict__ out, size_t oes, size_t ors) {
+    __shared__ T tile[kTr][kTr + 1];
+    const int tx = threadIdx.x & (kTr - 1), ty = threadIdx.x / kTr;  // ty in 0..7
+    const int c0 = blockIdx.x * kTr, r0 = blockIdx.y * kTr;
+    const size_t e = blockIdx.z;
+    const T* src = in + e * (size_t)R * C;
+#pragma unroll
+    for (int i = 0; i < kTr / 8; ++i) {
+        const int r = r0 + ty + 8 * i, c = c0 + tx;
+        if (r < R && c < C) tile[ty + 8 * i][tx] = src[(size_t)r * C + c];
+    }
+    __syncthreads();
+    T* dst = out + e * oes;
+#pragma unroll
+    for (int i = 0; i < kTr / 8; ++i) {
+        const int c = c0 + ty + 8 * i, r = r0 + tx;
+        if (r < R && c < C) dst[(size_t)c * ors + r] = tile[tx][ty + 8 * i];
+    }
+}
+
+MOE_DEV float load_el(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+MOE_DEV float load_el(const float* p, size_t i) { return p[i]; }
+MOE_DEV void store_el(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+MOE_DEV void store_el(float* p, size_t i, float v) { p[i] = v; }
+
+// One wave per expert-sorted row p: recomputes a = SiLU(h1) h3 from the
+// stored H1, H3 rows, forms dS = <dA, a> (fp32, lane-ordered partial sums,
+// then a butterfly: deterministic) and writes dH = [dh1 | dh3] ([rows, 2n]).
+// dS goes to dS_tk[sorted_pair[p]] (the (token, slot) order of topk_w).
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ H1, const T* __restrict__ H3,
+                                                         const T* __restrict__ dA, const float* __restrict__ topk_w,
+                                                         const int32_t* __restrict__ sorted_pair, int rows, int n,
+                                                         T* __restrict__ dH, float* __restrict__ dS_tk) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int p = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (p >= rows) return;
+    const int tk = sorted_pair[p];
+    const float w = topk_w[tk];
+    const size_t rb = (size_t)p * n;
+    float ds = 0.0f;
+    for (int j = lane; j < n; j += kWave) {
+        const float h1 = load_el(H1, rb + j), h3 = load_el(H3, rb + j), g = load_el(dA, rb + j);
+        const float sig = 1.0f / (1.0f + expf(-h1));
+        const float s1 = h1 * sig;
+        ds = fmaf(g, s1 * h3, ds);
+        const float wg = w * g;
+        store_el(dH, 2 * rb + j, wg * h3 * sig * (1.0f + h1 * (1.0f - sig)));
+        store_el(dH, 2 * rb + n + j, wg * s1);
+    }
+    ds = group_sum<kWave>(ds);
+    if (lane == 0) dS_tk[tk] = ds;
+}
+
+// dlogits[t, e] = w_k (dS_k - sum_j w_j dS_j) when e = idx[t, k], else 0;
+// one thread per (t, e).
+__global__ __launch_bounds__(256) void logit_grad_kernel(const int32_t* __restrict__ idx,
+                                                         const float* __restrict__ topk_w,
+                                                         const float* __restrict__ dS_tk, int T, int E, int K,
+                                                         float* __restrict__ dlogits) {
+    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (size_t)T * E) return;
+    const size_t t = q / E;
+    const int e = (int)(q % E);
+    float mean = 0.0f;
+    for (int k = 0; k < K; ++k) mean = fmaf(topk_w[t * K + k], dS_tk[t * K + k], mean);
+    float g = 0.0f;
+    for (int k = 0; k < K; ++k)
+        if (idx[t * K + k] == e) g = topk_w[t * K + k] * (dS_tk[t * K + k] - mean);
+    dlogits[q] = g;
+}
+
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ p, size_t n, float v) {
+    for (size_t q = (size_t)blockIdx.x * 256 + threadIdx.x; q < n; q += (size_t)gridDim.x * 256) p[q] = v;
+}
+
+}  // namespace
+
+hipError_t launch_transpose_experts(const void* in, int dtype, int E, int R, int C, void* out, size_t oes,
+                                    size_t ors, hipStream_t s) {
+    const dim3 grid((unsigned)((C + kTr - 1) / kTr), (unsigned)((R + kTr - 1) / kTr), (unsigned)E);
+    if (dtype == 1)
+        hipLaunchKernelGGL(transpose_experts_kernel<uint16_t>, grid, dim3(256), 0, s,
+                           static_cast<const uint16_t*>(in), R, C, static_cast<uint16_t*>(out), oes, ors);
+    else
+        hipLaunchKernelGGL(transpose_experts_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(in),
+                           R, C, static_cast<float*>(out), oes, ors);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const void* H1, const void* H3, const void* dA, const float* topk_w,
+                             const int32_t* sorted_pair, int dtype, int rows, int n, void* dH, float* dS_tk,
+                             hipStream_t s) {
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (rows <= 0) return hipSuccess;
+    if (dtype == 1)
+        hipLaunchKernelGGL(swiglu_bwd_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(H1),
+                           static_cast<const uint16_t*>(H3), static_cast<const uint16_t*>(dA), topk_w, sorted_pair,
+                           rows, n, static_cast<uint16_t*>(dH), dS_tk);
+    else
+        hipLaunchKernelGGL(swiglu_bwd_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(H1),
+                           static_cast<const float*>(H3), static_cast<const float*>(dA), topk_w, sorted_pair, rows,
+                           n, static_cast<float*>(dH), dS_tk);
+    return hipGetLastError();
+}
+
+hipError_t launch_logit_grad(const int32_t* idx, const float* topk_w, const float* dS_tk, int T, int E, int K,
+                             float* dlogits, hipStream_t s) {
+    const size_t n = (size_t)T * E;
+    hipLaunchKernelGGL(logit_grad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, topk_w, dS_tk, T,
+                       E, K, dlogits);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s) {
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+}  // namespace moe

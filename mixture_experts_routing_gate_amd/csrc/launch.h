@@ -88,4 +88,16 @@ hipError_t launch_tr_combine(const void* Y, const int32_t* slot_row, const float
 hipError_t launch_tr_gather_rows(const void* X, size_t row_bytes, int T, const int32_t* row_tok,
                                  const int32_t* offsets_r, int E, long long rows_cap, void* Xp, hipStream_t s);
 
+// Backward, data gradients.  out[e*oes + c*ors + r] = in[e][r][c] for in
+// [E][R][C] (dtype 0 fp32, 1 bf16); the SwiGLU backward with dS over
+// expert-sorted rows; the router-logit gradient; a float fill.
+hipError_t launch_transpose_experts(const void* in, int dtype, int E, int R, int C, void* out, size_t oes,
+                                    size_t ors, hipStream_t s);
+hipError_t launch_swiglu_bwd(const void* H1, const void* H3, const void* dA, const float* topk_w,
+                             const int32_t* sorted_pair, int dtype, int rows, int n, void* dH, float* dS_tk,
+                             hipStream_t s);
+hipError_t launch_logit_grad(const int32_t* idx, const float* topk_w, const float* dS_tk, int T, int E, int K,
+                             float* dlogits, hipStream_t s);
+hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s);
+
 }  // namespace moe

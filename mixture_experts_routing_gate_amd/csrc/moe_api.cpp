@@ -1,5 +1,5 @@
 // C ABI of libmoe: argument validation, workspace carving and kernel
-// orchestration for the MoE layer forward.  The entry points are declared
+// orchestration for the MoE layer forward and its data-gradient backward.  The entry points are declared
 // (with their semantics and the passages they follow) in include/moe.h.
 #include "../../include/moe.h"
 
@@ -119,6 +119,23 @@ size_t forward_ws(int T, int d, int E, int K, int n, int dtype) {
     b += align_up(A * 4) * 2;                          // sorted_pair, inv
     b += align_up(A * d * s) * 2 + align_up(A * n * s);  // Xp, Y, Act
     b += align_up(ffn_split_bytes(dtype, d, n));        // split tail of the grouped GEMMs
+    return b;
+}
+
+// Workspace of moe_backward_data, in carving order.
+size_t backward_ws(int T, int d, int E, int K, int n, int dtype) {
+    const size_t A = (size_t)T * K;
+    const size_t s = elem_bytes(dtype);
+    size_t b = 0;
+    b += 2 * align_up((size_t)num_chunks(T) * E * 4);       // blk, blkbase
+    b += align_up(A * 4) * 2;                               // topk_idx, topk_w
+    b += align_up(E * 4) + align_up((E + 1) * 4);           // counts, offsets
+    b += align_up(A * 4) * 2;                               // sorted_pair, inv
+    b += align_up(A * 4) * 2;                               // dS, unit weights
+    b += align_up(A * d * s) * 2;                           // Xp (then dXp), dout rows
+    b += align_up(A * n * s) * 3 + align_up(A * 2 * n * s);  // H1, H3, dA, dH
+    b += align_up((size_t)E * d * n * s) * 3;               // W2^T, [W1^T ; W3^T]
+    b += align_up(ffn_split_bytes(dtype, 256, 128));        // split tail of the grouped GEMMs
     return b;
 }
 
@@ -593,6 +610,93 @@ int moe_forward_tr(const void* X, const float* logits, const void* W1, const voi
         HIPCHECK(launch_ffn(Xp, W1, W3, W2, dtype, (int)R, d, E, n, counts_r, offsets_r, Act, Yb, part, true, s));
     }
     HIPCHECK(launch_tr_combine(Yb, slot_row, slot_w, dtype, T, E, d, R, out, s));
+    return MOE_OK;
+}
+
+size_t moe_backward_data_workspace_bytes(int T, int d, int E, int K, int n, int dtype) {
+    if (check_tek(T, E, K) != MOE_OK || check_dtype(dtype) != MOE_OK || check_dim("d", d, dtype) != MOE_OK ||
+        check_dim("n", n, dtype) != MOE_OK)
+        return 0;
+    return backward_ws(T, d, E, K, n, dtype);
+}
+
+int moe_backward_data(const void* X, const float* logits, const void* W1, const void* W3, const void* W2, int dtype,
+                      int T, int d, int E, int K, int n, const void* dout, void* dX, float* dlogits, float* dw,
+                      void* ws, size_t ws_bytes, void* stream) {
+    CHECK(check_tek(T, E, K));
+    CHECK(check_dtype(dtype));
+    CHECK(check_dim("d", d, dtype));
+    CHECK(check_dim("n", n, dtype));
+    NONNULL(X);
+    NONNULL(logits);
+    NONNULL(W1);
+    NONNULL(W3);
+    NONNULL(W2);
+    NONNULL(dout);
+    NONNULL(dX);
+    NONNULL(dlogits);
+    if (dw != nullptr && !aligned16(dw)) return fail(MOE_ERR_INVALID_ARG, "dw must be 16-byte aligned");
+    if ((long long)T * K * 2LL * (long long)(d > n ? d : n) >= (1LL << 40))
+        return fail(MOE_ERR_UNSUPPORTED, "T*K*2*max(d,n) must be < 2^40");
+    const size_t need = backward_ws(T, d, E, K, n, dtype);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "moe_backward_data needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t A = (size_t)T * K;
+    const size_t sz = elem_bytes(dtype);
+    const int B = num_chunks(T);
+    Carver c(ws);
+    int32_t* blk = c.take<int32_t>((size_t)B * E);
+    int32_t* blkbase = c.take<int32_t>((size_t)B * E);
+    int32_t* idx = c.take<int32_t>(A);
+    float* w = c.take<float>(A);
+    int32_t* counts = c.take<int32_t>(E);
+    int32_t* offsets = c.take<int32_t>(E + 1);
+    int32_t* sorted_pair = c.take<int32_t>(A);
+    int32_t* inv = c.take<int32_t>(A);
+    float* ws_ds = c.take<float>(A);
+    float* ones = c.take<float>(A);
+    void* Xp = c.take<char>(A * d * sz);  // later dXp
+    void* dY = c.take<char>(A * d * sz);
+    void* H1 = c.take<char>(A * n * sz);
+    void* H3 = c.take<char>(A * n * sz);
+    void* dA = c.take<char>(A * n * sz);
+    void* dH = c.take<char>(A * 2 * n * sz);
+    void* W2t = c.take<char>((size_t)E * d * n * sz);
+    void* W13t = c.take<char>((size_t)E * 2 * d * n * sz);
+    const size_t split_bytes = ffn_split_bytes(dtype, 256, 128);
+    float* part = split_bytes ? c.take<float>(split_bytes / sizeof(float)) : nullptr;
+    float* dS = dw != nullptr ? dw : ws_ds;
+
+    // routing, as in moe_forward
+    HIPCHECK(launch_gate(logits, T, E, K, idx, w, blk, s));
+    if (scan_rank_fused(T, E)) {
+        HIPCHECK(launch_scan_rank(idx, T, E, K, blk, counts, offsets, sorted_pair, inv, nullptr, 0, s));
+    } else {
+        HIPCHECK(launch_scan(blk, B, E, counts, offsets, blkbase, s));
+        HIPCHECK(launch_rank(idx, T, E, K, blkbase, sorted_pair, inv, s));
+    }
+    // expert-sorted rows of X and of dout
+    HIPCHECK(launch_copy_rows(X, (size_t)d * sz, T, K, inv, Xp, s));
+    HIPCHECK(launch_copy_rows(dout, (size_t)d * sz, T, K, inv, dY, s));
+    // transposed weights: W2^T [E, d, n]; [W1^T ; W3^T] [E, 2n, d]
+    HIPCHECK(launch_transpose_experts(W2, dtype, E, n, d, W2t, (size_t)d * n, (size_t)n, s));
+    HIPCHECK(launch_transpose_experts(W1, dtype, E, d, n, W13t, (size_t)2 * n * d, (size_t)d, s));
+    HIPCHECK(launch_transpose_experts(W3, dtype, E, d, n, static_cast<char*>(W13t) + (size_t)n * d * sz,
+                                      (size_t)2 * n * d, (size_t)d, s));
+    // pre-activations H1 = Xp W1, H3 = Xp W3; dA = dY W2^T (grouped, per expert)
+    HIPCHECK(launch_ffn_down(Xp, W1, dtype, (int)A, n, E, d, counts, offsets, H1, part, false, s));
+    HIPCHECK(launch_ffn_down(Xp, W3, dtype, (int)A, n, E, d, counts, offsets, H3, part, false, s));
+    HIPCHECK(launch_ffn_down(dY, W2t, dtype, (int)A, n, E, d, counts, offsets, dA, part, false, s));
+    // SwiGLU backward and dS; then dXp = [dh1 | dh3] [W1^T ; W3^T]
+    HIPCHECK(launch_swiglu_bwd(H1, H3, dA, w, sorted_pair, dtype, (int)A, n, dH, dS, s));
+    HIPCHECK(launch_ffn_down(dH, W13t, dtype, (int)A, d, E, 2 * n, counts, offsets, Xp, part, false, s));
+    // dX[t] = sum over the token's rows, unit weights; logit gradient from dS
+    HIPCHECK(launch_fill_f32(ones, A, 1.0f, s));
+    HIPCHECK(launch_combine(Xp, ones, inv, dtype, T, d, K, dX, s));
+    HIPCHECK(launch_logit_grad(idx, w, dS, T, E, K, dlogits, s));
     return MOE_OK;
 }
 
