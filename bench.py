@@ -14,6 +14,8 @@ n=14336, bf16, fp32 accumulation), inputs resident in HBM.  Prints ONE JSON line
   token_rounding = the layer with Token Rounding at tile height 256 beside
                 plain top-K on the same inputs (mixtral here; the other shapes
                 under other_workloads), with its plan and combine back to back
+  backward_data = moe_backward_data (dX and the router-logit gradient) on the
+                same layer, per call, with the rate of its grouped GEMMs
   cpu_baseline= the CPU oracle (per-token loop, fp64 accumulation) on a bounded
                 sample of the same layer, on this host's cores
 Inputs are seeded synthetic tensors (see synth/); nothing is read from disk
@@ -291,6 +293,7 @@ def main():
 
     if not args.no_other_workloads:
         out["token_rounding"] = {"mixtral": token_rounding(cfg, g, plan, moe, torch, np, dev)}
+        out["backward_data"] = backward_data(cfg, g, moe, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, g, args.cpu_seconds, np, torch, synth)
     if not args.no_other_workloads:
@@ -357,6 +360,29 @@ def other_workload(name, moe, synth, torch, np, dev, steps=5):
            "tile_padding": padded / A - 1.0,
            "token_rounding": token_rounding(c, g, plan, moe, torch, np, dev)}
     del g, plan, Yc, Wr, rb, rws
+    torch.cuda.empty_cache()
+    return res
+
+
+def backward_data(c, g, moe, torch, dev, calls=3):
+    """moe_backward_data on the same layer (dX and the router-logit gradient for a
+    seeded dout): time per call, 3 calls back to back after one warm-up, and the
+    rate of its grouped GEMMs, 10*d*n FLOPs per assignment (H1 and H3 recomputed,
+    dA = dY W2^T, dXp = [dh1 | dh3] [W1^T ; W3^T])."""
+    lib = moe.load_library()
+    ws = torch.empty(lib.moe_backward_data_workspace_bytes(c.T, c.d, c.E, c.K, c.n, 1), dtype=torch.uint8,
+                     device=dev)
+    gen = torch.Generator(device="cpu").manual_seed(12)
+    dout = torch.randn((c.T, c.d), generator=gen).to(c.torch_dtype).to(dev)
+
+    def run():
+        moe.moe_backward_data(g["X"], g["logits"], g["W1"], g["W3"], g["W2"], c.K, dout, ws=ws)
+
+    ms = b2b_time_ms(torch, run, n=calls, reps=1)
+    flops = 10.0 * c.T * c.K * c.d * c.n
+    res = {"what": "dX, dlogits and dw (no weight gradients)", "ms_per_call": round(ms, 4),
+           "TFLOPS": flops / (ms * 1e-3) / 1e12, "flops_per_call": flops}
+    del ws, dout
     torch.cuda.empty_cache()
     return res
 

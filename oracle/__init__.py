@@ -61,10 +61,11 @@ def _load():
         lib.oracle_tr_combine.argtypes = [P, P, P, I, I, I, L, P]
         lib.oracle_tr_layer.argtypes = [P, I, P, P, P, P, P, I, I, I, I, P, I, P]
         lib.oracle_layer_backward.argtypes = [P, I, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P]
+        lib.oracle_layer_backward_rows.argtypes = [P, I, P, P, P, P, I, I, I, I, I, P, P, I, P, P, P]
         for f in (lib.oracle_softmax, lib.oracle_route, lib.oracle_permute, lib.oracle_gather_rows,
                   lib.oracle_expert_ffn, lib.oracle_combine, lib.oracle_layer, lib.oracle_expert_down,
                   lib.oracle_router, lib.oracle_token_round, lib.oracle_tr_combine, lib.oracle_tr_layer,
-                  lib.oracle_layer_backward):
+                  lib.oracle_layer_backward, lib.oracle_layer_backward_rows):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -240,6 +241,29 @@ def layer_backward(X, logits, W1, W3, W2, K: int, dout):
     _check(_load().oracle_layer_backward(_ptr(Xs), dt, _ptr(lg), _ptr(W1s), _ptr(W3s), _ptr(W2s), T, d, E, K, n,
                                          _ptr(g), _ptr(r["dX"]), _ptr(r["dlogits"]), _ptr(r["dW1"]), _ptr(r["dW3"]),
                                          _ptr(r["dW2"]), _ptr(r["dw"])), "oracle_layer_backward")
+    return r
+
+
+def layer_backward_rows(X, logits, W1, W3, W2, K: int, dout, tokens):
+    """layer_backward() for the listed tokens only, without weight gradients:
+    a dict of dX [ntok, d], dlogits [ntok, E] and dw [ntok, K] (float32)."""
+    Xs, dt = _storage(X)
+    W1s, d1 = _storage(W1)
+    W3s, d3 = _storage(W3)
+    W2s, d2 = _storage(W2)
+    if not (dt == d1 == d3 == d2):
+        raise ValueError("X and the expert weights must share one storage dtype")
+    lg = _c(logits, np.float32)
+    g = _c(dout, np.float32)
+    tk = _c(tokens, np.int32)
+    T, d = Xs.shape
+    E, _, n = W1s.shape
+    m = tk.size
+    r = {"dX": np.empty((m, d), np.float32), "dlogits": np.empty((m, E), np.float32),
+         "dw": np.empty((m, K), np.float32)}
+    _check(_load().oracle_layer_backward_rows(_ptr(Xs), dt, _ptr(lg), _ptr(W1s), _ptr(W3s), _ptr(W2s), T, d, E, K,
+                                              n, _ptr(g), _ptr(tk), m, _ptr(r["dX"]), _ptr(r["dlogits"]),
+                                              _ptr(r["dw"])), "oracle_layer_backward_rows")
     return r
 
 

@@ -517,6 +517,79 @@ int oracle_tr_layer(const void* X, int dtype, const int32_t* slot_row, const flo
  * the real-valued function that oracle_layer evaluates.  Sized for small
  * inputs: it holds fp64 copies of the three weight gradients.
  * dw may be NULL. */
+/* One token of the backward: its routing, dX row (gx, d doubles), its K
+ * routing-weight gradients (dwk) and, when gW1 is not NULL, its contribution
+ * to the three weight gradients (fp64 accumulators).  Scratch: h1, h3, a, ga,
+ * dh1, dh3 of n doubles.  Returns oracle_route's status. */
+static int bwd_token(const void* X, int dtype, const float* logits, const void* W1, const void* W3, const void* W2,
+                     int t, int d, int E, int K, int n, const float* g, int32_t* idx, float* w, int32_t* cnt,
+                     int32_t* off, double* h1, double* h3, double* a, double* ga, double* dh1, double* dh3,
+                     double* gx, double* dwk, double* gW1, double* gW3, double* gW2) {
+    const int rc = oracle_route(logits + (size_t)t * E, 1, E, K, idx, w, cnt, off);
+    if (rc) return rc;
+    const size_t xoff = (size_t)t * d;
+    for (int i = 0; i < d; ++i) gx[i] = 0.0;
+    for (int k = 0; k < K; ++k) {
+        const int e = idx[k];
+        const size_t o13 = (size_t)e * d * n, o2 = (size_t)e * n * d;
+        const double wk = (double)w[k];
+        for (int j = 0; j < n; ++j) { h1[j] = 0.0; h3[j] = 0.0; }
+        for (int i = 0; i < d; ++i) {
+            const double xi = load_elem(X, dtype, xoff + i);
+            for (int j = 0; j < n; ++j) {
+                h1[j] += xi * load_elem(W1, dtype, o13 + (size_t)i * n + j);
+                h3[j] += xi * load_elem(W3, dtype, o13 + (size_t)i * n + j);
+            }
+        }
+        double dws = 0.0;
+        for (int j = 0; j < n; ++j) {
+            a[j] = h1[j] / (1.0 + exp(-h1[j])) * h3[j];
+            double sacc = 0.0;
+            for (int c = 0; c < d; ++c) sacc += (double)g[c] * load_elem(W2, dtype, o2 + (size_t)j * d + c);
+            ga[j] = sacc;  /* (g W2[e]^T)[j] */
+        }
+        /* dS = <g, y> with y = a W2[e], summed over the output columns */
+        for (int c = 0; c < d; ++c) {
+            double yc = 0.0;
+            for (int j = 0; j < n; ++j) yc += a[j] * load_elem(W2, dtype, o2 + (size_t)j * d + c);
+            dws += (double)g[c] * yc;
+        }
+        dwk[k] = dws;
+        if (gW2)
+            for (int j = 0; j < n; ++j)
+                for (int c = 0; c < d; ++c) gW2[o2 + (size_t)j * d + c] += wk * a[j] * (double)g[c];
+        for (int j = 0; j < n; ++j) {
+            const double sig = 1.0 / (1.0 + exp(-h1[j]));
+            const double s1 = h1[j] * sig;
+            const double da = wk * ga[j];
+            dh3[j] = da * s1;
+            dh1[j] = da * h3[j] * sig * (1.0 + h1[j] * (1.0 - sig));
+        }
+        for (int i = 0; i < d; ++i) {
+            const double xi = load_elem(X, dtype, xoff + i);
+            double sacc = 0.0;
+            for (int j = 0; j < n; ++j) {
+                sacc += dh1[j] * load_elem(W1, dtype, o13 + (size_t)i * n + j) +
+                        dh3[j] * load_elem(W3, dtype, o13 + (size_t)i * n + j);
+                if (gW1) {
+                    gW1[o13 + (size_t)i * n + j] += xi * dh1[j];
+                    gW3[o13 + (size_t)i * n + j] += xi * dh3[j];
+                }
+            }
+            gx[i] += sacc;
+        }
+    }
+    return 0;
+}
+
+/* The logit gradient of one token from its weights and weight gradients. */
+static void bwd_logits(const int32_t* idx, const float* w, const double* dwk, int E, int K, float* dl) {
+    double mean = 0.0;
+    for (int k = 0; k < K; ++k) mean += (double)w[k] * dwk[k];
+    for (int e = 0; e < E; ++e) dl[e] = 0.0f;
+    for (int k = 0; k < K; ++k) dl[idx[k]] = (float)((double)w[k] * (dwk[k] - mean));
+}
+
 int oracle_layer_backward(const void* X, int dtype, const float* logits, const void* W1, const void* W3,
                           const void* W2, int T, int d, int E, int K, int n, const float* dout, float* dX,
                           float* dlogits, float* dW1, float* dW3, float* dW2, float* dw) {
@@ -531,79 +604,20 @@ int oracle_layer_backward(const void* X, int dtype, const float* logits, const v
     float* w = (float*)malloc(sizeof(float) * (size_t)K);
     int32_t* cnt = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
     int32_t* off = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
-    double* h1 = (double*)malloc(sizeof(double) * (size_t)n);
-    double* h3 = (double*)malloc(sizeof(double) * (size_t)n);
-    double* a = (double*)malloc(sizeof(double) * (size_t)n);
-    double* ga = (double*)malloc(sizeof(double) * (size_t)n);
-    double* dh1 = (double*)malloc(sizeof(double) * (size_t)n);
-    double* dh3 = (double*)malloc(sizeof(double) * (size_t)n);
-    double* gx = (double*)malloc(sizeof(double) * (size_t)d);
-    double* dwk = (double*)malloc(sizeof(double) * (size_t)K);
+    double* scr = (double*)malloc(sizeof(double) * (size_t)(6 * n + d + K));
     int rc = 0;
-    if (!gW1 || !gW3 || !gW2 || !idx || !w || !cnt || !off || !h1 || !h3 || !a || !ga || !dh1 || !dh3 || !gx ||
-        !dwk)
-        rc = -3;
+    if (!gW1 || !gW3 || !gW2 || !idx || !w || !cnt || !off || !scr) rc = -3;
     for (int t = 0; t < T && rc == 0; ++t) {
-        rc = oracle_route(logits + (size_t)t * E, 1, E, K, idx, w, cnt, off);
+        double* gx = scr + 6 * (size_t)n;
+        double* dwk = gx + d;
+        rc = bwd_token(X, dtype, logits, W1, W3, W2, t, d, E, K, n, dout + (size_t)t * d, idx, w, cnt, off, scr,
+                       scr + n, scr + 2 * (size_t)n, scr + 3 * (size_t)n, scr + 4 * (size_t)n, scr + 5 * (size_t)n,
+                       gx, dwk, gW1, gW3, gW2);
         if (rc) break;
-        const float* g = dout + (size_t)t * d;
-        const size_t xoff = (size_t)t * d;
-        for (int i = 0; i < d; ++i) gx[i] = 0.0;
-        for (int k = 0; k < K; ++k) {
-            const int e = idx[k];
-            const size_t o13 = (size_t)e * d * n, o2 = (size_t)e * n * d;
-            const double wk = (double)w[k];
-            for (int j = 0; j < n; ++j) { h1[j] = 0.0; h3[j] = 0.0; }
-            for (int i = 0; i < d; ++i) {
-                const double xi = load_elem(X, dtype, xoff + i);
-                for (int j = 0; j < n; ++j) {
-                    h1[j] += xi * load_elem(W1, dtype, o13 + (size_t)i * n + j);
-                    h3[j] += xi * load_elem(W3, dtype, o13 + (size_t)i * n + j);
-                }
-            }
-            double dws = 0.0;
-            for (int j = 0; j < n; ++j) {
-                a[j] = h1[j] / (1.0 + exp(-h1[j])) * h3[j];
-                double s = 0.0;
-                for (int c = 0; c < d; ++c) s += (double)g[c] * load_elem(W2, dtype, o2 + (size_t)j * d + c);
-                ga[j] = s;  /* (g W2[e]^T)[j] */
-            }
-            /* dS = <g, y> with y = a W2[e], summed over the output columns */
-            for (int c = 0; c < d; ++c) {
-                double yc = 0.0;
-                for (int j = 0; j < n; ++j) yc += a[j] * load_elem(W2, dtype, o2 + (size_t)j * d + c);
-                dws += (double)g[c] * yc;
-            }
-            dwk[k] = dws;
-            for (int j = 0; j < n; ++j)
-                for (int c = 0; c < d; ++c) gW2[o2 + (size_t)j * d + c] += wk * a[j] * (double)g[c];
-            for (int j = 0; j < n; ++j) {
-                const double sig = 1.0 / (1.0 + exp(-h1[j]));
-                const double s1 = h1[j] * sig;
-                const double da = wk * ga[j];
-                dh3[j] = da * s1;
-                dh1[j] = da * h3[j] * sig * (1.0 + h1[j] * (1.0 - sig));
-            }
-            for (int i = 0; i < d; ++i) {
-                const double xi = load_elem(X, dtype, xoff + i);
-                double s = 0.0;
-                for (int j = 0; j < n; ++j) {
-                    s += dh1[j] * load_elem(W1, dtype, o13 + (size_t)i * n + j) +
-                         dh3[j] * load_elem(W3, dtype, o13 + (size_t)i * n + j);
-                    gW1[o13 + (size_t)i * n + j] += xi * dh1[j];
-                    gW3[o13 + (size_t)i * n + j] += xi * dh3[j];
-                }
-                gx[i] += s;
-            }
-        }
-        for (int i = 0; i < d; ++i) dX[xoff + i] = (float)gx[i];
-        double mean = 0.0;
-        for (int k = 0; k < K; ++k) mean += (double)w[k] * dwk[k];
-        for (int e = 0; e < E; ++e) dlogits[(size_t)t * E + e] = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            dlogits[(size_t)t * E + idx[k]] = (float)((double)w[k] * (dwk[k] - mean));
-            if (dw) dw[(size_t)t * K + k] = (float)dwk[k];
-        }
+        for (int i = 0; i < d; ++i) dX[(size_t)t * d + i] = (float)gx[i];
+        bwd_logits(idx, w, dwk, E, K, dlogits + (size_t)t * E);
+        if (dw)
+            for (int k = 0; k < K; ++k) dw[(size_t)t * K + k] = (float)dwk[k];
     }
     if (rc == 0)
         for (size_t q = 0; q < wn; ++q) {
@@ -611,7 +625,41 @@ int oracle_layer_backward(const void* X, int dtype, const float* logits, const v
             dW3[q] = (float)gW3[q];
             dW2[q] = (float)gW2[q];
         }
-    free(gW1); free(gW3); free(gW2); free(idx); free(w); free(cnt); free(off); free(h1); free(h3); free(a);
-    free(ga); free(dh1); free(dh3); free(gx); free(dwk);
+    free(gW1); free(gW3); free(gW2); free(idx); free(w); free(cnt); free(off); free(scr);
     return rc;
+}
+
+/* The same backward for a subset of tokens, without the weight gradients:
+ * rows s of dX [ntok, d], dlogits [ntok, E] and dw [ntok, K] belong to token
+ * tokens[s]; dout is the full [T, d].  For sampled checks of large layers. */
+int oracle_layer_backward_rows(const void* X, int dtype, const float* logits, const void* W1, const void* W3,
+                               const void* W2, int T, int d, int E, int K, int n, const float* dout,
+                               const int32_t* tokens, int ntok, float* dX, float* dlogits, float* dw) {
+    if (!X || !logits || !W1 || !W3 || !W2 || !dout || !tokens || !dX || !dlogits || !dw) return -1;
+    if (T < 0 || d < 1 || E < 1 || K < 1 || K > E || n < 1 || ntok < 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int s = 0; s < ntok; ++s) {
+        const int t = tokens[s];
+        if (t < 0 || t >= T) { bad |= 1; continue; }
+        int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
+        float* w = (float*)malloc(sizeof(float) * (size_t)K);
+        int32_t* cnt = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+        int32_t* off = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+        double* scr = (double*)malloc(sizeof(double) * (size_t)(6 * n + d + K));
+        double* gx = scr + 6 * (size_t)n;
+        double* dwk = gx + d;
+        if (bwd_token(X, dtype, logits, W1, W3, W2, t, d, E, K, n, dout + (size_t)t * d, idx, w, cnt, off, scr,
+                      scr + n, scr + 2 * (size_t)n, scr + 3 * (size_t)n, scr + 4 * (size_t)n, scr + 5 * (size_t)n,
+                      gx, dwk, NULL, NULL, NULL) != 0)
+            bad |= 1;
+        else {
+            for (int i = 0; i < d; ++i) dX[(size_t)s * d + i] = (float)gx[i];
+            bwd_logits(idx, w, dwk, E, K, dlogits + (size_t)s * E);
+            for (int k = 0; k < K; ++k) dw[(size_t)s * K + k] = (float)dwk[k];
+        }
+        free(idx); free(w); free(cnt); free(off); free(scr);
+    }
+    return bad ? -1 : 0;
 }

@@ -69,3 +69,26 @@ def test_backward_data_is_deterministic():
     for k in a:
         assert torch.equal(a[k].view(torch.int16) if a[k].dtype == torch.bfloat16 else a[k].view(torch.int32),
                            b[k].view(torch.int16) if b[k].dtype == torch.bfloat16 else b[k].view(torch.int32)), k
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["mixtral", "dsv3"])
+def test_backward_data_full_size(name):
+    """The full-size layers, as the benchmark times them, on sampled tokens."""
+    cfg = synth.CONFIGS[name]
+    print(f"[bwd] full {name}: generating inputs", flush=True)
+    g = synth.make_inputs(cfg, "cuda", 0)
+    G = np.random.default_rng(12).standard_normal((cfg.T, cfg.d)).astype(np.float32)
+    Gt = torch.from_numpy(G).to(cfg.torch_dtype)
+    print(f"[bwd] full {name}: moe_backward_data", flush=True)
+    r = moe.moe_backward_data(g["X"], g["logits"], g["W1"], g["W3"], g["W2"], cfg.K, cuda(Gt))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    toks = np.array(sorted(set(rng.choice(cfg.T, size=8, replace=False).tolist()) | {0, cfg.T - 1}), np.int32)
+    print(f"[bwd] full {name}: oracle on {toks.size} tokens", flush=True)
+    ref = oracle.layer_backward_rows(to_np(g["X"]), to_np(g["logits"]), to_np(g["W1"]), to_np(g["W3"]),
+                                     to_np(g["W2"]), cfg.K, Gt.float().numpy(), toks)
+    sel = torch.from_numpy(toks).long().cuda()
+    check_close(r["dX"][sel], ref["dX"], cfg.dtype, "dX (sampled tokens)")
+    check_close(r["dw"][sel], ref["dw"], cfg.dtype, "dw (sampled tokens)")
+    check_logit_grad(r["dlogits"][sel], ref, cfg.dtype, "dlogits (sampled tokens)")

@@ -137,3 +137,12 @@ def test_linear_in_dout_and_exact_bf16_widening():
     d = oracle.layer_backward(wide[0], lg, wide[1], wide[2], wide[3], 2, G)
     for k in c:
         assert np.array_equal(c[k], d[k]), k
+
+
+def test_rows_variant_equals_the_full_backward():
+    X, lg, W1, W3, W2, G = _case(8, T=9, K=2)
+    full = oracle.layer_backward(X, lg, W1, W3, W2, 2, G)
+    toks = np.array([8, 0, 3, 3], np.int32)
+    part = oracle.layer_backward_rows(X, lg, W1, W3, W2, 2, G, toks)
+    for k in ("dX", "dlogits", "dw"):
+        assert np.array_equal(part[k], full[k][toks]), k
