@@ -22,10 +22,11 @@ namespace moe {
 
 namespace {
 
-constexpr int kTr = 32;  // transpose tile
+constexpr int kTr = 32;  // fp32 transpose tile
+constexpr int kTr16 = 64;  // bf16 transpose tile: rows of 128 bytes
 
 // out[e*oes + c*ors + r] = in[e][r][c] for in [E][R][C]; one 32 x 32 tile per
-// workgroup (256 threads), through LDS.
+// workgroup (256 threads), through LDS.  fp32.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_experts_kernel(const T* __restrict__ in, int R, int C,
                                                                 T* __restrict__ out, size_t oes, size_t ors) {
@@ -45,6 +46,49 @@ __global__ __launch_bounds__(256) void transpose_experts_kernel(const T* __restr
     for (int i = 0; i < kTr / 8; ++i) {
         const int c = c0 + ty + 8 * i, r = r0 + tx;
         if (r < R && c < C) dst[(size_t)c * ors + r] = tile[tx][ty + 8 * i];
+    }
+}
+
+// The bf16 transpose, one 64 x 64 tile per workgroup: 16-byte loads along
+// the input rows and 16-byte stores along the output rows (8 elements each),
+// so that every global access is a whole 128-byte row segment.  R, C, oes and
+// ors must be multiples of 8 (whole pieces); tiles past R or C are skipped
+// piece by piece.
+__global__ __launch_bounds__(256) void transpose_experts_bf16_kernel(const uint16_t* __restrict__ in, int R, int C,
+                                                                     uint16_t* __restrict__ out, size_t oes,
+                                                                     size_t ors) {
+    __shared__ uint16_t tile[kTr16][kTr16 + 2];
+    const int c0 = blockIdx.x * kTr16, r0 = blockIdx.y * kTr16;
+    const size_t e = blockIdx.z;
+    const uint16_t* src = in + e * (size_t)R * C;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = threadIdx.x + 256 * h;  // 512 pieces: 64 rows x 8
+        const int row = q >> 3, pc = q & 7;
+        const int r = r0 + row, c = c0 + pc * 8;
+        if (r < R && c < C) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)r * C + c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                tile[row][pc * 8 + 2 * i] = (uint16_t)(v[i] & 0xFFFFu);
+                tile[row][pc * 8 + 2 * i + 1] = (uint16_t)(v[i] >> 16);
+            }
+        }
+    }
+    __syncthreads();
+    uint16_t* dst = out + e * oes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = threadIdx.x + 256 * h;  // 64 output rows (c) x 8 pieces of r
+        const int col = q >> 3, pr = q & 7;
+        const int c = c0 + col, r = r0 + pr * 8;
+        if (r < R && c < C) {
+            u32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[i] = (uint32_t)tile[pr * 8 + 2 * i][col] | ((uint32_t)tile[pr * 8 + 2 * i + 1][col] << 16);
+            *reinterpret_cast<u32x4*>(dst + (size_t)c * ors + r) = v;
+        }
     }
 }
 
@@ -82,6 +126,51 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ H
     if (lane == 0) dS_tk[tk] = ds;
 }
 
+// The bf16 SwiGLU backward with 8 elements per lane (16-byte loads and
+// stores); n must be a multiple of 8.  Same arithmetic as above per element.
+__global__ __launch_bounds__(256) void swiglu_bwd_bf16_kernel(const uint16_t* __restrict__ H1,
+                                                              const uint16_t* __restrict__ H3,
+                                                              const uint16_t* __restrict__ dA,
+                                                              const float* __restrict__ topk_w,
+                                                              const int32_t* __restrict__ sorted_pair, int rows, int n,
+                                                              uint16_t* __restrict__ dH, float* __restrict__ dS_tk) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int p = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (p >= rows) return;
+    const int tk = sorted_pair[p];
+    const float w = topk_w[tk];
+    const size_t rb = (size_t)p * n;
+    float ds = 0.0f;
+    for (int j = lane * 8; j < n; j += kWave * 8) {
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(H1 + rb + j);
+        const u32x4 a3 = *reinterpret_cast<const u32x4*>(H3 + rb + j);
+        const u32x4 ga = *reinterpret_cast<const u32x4*>(dA + rb + j);
+        u32x4 o1, o3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float r1[2], r3[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const float h1 = bf16_to_f32((uint16_t)(a1[i] >> (16 * hh)));
+                const float h3 = bf16_to_f32((uint16_t)(a3[i] >> (16 * hh)));
+                const float g = bf16_to_f32((uint16_t)(ga[i] >> (16 * hh)));
+                const float sig = 1.0f / (1.0f + expf(-h1));
+                const float s1 = h1 * sig;
+                ds = fmaf(g, s1 * h3, ds);
+                const float wg = w * g;
+                r1[hh] = wg * h3 * sig * (1.0f + h1 * (1.0f - sig));
+                r3[hh] = wg * s1;
+            }
+            o1[i] = pack_bf16x2(r1[0], r1[1]);
+            o3[i] = pack_bf16x2(r3[0], r3[1]);
+        }
+        *reinterpret_cast<u32x4*>(dH + 2 * rb + j) = o1;
+        *reinterpret_cast<u32x4*>(dH + 2 * rb + n + j) = o3;
+    }
+    ds = group_sum<kWave>(ds);
+    if (lane == 0) dS_tk[tk] = ds;
+}
+
 // dlogits[t, e] = w_k (dS_k - sum_j w_j dS_j) when e = idx[t, k], else 0;
 // one thread per (t, e).
 __global__ __launch_bounds__(256) void logit_grad_kernel(const int32_t* __restrict__ idx,
@@ -109,10 +198,11 @@ __global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ p, si
 hipError_t launch_transpose_experts(const void* in, int dtype, int E, int R, int C, void* out, size_t oes,
                                     size_t ors, hipStream_t s) {
     const dim3 grid((unsigned)((C + kTr - 1) / kTr), (unsigned)((R + kTr - 1) / kTr), (unsigned)E);
-    if (dtype == 1)
-        hipLaunchKernelGGL(transpose_experts_kernel<uint16_t>, grid, dim3(256), 0, s,
-                           static_cast<const uint16_t*>(in), R, C, static_cast<uint16_t*>(out), oes, ors);
-    else
+    if (dtype == 1) {
+        const dim3 g16((unsigned)((C + kTr16 - 1) / kTr16), (unsigned)((R + kTr16 - 1) / kTr16), (unsigned)E);
+        hipLaunchKernelGGL(transpose_experts_bf16_kernel, g16, dim3(256), 0, s, static_cast<const uint16_t*>(in), R,
+                           C, static_cast<uint16_t*>(out), oes, ors);
+    } else
         hipLaunchKernelGGL(transpose_experts_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(in),
                            R, C, static_cast<float*>(out), oes, ors);
     return hipGetLastError();
@@ -124,7 +214,7 @@ hipError_t launch_swiglu_bwd(const void* H1, const void* H3, const void* dA, con
     const dim3 grid((unsigned)((rows + 3) / 4));
     if (rows <= 0) return hipSuccess;
     if (dtype == 1)
-        hipLaunchKernelGGL(swiglu_bwd_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(H1),
+        hipLaunchKernelGGL(swiglu_bwd_bf16_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(H1),
                            static_cast<const uint16_t*>(H3), static_cast<const uint16_t*>(dA), topk_w, sorted_pair,
                            rows, n, static_cast<uint16_t*>(dH), dS_tk);
     else
