@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the DeepSeek-V3-shaped and fine-grained layer timings")
+    ap.add_argument("--backward-probe", action="store_true",
+                    help="run moe_backward_data on the mixtral-shaped layer once, then 3 times back to back, "
+                         "for a kernel trace, and print its time")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a plain copy of known size and each step once (for rocprofv3 --pmc) and exit")
     return ap.parse_args()
@@ -157,6 +160,11 @@ def main():
     torch.cuda.set_device(dev)
     if args.traffic_probe:
         traffic_probe(moe, synth, torch, dev)
+        return
+    if args.backward_probe:
+        c = synth.CONFIGS["mixtral"]
+        print(json.dumps({"backward_probe": backward_data(c, synth.make_inputs(c, dev, seed=0), moe, torch, dev)}),
+              flush=True)
         return
 
     cfg = synth.CONFIGS["mixtral"]
