@@ -304,7 +304,7 @@ int moe_forward_tr(const void* X, const float* logits, const void* W1, const voi
  *   dw[t,k] = <dA, a>, dh1 = w_k dA h3 SiLU'(h1), dh3 = w_k dA SiLU(h1),
  *   dX[t] = sum_k dh1 W1[e]^T + dh3 W3[e]^T,
  *   dlogits[t, idx_k] = w_k (dw[t,k] - sum_j w_j dw[t,j]), 0 for other experts.
- * The expert-weight gradients are not computed.
+ * The expert-weight gradients are not computed here (moe_backward adds them).
  * In:  X [T,d], W1/W3 [E,d,n], W2 [E,n,d] and dout [T,d] in dtype; logits
  *      [T,E] fp32.  Sizes and limits as moe_forward.
  * Out: dX [T,d] (dtype), dlogits [T,E] fp32, dw [T,K] fp32 (may be NULL).
@@ -320,6 +320,21 @@ size_t moe_backward_data_workspace_bytes(int T, int d, int E, int K, int n, int 
 int moe_backward_data(const void* X, const float* logits, const void* W1, const void* W3, const void* W2, int dtype,
                       int T, int d, int E, int K, int n, const void* dout, void* dX, float* dlogits, float* dw,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_backward -- moe_backward_data plus the expert-weight gradients, summed
+ * over the assignments of each expert (in ascending row order, fp32):
+ *   dW1[e] = sum x^T dh1,  dW3[e] = sum x^T dh3,  dW2[e] = sum (w_k a)^T g
+ * with x the token row, dh1, dh3, a and g as in moe_backward_data.
+ * Out: as moe_backward_data, plus dW1, dW3 [E,d,n] and dW2 [E,n,d] fp32
+ *      (required, 16-byte aligned; experts with no rows get zeros).
+ * Workspace: moe_backward_workspace_bytes(T,d,E,K,n,dtype) bytes (the data
+ *      backward's plus one [T*K, n] buffer).  Errors as moe_backward_data.
+ */
+size_t moe_backward_workspace_bytes(int T, int d, int E, int K, int n, int dtype);
+int moe_backward(const void* X, const float* logits, const void* W1, const void* W3, const void* W2, int dtype, int T,
+                 int d, int E, int K, int n, const void* dout, void* dX, float* dlogits, float* dw, float* dW1,
+                 float* dW3, float* dW2, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

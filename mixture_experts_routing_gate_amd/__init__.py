@@ -66,6 +66,8 @@ def load_library() -> ctypes.CDLL:
         "moe_forward_tr": ([P, P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, Z, P], I),
         "moe_backward_data_workspace_bytes": ([I, I, I, I, I, I], Z),
         "moe_backward_data": ([P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
+        "moe_backward_workspace_bytes": ([I, I, I, I, I, I], Z),
+        "moe_backward": ([P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P], I),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -392,4 +394,30 @@ def moe_backward_data(X: torch.Tensor, logits: torch.Tensor, W1: torch.Tensor, W
                                  _dev(W3, "W3", dt), _dev(W2, "W2", dt), dtype_code(dt), T, d, E, K, n,
                                  _dev(dout, "dout", dt), r["dX"].data_ptr(), r["dlogits"].data_ptr(),
                                  r["dw"].data_ptr(), _dev(ws, "ws"), ws.numel(), _stream(dev)), "moe_backward_data")
+    return r
+
+
+def moe_backward(X: torch.Tensor, logits: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, W2: torch.Tensor,
+                 K: int, dout: torch.Tensor, ws: torch.Tensor | None = None):
+    """moe_backward_data plus the expert-weight gradients dW1, dW3 [E,d,n] and dW2 [E,n,d] (f32).
+    Returns a dict with dX, dlogits, dw, dW1, dW3, dW2."""
+    lib = load_library()
+    T, d = X.shape
+    E, _, n = W1.shape
+    dt = X.dtype
+    dev = X.device
+    nws = lib.moe_backward_workspace_bytes(T, d, E, K, n, dtype_code(dt))
+    if nws == 0:
+        raise MoEError(MOE_ERR_UNSUPPORTED, "moe_backward_workspace_bytes", lib.moe_last_error().decode())
+    if ws is None:
+        ws = _workspace(nws, dev)
+    f32 = torch.float32
+    r = {"dX": torch.empty((T, d), dtype=dt, device=dev), "dlogits": torch.empty((T, E), dtype=f32, device=dev),
+         "dw": torch.empty((T, K), dtype=f32, device=dev), "dW1": torch.empty((E, d, n), dtype=f32, device=dev),
+         "dW3": torch.empty((E, d, n), dtype=f32, device=dev), "dW2": torch.empty((E, n, d), dtype=f32, device=dev)}
+    _check(lib.moe_backward(_dev(X, "X", dt), _dev(logits, "logits", f32), _dev(W1, "W1", dt), _dev(W3, "W3", dt),
+                            _dev(W2, "W2", dt), dtype_code(dt), T, d, E, K, n, _dev(dout, "dout", dt),
+                            r["dX"].data_ptr(), r["dlogits"].data_ptr(), r["dw"].data_ptr(), r["dW1"].data_ptr(),
+                            r["dW3"].data_ptr(), r["dW2"].data_ptr(), _dev(ws, "ws"), ws.numel(), _stream(dev)),
+           "moe_backward")
     return r

@@ -14,7 +14,10 @@
 //   dlogits[t, idx_k] = w_k (dS_k - sum_j w_j dS_j), 0 for experts not chosen.
 // The GEMMs are the forward's grouped kernels on transposed weight copies;
 // this file holds the kernels that are new: the weight transpose, the SwiGLU
-// backward with dS, the logit gradient and a fill.
+// backward with dS, the logit gradient, a fill, and the weight gradients
+//   dW1[e] = Xp^T dh1, dW3[e] = Xp^T dh3, dW2[e] = (w a)^T dY
+// summed over each expert's rows (its own kernel: the reduction runs over the
+// ragged rows, so tiles are indexed by expert rather than by row).
 #include "common.h"
 #include "launch.h"
 
@@ -105,7 +108,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ H1, const T* __restrict__ H3,
                                                          const T* __restrict__ dA, const float* __restrict__ topk_w,
                                                          const int32_t* __restrict__ sorted_pair, int rows, int n,
-                                                         T* __restrict__ dH, float* __restrict__ dS_tk) {
+                                                         T* __restrict__ dH, float* __restrict__ dS_tk,
+                                                         T* __restrict__ aw) {
     const int lane = threadIdx.x & (kWave - 1);
     const int p = blockIdx.x * 4 + threadIdx.x / kWave;
     if (p >= rows) return;
@@ -121,6 +125,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ H
         const float wg = w * g;
         store_el(dH, 2 * rb + j, wg * h3 * sig * (1.0f + h1 * (1.0f - sig)));
         store_el(dH, 2 * rb + n + j, wg * s1);
+        if (aw != nullptr) store_el(aw, rb + j, w * (s1 * h3));
     }
     ds = group_sum<kWave>(ds);
     if (lane == 0) dS_tk[tk] = ds;
@@ -133,7 +138,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_bf16_kernel(const uint16_t* __
                                                               const uint16_t* __restrict__ dA,
                                                               const float* __restrict__ topk_w,
                                                               const int32_t* __restrict__ sorted_pair, int rows, int n,
-                                                              uint16_t* __restrict__ dH, float* __restrict__ dS_tk) {
+                                                              uint16_t* __restrict__ dH, float* __restrict__ dS_tk,
+                                                              uint16_t* __restrict__ aw) {
     const int lane = threadIdx.x & (kWave - 1);
     const int p = blockIdx.x * 4 + threadIdx.x / kWave;
     if (p >= rows) return;
@@ -145,10 +151,10 @@ __global__ __launch_bounds__(256) void swiglu_bwd_bf16_kernel(const uint16_t* __
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(H1 + rb + j);
         const u32x4 a3 = *reinterpret_cast<const u32x4*>(H3 + rb + j);
         const u32x4 ga = *reinterpret_cast<const u32x4*>(dA + rb + j);
-        u32x4 o1, o3;
+        u32x4 o1, o3, oa;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float r1[2], r3[2];
+            float r1[2], r3[2], ra[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const float h1 = bf16_to_f32((uint16_t)(a1[i] >> (16 * hh)));
@@ -160,15 +166,123 @@ __global__ __launch_bounds__(256) void swiglu_bwd_bf16_kernel(const uint16_t* __
                 const float wg = w * g;
                 r1[hh] = wg * h3 * sig * (1.0f + h1 * (1.0f - sig));
                 r3[hh] = wg * s1;
+                ra[hh] = w * (s1 * h3);
             }
             o1[i] = pack_bf16x2(r1[0], r1[1]);
             o3[i] = pack_bf16x2(r3[0], r3[1]);
+            oa[i] = pack_bf16x2(ra[0], ra[1]);
         }
         *reinterpret_cast<u32x4*>(dH + 2 * rb + j) = o1;
         *reinterpret_cast<u32x4*>(dH + 2 * rb + n + j) = o3;
+        if (aw != nullptr) *reinterpret_cast<u32x4*>(aw + rb + j) = oa;
     }
     ds = group_sum<kWave>(ds);
     if (lane == 0) dS_tk[tk] = ds;
+}
+
+// Weight gradient of one expert's linear map, summed over its rows:
+//   dW[e][m][c] = sum over rows r of expert e of P[r][m] * Q[r][qoff + c]
+// (fp32 out, [E, M, N]).  For dW1 / dW3: P = the expert-sorted X, Q = the
+// dh1 / dh3 halves of dH; for dW2: P = w * act, Q = the expert-sorted dout.
+// One 128 x 128 tile of one expert per workgroup, four waves of 64 x 64 on
+// v_mfma_f32_32x32x16_bf16; rows are the reduction, 32 at a time, both
+// operands transposed into LDS (k contiguous) so that each fragment is one
+// 16-byte read; rows past the expert's count read as zeros.  The sum runs over
+// rows in ascending order: deterministic.
+__global__ __launch_bounds__(256, 2) void dw_bf16_kernel(const uint16_t* __restrict__ P, int ldp,
+                                                         const uint16_t* __restrict__ Q, int ldq, int qoff,
+                                                         const int32_t* __restrict__ counts,
+                                                         const int32_t* __restrict__ offsets, int M, int N, int rows,
+                                                         float* __restrict__ dW) {
+    constexpr int BM = 128, BN = 128, BK = 32, LDK = BK + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t Ps[BM * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Qs[BN * LDK];
+    const int MT = M / BM, NT = N / BN;
+    const int tile = blockIdx.x;
+    const int e = tile / (MT * NT), rem = tile % (MT * NT);
+    const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, lh = lane >> 5;
+    const int cnt = counts[e];
+    const int r0 = offsets[e];
+    // rows of the expert that exist; never past the end of P/Q whatever counts/offsets hold
+    const int nr = (r0 < 0 || r0 >= rows || cnt <= 0) ? 0 : min(cnt, rows - r0);
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+
+    for (int k0 = 0; k0 < nr; k0 += BK) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + 256 * i;  // 32 rows x 16 pieces of 8 columns
+            const int kr = c >> 4, mc = (c & 15) << 3;
+            u32x4 vp = {0u, 0u, 0u, 0u}, vq = {0u, 0u, 0u, 0u};
+            if (k0 + kr < nr) {
+                const size_t r = (size_t)(r0 + k0 + kr);
+                vp = *reinterpret_cast<const u32x4*>(P + r * ldp + m0 + mc);
+                vq = *reinterpret_cast<const u32x4*>(Q + r * ldq + qoff + n0 + mc);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                Ps[(mc + j) * LDK + kr] = (uint16_t)(vp[j >> 1] >> (16 * (j & 1)));
+                Qs[(mc + j) * LDK + kr] = (uint16_t)(vq[j >> 1] >> (16 * (j & 1)));
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            bf16x8 a[2], b[2];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+                a[mi] = *reinterpret_cast<const bf16x8*>(Ps + (wm * 64 + mi * 32 + l32) * LDK + ks * 16 + lh * 8);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                b[ni] = *reinterpret_cast<const bf16x8*>(Qs + (wn * 64 + ni * 32 + l32) * LDK + ks * 16 + lh * 8);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+        }
+    }
+    // element i of lane l: row (i/4)*8 + (l/32)*4 + i%4, column l%32 of the 32 x 32 block
+    float* out = dW + (size_t)e * M * N;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + wm * 64 + mi * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+                const int col = n0 + wn * 64 + ni * 32 + l32;
+                out[(size_t)row * N + col] = acc[mi][ni][i];
+            }
+}
+
+// The same sum in fp32: one thread per output element, rows in ascending order.
+__global__ __launch_bounds__(256) void dw_f32_kernel(const float* __restrict__ P, int ldp, const float* __restrict__ Q,
+                                                     int ldq, int qoff, const int32_t* __restrict__ counts,
+                                                     const int32_t* __restrict__ offsets, int E, int M, int N,
+                                                     int rows, float* __restrict__ dW) {
+    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (size_t)E * M * N) return;
+    const int e = (int)(q / ((size_t)M * N));
+    const size_t rem = q % ((size_t)M * N);
+    const int m = (int)(rem / N), c = (int)(rem % N);
+    const int cnt = counts[e], r0 = offsets[e];
+    const int nr = (r0 < 0 || r0 >= rows || cnt <= 0) ? 0 : min(cnt, rows - r0);
+    float acc = 0.0f;
+    for (int k = 0; k < nr; ++k) {
+        const size_t r = (size_t)(r0 + k);
+        acc = fmaf(P[r * ldp + m], Q[r * ldq + qoff + c], acc);
+    }
+    dW[q] = acc;
 }
 
 // dlogits[t, e] = w_k (dS_k - sum_j w_j dS_j) when e = idx[t, k], else 0;
@@ -210,17 +324,32 @@ hipError_t launch_transpose_experts(const void* in, int dtype, int E, int R, int
 
 hipError_t launch_swiglu_bwd(const void* H1, const void* H3, const void* dA, const float* topk_w,
                              const int32_t* sorted_pair, int dtype, int rows, int n, void* dH, float* dS_tk,
-                             hipStream_t s) {
+                             void* aw, hipStream_t s) {
     const dim3 grid((unsigned)((rows + 3) / 4));
     if (rows <= 0) return hipSuccess;
     if (dtype == 1)
         hipLaunchKernelGGL(swiglu_bwd_bf16_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(H1),
                            static_cast<const uint16_t*>(H3), static_cast<const uint16_t*>(dA), topk_w, sorted_pair,
-                           rows, n, static_cast<uint16_t*>(dH), dS_tk);
+                           rows, n, static_cast<uint16_t*>(dH), dS_tk, static_cast<uint16_t*>(aw));
     else
         hipLaunchKernelGGL(swiglu_bwd_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(H1),
                            static_cast<const float*>(H3), static_cast<const float*>(dA), topk_w, sorted_pair, rows,
-                           n, static_cast<float*>(dH), dS_tk);
+                           n, static_cast<float*>(dH), dS_tk, static_cast<float*>(aw));
+    return hipGetLastError();
+}
+
+hipError_t launch_dw(const void* P, int ldp, const void* Q, int ldq, int qoff, const int32_t* counts,
+                     const int32_t* offsets, int dtype, int E, int M, int N, int rows, float* dW, hipStream_t s) {
+    if (dtype == 1) {
+        const unsigned tiles = (unsigned)((size_t)E * (M / 128) * (N / 128));
+        hipLaunchKernelGGL(dw_bf16_kernel, dim3(tiles), dim3(256), 0, s, static_cast<const uint16_t*>(P), ldp,
+                           static_cast<const uint16_t*>(Q), ldq, qoff, counts, offsets, M, N, rows, dW);
+    } else {
+        const size_t nel = (size_t)E * M * N;
+        hipLaunchKernelGGL(dw_f32_kernel, dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, s,
+                           static_cast<const float*>(P), ldp, static_cast<const float*>(Q), ldq, qoff, counts,
+                           offsets, E, M, N, rows, dW);
+    }
     return hipGetLastError();
 }
 

@@ -95,7 +95,11 @@ hipError_t launch_transpose_experts(const void* in, int dtype, int E, int R, int
                                     size_t ors, hipStream_t s);
 hipError_t launch_swiglu_bwd(const void* H1, const void* H3, const void* dA, const float* topk_w,
                              const int32_t* sorted_pair, int dtype, int rows, int n, void* dH, float* dS_tk,
-                             hipStream_t s);
+                             void* aw, hipStream_t s);
+// dW[e][m][c] = sum over expert e's rows r of P[r][m] Q[r][qoff + c] (fp32 out [E, M, N]);
+// bf16 needs M and N multiples of 128.
+hipError_t launch_dw(const void* P, int ldp, const void* Q, int ldq, int qoff, const int32_t* counts,
+                     const int32_t* offsets, int dtype, int E, int M, int N, int rows, float* dW, hipStream_t s);
 hipError_t launch_logit_grad(const int32_t* idx, const float* topk_w, const float* dS_tk, int T, int E, int K,
                              float* dlogits, hipStream_t s);
 hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s);

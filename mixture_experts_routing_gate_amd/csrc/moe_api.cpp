@@ -123,7 +123,7 @@ size_t forward_ws(int T, int d, int E, int K, int n, int dtype) {
 }
 
 // Workspace of moe_backward_data, in carving order.
-size_t backward_ws(int T, int d, int E, int K, int n, int dtype) {
+size_t backward_ws(int T, int d, int E, int K, int n, int dtype, bool weights) {
     const size_t A = (size_t)T * K;
     const size_t s = elem_bytes(dtype);
     size_t b = 0;
@@ -136,6 +136,7 @@ size_t backward_ws(int T, int d, int E, int K, int n, int dtype) {
     b += align_up(A * n * s) * 3 + align_up(A * 2 * n * s);  // H1, H3, dA, dH
     b += align_up((size_t)E * d * n * s) * 3;               // W2^T, [W1^T ; W3^T]
     b += align_up(ffn_split_bytes(dtype, 256, 128));        // split tail of the grouped GEMMs
+    if (weights) b += align_up(A * n * s);                  // w * act, for dW2
     return b;
 }
 
@@ -617,12 +618,25 @@ size_t moe_backward_data_workspace_bytes(int T, int d, int E, int K, int n, int 
     if (check_tek(T, E, K) != MOE_OK || check_dtype(dtype) != MOE_OK || check_dim("d", d, dtype) != MOE_OK ||
         check_dim("n", n, dtype) != MOE_OK)
         return 0;
-    return backward_ws(T, d, E, K, n, dtype);
+    return backward_ws(T, d, E, K, n, dtype, false);
 }
 
-int moe_backward_data(const void* X, const float* logits, const void* W1, const void* W3, const void* W2, int dtype,
-                      int T, int d, int E, int K, int n, const void* dout, void* dX, float* dlogits, float* dw,
-                      void* ws, size_t ws_bytes, void* stream) {
+size_t moe_backward_workspace_bytes(int T, int d, int E, int K, int n, int dtype) {
+    if (check_tek(T, E, K) != MOE_OK || check_dtype(dtype) != MOE_OK || check_dim("d", d, dtype) != MOE_OK ||
+        check_dim("n", n, dtype) != MOE_OK)
+        return 0;
+    return backward_ws(T, d, E, K, n, dtype, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The backward of both entry points; the weight gradients when dW1 is not NULL.
+int backward_impl(const char* name, const void* X, const float* logits, const void* W1, const void* W3,
+                  const void* W2, int dtype, int T, int d, int E, int K, int n, const void* dout, void* dX,
+                  float* dlogits, float* dw, float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes,
+                  void* stream) {
     CHECK(check_tek(T, E, K));
     CHECK(check_dtype(dtype));
     CHECK(check_dim("d", d, dtype));
@@ -635,12 +649,17 @@ int moe_backward_data(const void* X, const float* logits, const void* W1, const 
     NONNULL(dout);
     NONNULL(dX);
     NONNULL(dlogits);
+    const bool weights = dW1 != nullptr;
+    if (weights) {
+        NONNULL(dW3);
+        NONNULL(dW2);
+    }
     if (dw != nullptr && !aligned16(dw)) return fail(MOE_ERR_INVALID_ARG, "dw must be 16-byte aligned");
     if ((long long)T * K * 2LL * (long long)(d > n ? d : n) >= (1LL << 40))
         return fail(MOE_ERR_UNSUPPORTED, "T*K*2*max(d,n) must be < 2^40");
-    const size_t need = backward_ws(T, d, E, K, n, dtype);
+    const size_t need = backward_ws(T, d, E, K, n, dtype, weights);
     if (ws == nullptr || ws_bytes < need)
-        return fail(MOE_ERR_WORKSPACE, "moe_backward_data needs %zu workspace bytes (got %zu)", need, ws_bytes);
+        return fail(MOE_ERR_WORKSPACE, "%s needs %zu workspace bytes (got %zu)", name, need, ws_bytes);
     if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "ws must be 16-byte aligned");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -668,6 +687,7 @@ int moe_backward_data(const void* X, const float* logits, const void* W1, const 
     void* W13t = c.take<char>((size_t)E * 2 * d * n * sz);
     const size_t split_bytes = ffn_split_bytes(dtype, 256, 128);
     float* part = split_bytes ? c.take<float>(split_bytes / sizeof(float)) : nullptr;
+    void* aw = weights ? c.take<char>(A * n * sz) : nullptr;
     float* dS = dw != nullptr ? dw : ws_ds;
 
     // routing, as in moe_forward
@@ -690,14 +710,40 @@ int moe_backward_data(const void* X, const float* logits, const void* W1, const 
     HIPCHECK(launch_ffn_down(Xp, W1, dtype, (int)A, n, E, d, counts, offsets, H1, part, false, s));
     HIPCHECK(launch_ffn_down(Xp, W3, dtype, (int)A, n, E, d, counts, offsets, H3, part, false, s));
     HIPCHECK(launch_ffn_down(dY, W2t, dtype, (int)A, n, E, d, counts, offsets, dA, part, false, s));
-    // SwiGLU backward and dS; then dXp = [dh1 | dh3] [W1^T ; W3^T]
-    HIPCHECK(launch_swiglu_bwd(H1, H3, dA, w, sorted_pair, dtype, (int)A, n, dH, dS, s));
+    // SwiGLU backward and dS (and w * act for dW2)
+    HIPCHECK(launch_swiglu_bwd(H1, H3, dA, w, sorted_pair, dtype, (int)A, n, dH, dS, aw, s));
+    if (weights) {
+        // dW1 = Xp^T dh1, dW3 = Xp^T dh3, dW2 = (w act)^T dY, over each expert's rows
+        HIPCHECK(launch_dw(Xp, d, dH, 2 * n, 0, counts, offsets, dtype, E, d, n, (int)A, dW1, s));
+        HIPCHECK(launch_dw(Xp, d, dH, 2 * n, n, counts, offsets, dtype, E, d, n, (int)A, dW3, s));
+        HIPCHECK(launch_dw(aw, n, dY, d, 0, counts, offsets, dtype, E, n, d, (int)A, dW2, s));
+    }
+    // dXp = [dh1 | dh3] [W1^T ; W3^T] (overwrites Xp)
     HIPCHECK(launch_ffn_down(dH, W13t, dtype, (int)A, d, E, 2 * n, counts, offsets, Xp, part, false, s));
     // dX[t] = sum over the token's rows, unit weights; logit gradient from dS
     HIPCHECK(launch_fill_f32(ones, A, 1.0f, s));
     HIPCHECK(launch_combine(Xp, ones, inv, dtype, T, d, K, dX, s));
     HIPCHECK(launch_logit_grad(idx, w, dS, T, E, K, dlogits, s));
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_backward_data(const void* X, const float* logits, const void* W1, const void* W3, const void* W2, int dtype,
+                      int T, int d, int E, int K, int n, const void* dout, void* dX, float* dlogits, float* dw,
+                      void* ws, size_t ws_bytes, void* stream) {
+    return backward_impl("moe_backward_data", X, logits, W1, W3, W2, dtype, T, d, E, K, n, dout, dX, dlogits, dw,
+                         nullptr, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int moe_backward(const void* X, const float* logits, const void* W1, const void* W3, const void* W2, int dtype, int T,
+                 int d, int E, int K, int n, const void* dout, void* dX, float* dlogits, float* dw, float* dW1,
+                 float* dW3, float* dW2, void* ws, size_t ws_bytes, void* stream) {
+    if (dW1 == nullptr) return fail(MOE_ERR_INVALID_ARG, "dW1 must not be NULL");
+    return backward_impl("moe_backward", X, logits, W1, W3, W2, dtype, T, d, E, K, n, dout, dX, dlogits, dw, dW1,
+                         dW3, dW2, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -92,3 +92,26 @@ def test_backward_data_full_size(name):
     check_close(r["dX"][sel], ref["dX"], cfg.dtype, "dX (sampled tokens)")
     check_close(r["dw"][sel], ref["dw"], cfg.dtype, "dw (sampled tokens)")
     check_logit_grad(r["dlogits"][sel], ref, cfg.dtype, "dlogits (sampled tokens)")
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+def test_backward_weight_gradients_match_oracle(cfg):
+    """moe_backward: the data gradients equal moe_backward_data's bit for bit,
+    and dW1, dW3, dW2 match the oracle within the output tolerance."""
+    print(f"[bwd-w] {cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} K={cfg.K} n={cfg.n} {cfg.dtype}", flush=True)
+    inp = synth.make_inputs(cfg, "cpu", 0)
+    G = np.random.default_rng(13).standard_normal((cfg.T, cfg.d)).astype(np.float32)
+    Gt = torch.from_numpy(G).to(cfg.torch_dtype)
+    args = (cuda(inp["X"]), cuda(inp["logits"]), cuda(inp["W1"]), cuda(inp["W3"]), cuda(inp["W2"]), cfg.K, cuda(Gt))
+    full = moe.moe_backward(*args)
+    data = moe.moe_backward_data(*args)
+    torch.cuda.synchronize()
+    for k in ("dX", "dlogits", "dw"):
+        assert torch.equal(full[k].float(), data[k].float()), k
+    ref = oracle.layer_backward(to_np(inp["X"]), to_np(inp["logits"]), to_np(inp["W1"]), to_np(inp["W3"]),
+                                to_np(inp["W2"]), cfg.K, Gt.float().numpy())
+    msg = []
+    for k in ("dW1", "dW3", "dW2"):
+        rel, _ = check_close(full[k], ref[k], cfg.dtype, k)
+        msg.append(f"{k} rel L2 {rel:.2e}")
+    print(f"[bwd-w] {cfg.name}: " + ", ".join(msg), flush=True)
