@@ -15,7 +15,8 @@ n=14336, bf16, fp32 accumulation), inputs resident in HBM.  Prints ONE JSON line
                 plain top-K on the same inputs (mixtral here; the other shapes
                 under other_workloads), with its plan and combine back to back
   backward_data = moe_backward_data (dX and the router-logit gradient) on the
-                same layer, per call, with the rate of its grouped GEMMs
+                same layer, per call, with the rate of its grouped GEMMs, and
+                moe_backward (the expert-weight gradients too)
   cpu_baseline= the CPU oracle (per-token loop, fp64 accumulation) on a bounded
                 sample of the same layer, on this host's cores
 Inputs are seeded synthetic tensors (see synth/); nothing is read from disk
@@ -390,7 +391,18 @@ def backward_data(c, g, moe, torch, dev, calls=3):
     flops = 10.0 * c.T * c.K * c.d * c.n
     res = {"what": "dX, dlogits and dw (no weight gradients)", "ms_per_call": round(ms, 4),
            "TFLOPS": flops / (ms * 1e-3) / 1e12, "flops_per_call": flops}
-    del ws, dout
+    del ws
+    # with the expert-weight gradients: 6*d*n more FLOPs per assignment
+    wsw = torch.empty(lib.moe_backward_workspace_bytes(c.T, c.d, c.E, c.K, c.n, 1), dtype=torch.uint8, device=dev)
+
+    def run_w():
+        moe.moe_backward(g["X"], g["logits"], g["W1"], g["W3"], g["W2"], c.K, dout, ws=wsw)
+
+    ms_w = b2b_time_ms(torch, run_w, n=calls, reps=1)
+    flops_w = 16.0 * c.T * c.K * c.d * c.n
+    res["with_weight_gradients"] = {"ms_per_call": round(ms_w, 4), "TFLOPS": flops_w / (ms_w * 1e-3) / 1e12,
+                                    "flops_per_call": flops_w}
+    del wsw, dout
     torch.cuda.empty_cache()
     return res
 

@@ -180,33 +180,57 @@ __global__ __launch_bounds__(256) void swiglu_bwd_bf16_kernel(const uint16_t* __
     if (lane == 0) dS_tk[tk] = ds;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i gets element i%4 of the
+// 8-byte pieces addressed by lanes i/4, 4+i/4, 8+i/4 and 12+i/4 (a 4 x 16 ->
+// 16 x 4 transpose of 16-bit values).
+MOE_DEV bf16x4 lds_tr4(const char* l) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(l)));
+}
+
 // Weight gradient of one expert's linear map, summed over its rows:
 //   dW[e][m][c] = sum over rows r of expert e of P[r][m] * Q[r][qoff + c]
 // (fp32 out, [E, M, N]).  For dW1 / dW3: P = the expert-sorted X, Q = the
 // dh1 / dh3 halves of dH; for dW2: P = w * act, Q = the expert-sorted dout.
 // One 128 x 128 tile of one expert per workgroup, four waves of 64 x 64 on
-// v_mfma_f32_32x32x16_bf16; rows are the reduction, 32 at a time, both
-// operands transposed into LDS (k contiguous) so that each fragment is one
-// 16-byte read; rows past the expert's count read as zeros.  The sum runs over
-// rows in ascending order: deterministic.
+// v_mfma_f32_32x32x16_bf16; the rows are the reduction, 32 at a time.  Both
+// operands arrive row-major (the reduction index outermost), so each 32-row
+// slab is stored as it is read, in 16-byte pieces (row r at r * 256 bytes,
+// piece c at position c ^ 4*(r % 4)), and the MFMA fragments (8 consecutive
+// rows per lane) come from transposing LDS reads.  Rows past the expert's
+// count read as zeros.  The sum runs over rows in ascending order.
 __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(const uint16_t* __restrict__ P, int ldp,
                                                          const uint16_t* __restrict__ Q, int ldq, int qoff,
                                                          const int32_t* __restrict__ counts,
                                                          const int32_t* __restrict__ offsets, int M, int N, int rows,
                                                          float* __restrict__ dW) {
-    constexpr int BM = 128, BN = 128, BK = 32, LDK = BK + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t Ps[BM * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[BN * LDK];
+    constexpr int BM = 128, BN = 128, BK = 32, SLAB = BK * 256;  // 8 KB per operand
+    __shared__ __attribute__((aligned(1024))) char Ps[SLAB];
+    __shared__ __attribute__((aligned(1024))) char Qs[SLAB];
     const int MT = M / BM, NT = N / BN;
     const int tile = blockIdx.x;
     const int e = tile / (MT * NT), rem = tile % (MT * NT);
     const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, lh = lane >> 5;
+    const int wm = wave >> 1, wn = wave & 1, lh = lane >> 5;
+    const int g16 = lane >> 4, s16 = lane & 15;
     const int cnt = counts[e];
     const int r0 = offsets[e];
     // rows of the expert that exist; never past the end of P/Q whatever counts/offsets hold
     const int nr = (r0 < 0 || r0 >= rows || cnt <= 0) ? 0 : min(cnt, rows - r0);
+    // byte offset of this lane's transposing read for the 32-column block starting at column cb
+    const int rd_lane = ((g16 >> 1) * 8 + (s16 >> 2)) * 256 + (s16 & 1) * 8;
+    const int rd_x = (s16 >> 2) << 2, rd_c = (g16 & 1) * 2 + ((s16 & 3) >> 1);
+    auto rd = [&](int cb) { return rd_lane + ((((cb >> 3) ^ rd_x) + rd_c) << 4); };
+    int pa[2], qa[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        pa[i] = rd(wm * 64 + i * 32);
+        qa[i] = rd(wn * 64 + i * 32);
+    }
+    (void)lh;
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -221,29 +245,28 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(const uint16_t* __restr
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int c = tid + 256 * i;  // 32 rows x 16 pieces of 8 columns
-            const int kr = c >> 4, mc = (c & 15) << 3;
+            const int kr = c >> 4, pc = c & 15;
             u32x4 vp = {0u, 0u, 0u, 0u}, vq = {0u, 0u, 0u, 0u};
             if (k0 + kr < nr) {
                 const size_t r = (size_t)(r0 + k0 + kr);
-                vp = *reinterpret_cast<const u32x4*>(P + r * ldp + m0 + mc);
-                vq = *reinterpret_cast<const u32x4*>(Q + r * ldq + qoff + n0 + mc);
+                vp = *reinterpret_cast<const u32x4*>(P + r * ldp + m0 + pc * 8);
+                vq = *reinterpret_cast<const u32x4*>(Q + r * ldq + qoff + n0 + pc * 8);
             }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                Ps[(mc + j) * LDK + kr] = (uint16_t)(vp[j >> 1] >> (16 * (j & 1)));
-                Qs[(mc + j) * LDK + kr] = (uint16_t)(vq[j >> 1] >> (16 * (j & 1)));
-            }
+            const int off = kr * 256 + ((pc ^ ((kr & 3) << 2)) << 4);
+            *reinterpret_cast<u32x4*>(Ps + off) = vp;
+            *reinterpret_cast<u32x4*>(Qs + off) = vq;
         }
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             bf16x8 a[2], b[2];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                a[mi] = *reinterpret_cast<const bf16x8*>(Ps + (wm * 64 + mi * 32 + l32) * LDK + ks * 16 + lh * 8);
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                b[ni] = *reinterpret_cast<const bf16x8*>(Qs + (wn * 64 + ni * 32 + l32) * LDK + ks * 16 + lh * 8);
+            for (int i = 0; i < 2; ++i) {
+                const char* pp = Ps + pa[i] + ks * 16 * 256;
+                const char* qq = Qs + qa[i] + ks * 16 * 256;
+                a[i] = __builtin_shufflevector(lds_tr4(pp), lds_tr4(pp + 4 * 256), 0, 1, 2, 3, 4, 5, 6, 7);
+                b[i] = __builtin_shufflevector(lds_tr4(qq), lds_tr4(qq + 4 * 256), 0, 1, 2, 3, 4, 5, 6, 7);
+            }
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -253,13 +276,14 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(const uint16_t* __restr
     }
     // element i of lane l: row (i/4)*8 + (l/32)*4 + i%4, column l%32 of the 32 x 32 block
     float* out = dW + (size_t)e * M * N;
+    const int l32 = lane & 31, lhh = lane >> 5;
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int row = m0 + wm * 64 + mi * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+                const int row = m0 + wm * 64 + mi * 32 + (i >> 2) * 8 + lhh * 4 + (i & 3);
                 const int col = n0 + wn * 64 + ni * 32 + l32;
                 out[(size_t)row * N + col] = acc[mi][ni][i];
             }
