@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(const uint16_t* __restr
     const int e = tile / (MT * NT), rem = tile % (MT * NT);
     const int m0 = (rem / NT) * BM, n0 = (rem % NT) * BN;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int wm = wave >> 1, wn = wave & 1, lh = lane >> 5;
+    const int wm = wave >> 1, wn = wave & 1;
     const int g16 = lane >> 4, s16 = lane & 15;
     const int cnt = counts[e];
     const int r0 = offsets[e];
@@ -230,7 +230,6 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(const uint16_t* __restr
         pa[i] = rd(wm * 64 + i * 32);
         qa[i] = rd(wn * 64 + i * 32);
     }
-    (void)lh;
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -276,14 +275,14 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(const uint16_t* __restr
     }
     // element i of lane l: row (i/4)*8 + (l/32)*4 + i%4, column l%32 of the 32 x 32 block
     float* out = dW + (size_t)e * M * N;
-    const int l32 = lane & 31, lhh = lane >> 5;
+    const int l32 = lane & 31, lh = lane >> 5;
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int row = m0 + wm * 64 + mi * 32 + (i >> 2) * 8 + lhh * 4 + (i & 3);
+                const int row = m0 + wm * 64 + mi * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
                 const int col = n0 + wn * 64 + ni * 32 + l32;
                 out[(size_t)row * N + col] = acc[mi][ni][i];
             }
