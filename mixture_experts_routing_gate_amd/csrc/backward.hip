@@ -195,8 +195,8 @@ MOE_DEV bf16x4 lds_tr4(const char* l) {
 // (fp32 out, [E, M, N]).  For dW1 / dW3: P = the expert-sorted X, Q = the
 // dh1 / dh3 halves of dH; for dW2: P = w * act, Q = the expert-sorted dout.
 // One 128 x 128 tile of one expert per workgroup, four waves of 64 x 64 on
-// v_mfma_f32_32x32x16_bf16; the rows are the reduction, 32 at a time.  Both
-// operands arrive row-major (the reduction index outermost), so each 32-row
+// v_mfma_f32_32x32x16_bf16; the rows are the reduction, 64 at a time.  Both
+// operands arrive row-major (the reduction index outermost), so each 64-row
 // slab is stored as it is read, in 16-byte pieces (row r at r * 256 bytes,
 // piece c at position c ^ 4*(r % 4)), and the MFMA fragments (8 consecutive
 // rows per lane) come from transposing LDS reads.  Rows past the expert's
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(const uint16_t* __restr
                                                          const int32_t* __restrict__ counts,
                                                          const int32_t* __restrict__ offsets, int M, int N, int rows,
                                                          float* __restrict__ dW) {
-    constexpr int BM = 128, BN = 128, BK = 32, SLAB = BK * 256;  // 8 KB per operand
+    constexpr int BM = 128, BN = 128, BK = 64, SLAB = BK * 256;  // 16 KB per operand
     __shared__ __attribute__((aligned(1024))) char Ps[SLAB];
     __shared__ __attribute__((aligned(1024))) char Qs[SLAB];
     const int MT = M / BM, NT = N / BN;
@@ -242,8 +242,8 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(const uint16_t* __restr
     for (int k0 = 0; k0 < nr; k0 += BK) {
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 256 * i;  // 32 rows x 16 pieces of 8 columns
+        for (int i = 0; i < BK / 16; ++i) {
+            const int c = tid + 256 * i;  // BK rows x 16 pieces of 8 columns
             const int kr = c >> 4, pc = c & 15;
             u32x4 vp = {0u, 0u, 0u, 0u}, vq = {0u, 0u, 0u, 0u};
             if (k0 + kr < nr) {
