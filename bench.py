@@ -241,6 +241,12 @@ def main():
     ge.synchronize()
     g_warm_ms = gs.elapsed_time(ge) / 20
     gate_bytes = gcfg.T * (4 * gcfg.E + 8 * gcfg.K)
+    # the small gate workload: launch-bound, reported for context (warm, back to back)
+    scfg = synth.CONFIGS["gate_s"]
+    slg = synth.make_inputs(scfg, dev, seed=0)["logits"]
+    s_ms = b2b_time_ms(torch, lambda: moe.moe_route(slg, scfg.K))
+    gate_small = {"workload": f"gate-only fp32 logits [T={scfg.T}, E={scfg.E}], K={scfg.K} (N(0,1))",
+                  "value": scfg.T / (s_ms * 1e-3) / 1e9, "unit": "Gtokens/s", "us_per_call_back_to_back": s_ms * 1e3}
     gate = {"workload": "gate-only fp32 logits [T=262144, E=128], K=8 (N(0,1))",
             "value": gcfg.T / (g_ms * 1e-3) / 1e9, "unit": "Gtokens/s", "us_per_call": g_ms * 1e3,
             "us_per_call_warm": g_warm_ms * 1e3,
@@ -276,6 +282,7 @@ def main():
                    "active_flops_per_step": flops, "expert_counts": counts_h.tolist(),
                    "load": load_stats(counts_h, A, E)},
         "gate": gate,
+        "gate_small": gate_small,
         "hbm_copy": hbm_copy,
         "steps_us": {
             "router": {"us": rt_ms * 1e3, "us_back_to_back": rt_b2b * 1e3,
