@@ -133,17 +133,27 @@ def moe_router(X: torch.Tensor, Wr: torch.Tensor, bias: torch.Tensor | None = No
     return logits
 
 
-def moe_route(logits: torch.Tensor, K: int):
-    """Steps 1-2.  logits [T,E] fp32 -> (topk_idx [T,K] i32, topk_w [T,K] f32, counts [E] i32, offsets [E+1] i32)."""
+def moe_route(logits: torch.Tensor, K: int, out=None, ws: torch.Tensor | None = None):
+    """Steps 1-2.  logits [T,E] fp32 -> (topk_idx [T,K] i32, topk_w [T,K] f32, counts [E] i32, offsets [E+1] i32).
+    `out` (optional) is such a tuple to write into and `ws` a workspace of moe_route_workspace_bytes bytes,
+    so that repeated calls allocate nothing."""
     lib = load_library()
     T, E = logits.shape
     dev = logits.device
-    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
-    w = torch.empty((T, K), dtype=torch.float32, device=dev)
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if out is None:
+        out = (torch.empty((T, K), dtype=torch.int32, device=dev), torch.empty((T, K), dtype=torch.float32, device=dev),
+               torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev))
+    idx, w, counts, offsets = out
+    for t, shape, dt, name in ((idx, (T, K), torch.int32, "topk_idx"), (w, (T, K), torch.float32, "topk_w"),
+                               (counts, (E,), torch.int32, "counts"), (offsets, (E + 1,), torch.int32, "offsets")):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        _dev(t, name, dt)
     nws = lib.moe_route_workspace_bytes(T, E, K)
-    ws = _workspace(nws, dev)
+    if ws is None:
+        ws = _workspace(nws, dev)
+    elif ws.numel() < nws:
+        raise ValueError(f"ws must hold {nws} bytes")
     _check(lib.moe_route(_dev(logits, "logits", torch.float32), T, E, K, idx.data_ptr(), w.data_ptr(),
                          counts.data_ptr(), offsets.data_ptr(), ws.data_ptr(), nws, _stream(dev)), "moe_route")
     return idx, w, counts, offsets
