@@ -21,6 +21,8 @@ CASES = [
     synth.MoEConfig("ragged_bias", T=1000, d=256, E=64, K=4, n=128, logits="bias", bias_var=2.0),
     synth.MoEConfig("k_equals_e", T=100, d=128, E=8, K=8, n=128),
     synth.MoEConfig("bf16_e256_k8", T=600, d=256, E=256, K=8, n=128, logits="bias", bias_var=1.5),
+    synth.MoEConfig("t1", T=1, d=128, E=16, K=4, n=128),           # one token: 12 experts without rows
+    synth.MoEConfig("dense_e1", T=130, d=128, E=1, K=1, n=256),    # one expert, weight 1: zero logit gradient
 ]
 
 
