@@ -241,19 +241,27 @@ __global__ __launch_bounds__(256, 2) void dw_bf16_kernel(const uint16_t* __restr
 
     for (int k0 = 0; k0 < nr; k0 += BK) {
         __syncthreads();
+        // BK rows x 16 pieces of 8 columns per operand: all loads issued, then all stores
+        u32x4 vp[BK / 16], vq[BK / 16];
 #pragma unroll
         for (int i = 0; i < BK / 16; ++i) {
-            const int c = tid + 256 * i;  // BK rows x 16 pieces of 8 columns
+            const int c = tid + 256 * i;
             const int kr = c >> 4, pc = c & 15;
-            u32x4 vp = {0u, 0u, 0u, 0u}, vq = {0u, 0u, 0u, 0u};
+            vp[i] = u32x4{0u, 0u, 0u, 0u};
+            vq[i] = u32x4{0u, 0u, 0u, 0u};
             if (k0 + kr < nr) {
                 const size_t r = (size_t)(r0 + k0 + kr);
-                vp = *reinterpret_cast<const u32x4*>(P + r * ldp + m0 + pc * 8);
-                vq = *reinterpret_cast<const u32x4*>(Q + r * ldq + qoff + n0 + pc * 8);
+                vp[i] = *reinterpret_cast<const u32x4*>(P + r * ldp + m0 + pc * 8);
+                vq[i] = *reinterpret_cast<const u32x4*>(Q + r * ldq + qoff + n0 + pc * 8);
             }
+        }
+#pragma unroll
+        for (int i = 0; i < BK / 16; ++i) {
+            const int c = tid + 256 * i;
+            const int kr = c >> 4, pc = c & 15;
             const int off = kr * 256 + ((pc ^ ((kr & 3) << 2)) << 4);
-            *reinterpret_cast<u32x4*>(Ps + off) = vp;
-            *reinterpret_cast<u32x4*>(Qs + off) = vq;
+            *reinterpret_cast<u32x4*>(Ps + off) = vp[i];
+            *reinterpret_cast<u32x4*>(Qs + off) = vq[i];
         }
         __syncthreads();
 #pragma unroll
