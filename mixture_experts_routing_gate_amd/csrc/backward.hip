@@ -1,5 +1,5 @@
-// Backward of the MoE layer, data gradients: dX and the router-logit gradient
-// from dout = dL/d(out).  Page [P4] "MoE architecture optimisation and
+// Backward of the MoE layer: dX, the router-logit gradient and (for
+// moe_backward) the expert-weight gradients from dout = dL/d(out).  Page [P4] "MoE architecture optimisation and
 // SonicMoE practice" section 2.2 names the products the backward needs beside
 // the weight gradients: dH through the SwiGLU and dS, the gradient of the
 // routing scores, taken as <dA, A> (the activation gradient before the score
