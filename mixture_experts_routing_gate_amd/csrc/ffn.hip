@@ -436,12 +436,19 @@ MOE_DEV size_t part_index(int wave, int f, int q, int lane) {
     return ((size_t)((wave * 16 + f) * 4 + q) * kWave + lane);
 }
 
-template <bool DUAL>
+// BT (plain GEMM only): B is given k-contiguous, as the transpose of each
+// expert's [N, kb] row-major matrix -- B0 for K-steps below kb / 32 and, when
+// Kd = 2 kb, B1 for the rest (C = A [B0^T ; B1^T]).  Its tile is staged like
+// A's (256 rows of the N side, 64 bytes of K each) and its fragments are read
+// like A's, so the backward multiplies by W2^T and [W1^T ; W3^T] without
+// transposing the weights first.
+template <bool DUAL, bool BT = false>
 __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     int E, int Kd, int N, int rows, float* __restrict__ part, int* __restrict__ ticket_ctr,
-    const int32_t* __restrict__ gather, int gK, int xrows) {
+    const int32_t* __restrict__ gather, int gK, int xrows, int kb) {
+    static_assert(!(DUAL && BT), "the k-contiguous B is for the plain GEMM");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     constexpr int OUTW = DUAL ? 128 : 256;
@@ -480,6 +487,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
         const int nn = DUAL ? (wn * 64 + (ni & 1) * 32) : ni * 32;
         b_rd[ni] = b_lane + half * 8192 + ((((nn >> 3) ^ b_x) + b_c) << 4);
     }
+    // BT: B row (output column) c, k-chunk q sits at 16K + c*64 + ((q ^ ((c/4)%4)) * 16),
+    // as A's rows do; fragment ni of sub-step ks at bt_rd[ks] + ni*32*64.
+    int bt_rd[2];
+    #pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+        bt_rd[ks] = 16384 + (wn * 128 + l32) * 64 + (((ks * 2 + lh) ^ ((l32 >> 2) & 3)) << 4);
 
     const uint32_t lds_base = uniform((int)(uint32_t)(uintptr_t)(lds_void*)smem);
     const int G = gridDim.x;
@@ -554,7 +567,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
             const rsrc_t ra = make_rsrc(gather != nullptr ? A : A + (size_t)r0 * Kd);
             const int half = wave >> 1;
             const uint16_t* bmat = (DUAL && half) ? B1 : B0;
-            const rsrc_t rb = make_rsrc(bmat + (size_t)e * Kd * N);
+            // BT: each expert's B0 (and B1) is N x kb; the descriptor's range
+            // ends at that matrix.
+            const int ktb = BT ? kb / kP4BK : KT;  // first K-step read from B1
+            const rsrc_t rb = BT ? make_rsrc(B0 + (size_t)e * kb * N, (uint32_t)((size_t)kb * N * 2))
+                                 : make_rsrc(bmat + (size_t)e * Kd * N);
+            const rsrc_t rb1 = (BT && B1 != nullptr) ? make_rsrc(B1 + (size_t)e * kb * N, (uint32_t)((size_t)kb * N * 2))
+                                                     : rb;
             uint32_t a_vo[4], b_vo[4];
             #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -567,7 +586,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                 const int kr = (wave & 1) * 16 + i * 4 + (lane >> 4);
                 const int bc = (lane & 15) ^ ((kr & 3) << 2);
                 const int col = (DUAL ? n0 : n0 + half * 128) + bc * 8;
-                b_vo[i] = ((uint32_t)kr * (uint32_t)N + col) * 2u;
+                b_vo[i] = BT ? ((uint32_t)(n0 + r) * (uint32_t)kb + ch * 8) * 2u
+                             : ((uint32_t)kr * (uint32_t)N + col) * 2u;
             }
             const uint32_t b_step = (uint32_t)kP4BK * (uint32_t)N * 2u;
             // DMA number i (0..7) of K-step kt into the stage at byte offset soff:
@@ -576,7 +596,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                 const uint32_t dst = lds_base + soff + (wave * 4) * 1024;
                 const uint32_t ka = (uint32_t)(ks0 + kt);
                 if (i < 4) dma16(ra, dst + i * 1024, a_vo[i], ka * (kP4BK * 2));
-                else dma16(rb, dst + 16384 + (i - 4) * 1024, b_vo[i - 4], ka * b_step);
+                else if constexpr (BT) {
+                    const bool hi = (int)ka >= ktb;
+                    dma16(hi ? rb1 : rb, dst + 16384 + (i - 4) * 1024, b_vo[i - 4],
+                          (hi ? ka - (uint32_t)ktb : ka) * (kP4BK * 2));
+                } else dma16(rb, dst + 16384 + (i - 4) * 1024, b_vo[i - 4], ka * b_step);
             };
             auto issue = [&](int kt, int soff) {
                 #pragma unroll
@@ -599,10 +623,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                     for (int mi = 0; mi < 4; ++mi) af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * 64);
                     #pragma unroll
                     for (int ni = 0; ni < 4; ++ni) {
-                        const char* pb = smem + soff + b_rd[ni] + ks * 16 * 256;
-                        const bf16x4 h0 = lds_read_tr(pb);
-                        const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
-                        bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        if constexpr (BT) {
+                            bfr[buf][ni] = *reinterpret_cast<const bf16x8*>(smem + soff + bt_rd[ks] + ni * 32 * 64);
+                        } else {
+                            const char* pb = smem + soff + b_rd[ni] + ks * 16 * 256;
+                            const bf16x4 h0 = lds_read_tr(pb);
+                            const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
+                            bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        }
                     }
                 };
                 auto mfma = [&](int buf, int lo, int hi) {
@@ -644,26 +672,36 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                         // Rest of sub-step 0 while sub-step 1's fragments are read.
                         load_frags(s_cur, 1, 1);
                         mfma(0, 8, 16);
-                        #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        }
-                        #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        // 12 LDS reads per sub-step (8 with BT) spread over the MFMAs.
+                        if constexpr (BT) {
+                            #pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            }
+                        } else {
+                            #pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            }
+                            #pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            }
                         }
                         __builtin_amdgcn_sched_barrier(0);
                         // Sub-step 1 while the next step's sub-step-0 fragments are read.
                         load_frags(s_nxt, 0, 0);
                         mfma(1, 0, 16);
+                        constexpr int kReads = BT ? 8 : 12;
                         #pragma unroll
-                        for (int i = 0; i < 12; ++i) {
+                        for (int i = 0; i < kReads; ++i) {
                             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                         }
-                        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 16 - kReads, 0);
                         s_cur = s_nxt;
                     }
                 }
@@ -705,6 +743,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                     const int nn = DUAL ? wave * 32 : (wave & 1) * 64 + ni * 32;
                     sb_rd[ni] = b_lane + sh * 8192 + ((((nn >> 3) ^ b_x) + b_c) << 4);
                 }
+                // BT: this wave's output columns wave*64 + ni*32 are B rows, read as A's.
+                int sbt_rd[2];
+                #pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    sbt_rd[ks] = 16384 + (wave * 64 + l32) * 64 + (((ks * 2 + lh) ^ ((l32 >> 2) & 3)) << 4);
                 f32x16 acc[MI][2];
                 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi)
@@ -719,10 +762,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                     for (int mi = 0; mi < MI; ++mi) af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * 64);
                     #pragma unroll
                     for (int ni = 0; ni < 2; ++ni) {
-                        const char* pb = smem + soff + sb_rd[ni] + ks * 16 * 256;
-                        const bf16x4 h0 = lds_read_tr(pb);
-                        const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
-                        bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        if constexpr (BT) {
+                            bfr[buf][ni] = *reinterpret_cast<const bf16x8*>(smem + soff + sbt_rd[ks] + ni * 32 * 64);
+                        } else {
+                            const char* pb = smem + soff + sb_rd[ni] + ks * 16 * 256;
+                            const bf16x4 h0 = lds_read_tr(pb);
+                            const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
+                            bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        }
                     }
                 };
                 auto mfma = [&](int buf) {
@@ -939,20 +986,20 @@ int* ffn_tickets(float* part) { return part ? reinterpret_cast<int*>(part + (siz
 int ffn_ticket_ints() { return 2 * kTicketInts; }
 
 // One pipelined GEMM (SwiGLU or plain), then the fixup of its split tail.
-template <bool DUAL>
+template <bool DUAL, bool BT = false>
 static hipError_t launch_pipelined(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                                    const int32_t* counts, const int32_t* offsets, int E, int Kd, int N, int rows,
                                    float* part, bool tickets_zeroed, const int32_t* gather, int gK, int xrows,
-                                   hipStream_t s) {
-    const hipError_t aerr =
-        hipFuncSetAttribute((const void*)ffn_p4_kernel<DUAL>, hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
+                                   hipStream_t s, int kb = 0) {
+    const hipError_t aerr = hipFuncSetAttribute((const void*)ffn_p4_kernel<DUAL, BT>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
     if (aerr != hipSuccess) return aerr;
     const int G = ffn_grid();
     int* tickets = part != nullptr ? ffn_tickets(part) + (DUAL ? 0 : kTicketInts) : nullptr;
     if (tickets != nullptr && !tickets_zeroed)
         hipLaunchKernelGGL(zero_ints, dim3(1), dim3(kTicketInts), 0, s, tickets, kTicketInts);
-    hipLaunchKernelGGL(ffn_p4_kernel<DUAL>, dim3(G), dim3(kThreads), kP4Lds, s, A, B0, B1, C, counts, offsets, E, Kd,
-                       N, rows, part, tickets, gather, gK, xrows);
+    hipLaunchKernelGGL((ffn_p4_kernel<DUAL, BT>), dim3(G), dim3(kThreads), kP4Lds, s, A, B0, B1, C, counts, offsets,
+                       E, Kd, N, rows, part, tickets, gather, gK, xrows, kb);
     if (part != nullptr)
         hipLaunchKernelGGL(ffn_split_fixup<DUAL>, dim3(G), dim3(kThreads), 0, s, part, C, counts, offsets, E, Kd, N,
                            rows, G);
@@ -1008,6 +1055,22 @@ hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows,
                            rows);
     }
     return hipGetLastError();
+}
+
+bool ffn_bt_ok(int dtype, int N, int Kd, int kb) {
+    return dtype == 1 && ffn_pipelined_ok(N, Kd) && kb % kP4BK == 0 && (Kd == kb || Kd == 2 * kb) &&
+           (size_t)kb * N * 2 < 0x80000000ull;
+}
+
+// C = A [B0^T ; B1^T] per expert, B0 and B1 given as N x kb row-major matrices
+// per expert (B1 only when Kd = 2 kb), pipelined kernel only (ffn_bt_ok()).
+hipError_t launch_ffn_bt(const void* A, const void* B0, const void* B1, int kb, int dtype, int rows, int N, int E,
+                         int Kd, const int32_t* counts, const int32_t* offsets, void* C, float* part,
+                         bool tickets_zeroed, hipStream_t s) {
+    if (!ffn_bt_ok(dtype, N, Kd, kb) || (Kd == 2 * kb) != (B1 != nullptr)) return hipErrorInvalidValue;
+    return launch_pipelined<false, true>(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B0),
+                                         static_cast<const uint16_t*>(B1), static_cast<uint16_t*>(C), counts, offsets,
+                                         E, Kd, N, rows, part, tickets_zeroed, nullptr, 1, 1, s, kb);
 }
 
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,

@@ -55,6 +55,13 @@ hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dty
 hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows, int d, int E, int n,
                            const int32_t* counts, const int32_t* offsets, void* Y, float* part,
                            bool tickets_zeroed, hipStream_t s);
+// C = A [B0^T ; B1^T] per expert (rows x N): B0 and B1 are each expert's
+// N x kb row-major matrices, B1 only when Kd = 2 kb (nullptr when Kd = kb).
+// bf16 pipelined kernel only: where ffn_bt_ok(), else hipErrorInvalidValue.
+bool ffn_bt_ok(int dtype, int N, int Kd, int kb);
+hipError_t launch_ffn_bt(const void* A, const void* B0, const void* B1, int kb, int dtype, int rows, int N, int E,
+                         int Kd, const int32_t* counts, const int32_t* offsets, void* C, float* part,
+                         bool tickets_zeroed, hipStream_t s);
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,
                       int rows, int d, int E, int n, const int32_t* counts, const int32_t* offsets,
                       void* Act, void* Y, float* part, bool tickets_zeroed, hipStream_t s,

@@ -134,7 +134,8 @@ size_t backward_ws(int T, int d, int E, int K, int n, int dtype, bool weights) {
     b += align_up(A * 4) * 2;                               // dS, unit weights
     b += align_up(A * d * s) * 2;                           // Xp (then dXp), dout rows
     b += align_up(A * n * s) * 3 + align_up(A * 2 * n * s);  // H1, H3, dA, dH
-    b += align_up((size_t)E * d * n * s) * 3;               // W2^T, [W1^T ; W3^T]
+    if (!ffn_bt_ok(dtype, n, d, d)) b += align_up((size_t)E * d * n * s);          // W2^T
+    if (!ffn_bt_ok(dtype, d, 2 * n, n)) b += align_up((size_t)E * 2 * d * n * s);  // [W1^T ; W3^T]
     b += align_up(ffn_split_bytes(dtype, 256, 128));        // split tail of the grouped GEMMs
     if (weights) b += align_up(A * n * s);                  // w * act, for dW2
     return b;
@@ -683,8 +684,11 @@ int backward_impl(const char* name, const void* X, const float* logits, const vo
     void* H3 = c.take<char>(A * n * sz);
     void* dA = c.take<char>(A * n * sz);
     void* dH = c.take<char>(A * 2 * n * sz);
-    void* W2t = c.take<char>((size_t)E * d * n * sz);
-    void* W13t = c.take<char>((size_t)E * 2 * d * n * sz);
+    // The bf16 pipelined GEMM reads W2 and W1, W3 k-contiguous as they are;
+    // the other kernels multiply by transposed copies.
+    const bool bt_da = ffn_bt_ok(dtype, n, d, d), bt_dx = ffn_bt_ok(dtype, d, 2 * n, n);
+    void* W2t = bt_da ? nullptr : c.take<char>((size_t)E * d * n * sz);
+    void* W13t = bt_dx ? nullptr : c.take<char>((size_t)E * 2 * d * n * sz);
     const size_t split_bytes = ffn_split_bytes(dtype, 256, 128);
     float* part = split_bytes ? c.take<float>(split_bytes / sizeof(float)) : nullptr;
     void* aw = weights ? c.take<char>(A * n * sz) : nullptr;
@@ -701,15 +705,18 @@ int backward_impl(const char* name, const void* X, const float* logits, const vo
     // expert-sorted rows of X and of dout
     HIPCHECK(launch_copy_rows(X, (size_t)d * sz, T, K, inv, Xp, s));
     HIPCHECK(launch_copy_rows(dout, (size_t)d * sz, T, K, inv, dY, s));
-    // transposed weights: W2^T [E, d, n]; [W1^T ; W3^T] [E, 2n, d]
-    HIPCHECK(launch_transpose_experts(W2, dtype, E, n, d, W2t, (size_t)d * n, (size_t)n, s));
-    HIPCHECK(launch_transpose_experts(W1, dtype, E, d, n, W13t, (size_t)2 * n * d, (size_t)d, s));
-    HIPCHECK(launch_transpose_experts(W3, dtype, E, d, n, static_cast<char*>(W13t) + (size_t)n * d * sz,
-                                      (size_t)2 * n * d, (size_t)d, s));
+    // transposed weights where needed: W2^T [E, d, n]; [W1^T ; W3^T] [E, 2n, d]
+    if (!bt_da) HIPCHECK(launch_transpose_experts(W2, dtype, E, n, d, W2t, (size_t)d * n, (size_t)n, s));
+    if (!bt_dx) {
+        HIPCHECK(launch_transpose_experts(W1, dtype, E, d, n, W13t, (size_t)2 * n * d, (size_t)d, s));
+        HIPCHECK(launch_transpose_experts(W3, dtype, E, d, n, static_cast<char*>(W13t) + (size_t)n * d * sz,
+                                          (size_t)2 * n * d, (size_t)d, s));
+    }
     // pre-activations H1 = Xp W1, H3 = Xp W3; dA = dY W2^T (grouped, per expert)
     HIPCHECK(launch_ffn_down(Xp, W1, dtype, (int)A, n, E, d, counts, offsets, H1, part, false, s));
     HIPCHECK(launch_ffn_down(Xp, W3, dtype, (int)A, n, E, d, counts, offsets, H3, part, false, s));
-    HIPCHECK(launch_ffn_down(dY, W2t, dtype, (int)A, n, E, d, counts, offsets, dA, part, false, s));
+    if (bt_da) HIPCHECK(launch_ffn_bt(dY, W2, nullptr, d, dtype, (int)A, n, E, d, counts, offsets, dA, part, false, s));
+    else HIPCHECK(launch_ffn_down(dY, W2t, dtype, (int)A, n, E, d, counts, offsets, dA, part, false, s));
     // SwiGLU backward and dS (and w * act for dW2)
     HIPCHECK(launch_swiglu_bwd(H1, H3, dA, w, sorted_pair, dtype, (int)A, n, dH, dS, aw, s));
     if (weights) {
@@ -719,7 +726,8 @@ int backward_impl(const char* name, const void* X, const float* logits, const vo
         HIPCHECK(launch_dw(aw, n, dY, d, 0, counts, offsets, dtype, E, n, d, (int)A, dW2, s));
     }
     // dXp = [dh1 | dh3] [W1^T ; W3^T] (overwrites Xp)
-    HIPCHECK(launch_ffn_down(dH, W13t, dtype, (int)A, d, E, 2 * n, counts, offsets, Xp, part, false, s));
+    if (bt_dx) HIPCHECK(launch_ffn_bt(dH, W1, W3, n, dtype, (int)A, d, E, 2 * n, counts, offsets, Xp, part, false, s));
+    else HIPCHECK(launch_ffn_down(dH, W13t, dtype, (int)A, d, E, 2 * n, counts, offsets, Xp, part, false, s));
     // dX[t] = sum over the token's rows, unit weights; logit gradient from dS
     HIPCHECK(launch_fill_f32(ones, A, 1.0f, s));
     HIPCHECK(launch_combine(Xp, ones, inv, dtype, T, d, K, dX, s));
