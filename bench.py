@@ -306,7 +306,7 @@ def main():
                         "us_back_to_back": c_b2b * 1e3,
                         "frac_hbm_back_to_back": comb_bytes / (c_b2b * 1e-3) / 1e9 / PEAK_HBM_GBS},
         },
-        "roofline": {"kernel": "ffn_p4_kernel<true> (moe_ffn_up: Act = SiLU(Xp W1) * (Xp W3), one launch)",
+        "roofline": {"kernel": "ffn_p4_kernel<true, false> (moe_ffn_up: Act = SiLU(Xp W1) * (Xp W3), one launch)",
                      "bound": "mfma", "achieved": round(up_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(up_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": kernel_traffic("mixtral", "ffn_up"),
