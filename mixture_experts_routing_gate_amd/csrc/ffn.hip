@@ -816,6 +816,167 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     }
 }
 
+// Expert-weight gradients on the pipelined kernel's K-loop (page [P4] section
+// 2.2: dW1 = X^T dH1, dW3 = X^T dH3, dW2 = (w act)^T dY, each over one
+// expert's rows).  For expert e with cnt = counts[e] rows starting at
+// offsets[e]: C[e] (M x N, fp32, row-major) = P_e^T Q_e, P_e the rows of P
+// (row stride ldp) and Q_e those of Q (row stride ldq, from column qoff).
+// The reduction runs over the rows, 32 per K-step, so both operands arrive
+// with K outermost: each is staged as the forward kernel stages its weights
+// (32 k-rows of two 128-column halves, XOR-swizzled by 16-byte piece) and
+// read with the transposing LDS read.  Rows past cnt read as zero: each
+// operand's buffer descriptor ends at the expert's last row, and the whole
+// offset goes in the range-checked VGPR operand.  One 256 x 256 tile per
+// work item, four waves of 128 x 128; a tile of an expert without rows
+// multiplies zeros and stores zeros.
+__global__ __launch_bounds__(kThreads, 1) void dw_p4_kernel(
+    const uint16_t* __restrict__ P, int ldp, const uint16_t* __restrict__ Q, int ldq, int qoff,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int E, int M, int N,
+    float* __restrict__ C) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = uniform(tid / kWave);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int g16 = lane >> 4, s16 = lane & 15;
+    // Fragment reads: column c of half h of an operand staged at X (P at 0,
+    // Q at 16K) sits at X + h*8K + k*256 + (((c/8) ^ 4*(k%4)) * 16) + (c%8)*2.
+    const int b_x = (s16 >> 2) << 2;
+    const int b_c = (g16 & 1) * 2 + ((s16 & 3) >> 1);
+    const int rd_lane = ((g16 >> 1) * 8 + (s16 >> 2)) * 256 + (s16 & 1) * 8;
+    int p_rd[4], q_rd[4];
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int piece = ((((i * 32) >> 3) ^ b_x) + b_c) << 4;
+        p_rd[i] = rd_lane + wm * 8192 + piece;
+        q_rd[i] = 16384 + rd_lane + wn * 8192 + piece;
+    }
+    const uint32_t lds_base = uniform((int)(uint32_t)(uintptr_t)(lds_void*)smem);
+    const int G = gridDim.x;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per_xcd = G >> 3;
+    const int MT = M / 256, NT = N / 256;
+    const int total = E * MT * NT;
+    // Work item j of this XCD: round j / per_xcd, slot j % per_xcd, as in the
+    // forward kernel, so that an XCD's workgroups share P panels in L2.
+    for (int j = slot;; j += per_xcd) {
+        const int round = j / per_xcd, jslot = j - round * per_xcd;
+        const int tile = round * G + xcd * per_xcd + jslot;
+        if (tile >= total) break;
+        const int e = tile / (MT * NT);
+        const int rem = tile - e * MT * NT;
+        const int m0 = (rem / NT) * 256, n0 = (rem - (rem / NT) * NT) * 256;
+        const int cnt = uniform(counts[e]), r0 = uniform(offsets[e]);
+        const int ksn = max(4, (cnt + 127) / 128 * 4);  // a multiple of 4 K-steps
+        const rsrc_t rp = make_rsrc(P + (size_t)r0 * ldp, (uint32_t)cnt * (uint32_t)ldp * 2u);
+        const rsrc_t rq = make_rsrc(Q + (size_t)r0 * ldq + qoff, (uint32_t)cnt * (uint32_t)ldq * 2u);
+        uint32_t p_vo[4], q_vo[4];
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kr = (wave & 1) * 16 + i * 4 + (lane >> 4);
+            const int col = (wave >> 1) * 128 + (((lane & 15) ^ ((kr & 3) << 2)) << 3);
+            p_vo[i] = ((uint32_t)kr * (uint32_t)ldp + (uint32_t)(m0 + col)) * 2u;
+            q_vo[i] = ((uint32_t)kr * (uint32_t)ldq + (uint32_t)(n0 + col)) * 2u;
+        }
+        const uint32_t p_step = 64u * (uint32_t)ldp, q_step = 64u * (uint32_t)ldq;
+        auto issue_one = [&](int kt, int soff, int i) {
+            const uint32_t dst = lds_base + soff + wave * 4096;
+            if (i < 4) dma16(rp, dst + i * 1024, p_vo[i] + (uint32_t)kt * p_step, 0);
+            else dma16(rq, dst + 16384 + (i - 4) * 1024, q_vo[i - 4] + (uint32_t)kt * q_step, 0);
+        };
+        auto issue = [&](int kt, int soff) {
+            #pragma unroll
+            for (int i = 0; i < 8; ++i) issue_one(kt, soff, i);
+        };
+        f32x16 acc[4][4];
+        #pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+            #pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                #pragma unroll
+                for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+        bf16x8 af[2][4], bfr[2][4];
+        auto load_frags = [&](int soff, int ks, int buf) {
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const char* pa = smem + soff + p_rd[i] + ks * 16 * 256;
+                af[buf][i] = __builtin_shufflevector(lds_read_tr(pa), lds_read_tr(pa + 4 * 256), 0, 1, 2, 3, 4, 5, 6, 7);
+                const char* pb = smem + soff + q_rd[i] + ks * 16 * 256;
+                bfr[buf][i] = __builtin_shufflevector(lds_read_tr(pb), lds_read_tr(pb + 4 * 256), 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        };
+        auto mfma = [&](int buf, int lo, int hi) {
+            #pragma unroll
+            for (int q = lo; q < hi; ++q) {
+                const int mi = q >> 2, ni = q & 3;
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
+            }
+        };
+        // The forward kernel's pipeline: four K-steps in flight, a step's
+        // stage refilled with step + 4 one DMA per MFMA, fragments of the next
+        // sub-step read under the current one's MFMAs.
+        issue(0, 0);
+        issue(1, kP4Stage);
+        issue(2, 2 * kP4Stage);
+        issue(3, 3 * kP4Stage);
+        __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
+        __syncthreads();
+        load_frags(0, 0, 0);
+        int s_cur = 0;
+        for (int kt0 = 0; kt0 < ksn; kt0 += 4) {
+            #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int kt = kt0 + u;
+                const int s_nxt = s_cur == (kP4Stages - 1) * kP4Stage ? 0 : s_cur + kP4Stage;
+                const int s_old = s_cur == 0 ? (kP4Stages - 1) * kP4Stage : s_cur - kP4Stage;
+                __builtin_amdgcn_sched_barrier(0);
+                __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+                __syncthreads();
+                const int kn = min(kt + 4, ksn - 1);
+                #pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    issue_one(kn, s_old, i);
+                    mfma(0, i, i + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                load_frags(s_cur, 1, 1);
+                mfma(0, 8, 16);
+                #pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                load_frags(s_nxt, 0, 0);
+                mfma(1, 0, 16);
+                #pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                s_cur = s_nxt;
+            }
+        }
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // Every wave is done reading the stages before the next tile refills them.
+        __syncthreads();
+        // acc[mi][ni] element q*4 + jj of lane l: row wm*128 + mi*32 + l%32,
+        // column wn*128 + ni*32 + q*8 + (l/32)*4 + jj of the tile.
+        float* cbase = C + ((size_t)e * M + m0 + wm * 128 + l32) * N + n0 + wn * 128 + lh * 4;
+        #pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+            #pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                #pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x16& av = acc[mi][ni];
+                    *reinterpret_cast<f32x4*>(cbase + (size_t)(mi * 32) * N + ni * 32 + q * 8) =
+                        f32x4{av[q * 4], av[q * 4 + 1], av[q * 4 + 2], av[q * 4 + 3]};
+                }
+    }
+}
+
 // Finishes the split tiles of the pipelined kernel launched with G workgroups:
 // adds each tile's S partial slots in slot order and runs the epilogue.
 template <bool DUAL>
@@ -1054,6 +1215,23 @@ hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows,
                            static_cast<const float*>(nullptr), static_cast<float*>(Y), counts, offsets, E, n, d,
                            rows);
     }
+    return hipGetLastError();
+}
+
+bool dw_p4_ok(int dtype, int M, int N, int rows, int ldp, int ldq) {
+    const long long ld = ldp > ldq ? ldp : ldq;
+    return dtype == 1 && M % 256 == 0 && N % 256 == 0 && ldp % 8 == 0 && ldq % 8 == 0 &&
+           ((long long)rows + 128) * ld * 2 < (1LL << 31);
+}
+
+hipError_t launch_dw_p4(const void* P, int ldp, const void* Q, int ldq, int qoff, const int32_t* counts,
+                        const int32_t* offsets, int E, int M, int N, int rows, float* dW, hipStream_t s) {
+    if (!dw_p4_ok(1, M, N, rows, ldp, ldq) || qoff % 8 != 0 || qoff + N > ldq) return hipErrorInvalidValue;
+    const hipError_t aerr =
+        hipFuncSetAttribute((const void*)dw_p4_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
+    if (aerr != hipSuccess) return aerr;
+    hipLaunchKernelGGL(dw_p4_kernel, dim3(ffn_grid()), dim3(kThreads), kP4Lds, s, static_cast<const uint16_t*>(P),
+                       ldp, static_cast<const uint16_t*>(Q), ldq, qoff, counts, offsets, E, M, N, dW);
     return hipGetLastError();
 }
 

@@ -23,6 +23,9 @@ CASES = [
     synth.MoEConfig("bf16_e256_k8", T=600, d=256, E=256, K=8, n=128, logits="bias", bias_var=1.5),
     synth.MoEConfig("t1", T=1, d=128, E=16, K=4, n=128),           # one token: 12 experts without rows
     synth.MoEConfig("dense_e1", T=130, d=128, E=1, K=1, n=256),    # one expert, weight 1: zero logit gradient
+    # 128 rows over 32 experts: experts without rows, and every expert's rows
+    # end inside the first K-step block of the pipelined weight-gradient kernel
+    synth.MoEConfig("sparse_e32", T=64, d=256, E=32, K=2, n=256, logits="bias", bias_var=1.0),
 ]
 
 
@@ -117,6 +120,12 @@ def test_backward_weight_gradients_match_oracle(cfg):
         rel, _ = check_close(full[k], ref[k], cfg.dtype, k)
         msg.append(f"{k} rel L2 {rel:.2e}")
     print(f"[bwd-w] {cfg.name}: " + ", ".join(msg), flush=True)
+    # experts without rows: exactly zero gradients
+    idx, _, _, _ = oracle.route(to_np(inp["logits"]), cfg.K)
+    empty = np.nonzero(np.bincount(idx.reshape(-1), minlength=cfg.E) == 0)[0]
+    for e in empty.tolist():
+        for k in ("dW1", "dW3", "dW2"):
+            assert torch.count_nonzero(full[k][e]).item() == 0, (k, e)
 
 
 @pytest.mark.slow
