@@ -311,9 +311,10 @@ int moe_forward_tr(const void* X, const float* logits, const void* W1, const voi
  *      bf16 intermediates (h1, h3, dA, dh) are stored rounded to bf16; the
  *      sums are fp32.
  * Workspace: moe_backward_data_workspace_bytes(T,d,E,K,n,dtype) bytes, 16-byte
- *      aligned; it holds the routing, expert-sorted copies of X and dout, the
- *      intermediates and transposed copies of the weights, all rewritten on
- *      every call.  The caller owns every buffer.  Errors as moe_forward:
+ *      aligned; it holds the routing, expert-sorted copies of X and dout and
+ *      the intermediates, all rewritten on every call.  For fp32, or for bf16
+ *      with n or d not a multiple of 256, it also holds transposed copies of
+ *      the weights (the bf16 GEMM otherwise reads them as stored).  The caller owns every buffer.  Errors as moe_forward:
  *      nothing is launched when an argument is rejected.
  */
 size_t moe_backward_data_workspace_bytes(int T, int d, int E, int K, int n, int dtype);
