@@ -1125,8 +1125,11 @@ __global__ __launch_bounds__(kThreads) void ffn_f32_kernel(const float* __restri
 }  // namespace
 
 // The pipelined bf16 kernel needs 256-wide down-projection tiles and K in
-// multiples of 128 for both GEMMs.
-static bool ffn_pipelined_ok(int d, int n) { return d % 256 == 0 && n % 128 == 0; }
+// multiples of 128 for both GEMMs, and addresses one expert's weight matrix
+// with 32-bit buffer offsets below the descriptor's 2^31-byte range.
+static bool ffn_pipelined_ok(int d, int n) {
+    return d % 256 == 0 && n % 128 == 0 && (long long)d * n * 2 < (1LL << 31);
+}
 
 // Gathered loads address X with 32-bit byte offsets.
 bool ffn_gather_ok(int dtype, int T, int d, int n) {
