@@ -404,6 +404,7 @@ def backward_data(c, g, moe, torch, dev, calls=3):
     flops = 10.0 * c.T * c.K * c.d * c.n
     res = {"what": "dX, dlogits and dw (no weight gradients)", "ms_per_call": round(ms, 4),
            "TFLOPS": flops / (ms * 1e-3) / 1e12, "flops_per_call": flops}
+    res["frac_of_bf16_peak"] = res["TFLOPS"] / PEAK_BF16_TFLOPS
     del ws
     # with the expert-weight gradients: 6*d*n more FLOPs per assignment
     wsw = torch.empty(lib.moe_backward_workspace_bytes(c.T, c.d, c.E, c.K, c.n, 1), dtype=torch.uint8, device=dev)
@@ -415,6 +416,7 @@ def backward_data(c, g, moe, torch, dev, calls=3):
     flops_w = 16.0 * c.T * c.K * c.d * c.n
     res["with_weight_gradients"] = {"ms_per_call": round(ms_w, 4), "TFLOPS": flops_w / (ms_w * 1e-3) / 1e12,
                                     "flops_per_call": flops_w}
+    res["with_weight_gradients"]["frac_of_bf16_peak"] = res["with_weight_gradients"]["TFLOPS"] / PEAK_BF16_TFLOPS
     del wsw, dout
     torch.cuda.empty_cache()
     return res
