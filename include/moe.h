@@ -215,7 +215,10 @@ int moe_combine(const void* Y, const float* topk_w, const int32_t* inv, int dtyp
  *      topk_idx [T,K], topk_w [T,K], counts [E], offsets [E+1],
  *      sorted_pair [T*K], inv [T*K].
  * Workspace: moe_forward_workspace_bytes(T,d,E,K,n,dtype) bytes; it also holds
- *      Xp [T*K,d], Act [T*K,n] and Y [T*K,d].
+ *      Act [T*K,n] and Y [T*K,d], and Xp [T*K,d] only where the SwiGLU GEMM
+ *      cannot read the X rows in place (bf16 with d % 256 == 0, n % 128 == 0,
+ *      d*n*2 < 2^31 and T*d*2 < 2^31 gather them; other sizes and fp32 take
+ *      the copy).
  */
 int moe_forward(const void* X, const float* logits, const void* W1, const void* W3,
                 const void* W2, int dtype, int T, int d, int E, int K, int n, void* out,

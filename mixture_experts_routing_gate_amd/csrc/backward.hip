@@ -371,8 +371,7 @@ hipError_t launch_swiglu_bwd(const void* H1, const void* H3, const void* dA, con
 
 hipError_t launch_dw(const void* P, int ldp, const void* Q, int ldq, int qoff, const int32_t* counts,
                      const int32_t* offsets, int dtype, int E, int M, int N, int rows, float* dW, hipStream_t s) {
-    // (the pipelined kernel numbers its 256 x 256 tiles with an int)
-    if (dw_p4_ok(dtype, M, N, rows, ldp, ldq) && (long long)E * (M / 256) * (N / 256) < (1LL << 31))
+    if (dw_p4_ok(dtype, E, M, N, rows, ldp, ldq))
         return launch_dw_p4(P, ldp, Q, ldq, qoff, counts, offsets, E, M, N, rows, dW, s);
     if (dtype == 1) {
         const unsigned tiles = (unsigned)((size_t)E * (M / 128) * (N / 128));

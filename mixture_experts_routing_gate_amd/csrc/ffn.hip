@@ -826,12 +826,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
 // (32 k-rows of two 128-column halves, XOR-swizzled by 16-byte piece) and
 // read with the transposing LDS read.  Rows past cnt read as zero: each
 // operand's buffer descriptor ends at the expert's last row, and the whole
-// offset goes in the range-checked VGPR operand.  One 256 x 256 tile per
-// work item, four waves of 128 x 128; a tile of an expert without rows
-// multiplies zeros and stores zeros.
+// offset goes in the range-checked VGPR operand.  An expert's rows are
+// clamped to the `rows` rows the operands hold, whatever counts and offsets
+// say.  One 256 x 256 tile per work item, four waves of 128 x 128; a tile of
+// an expert without rows skips the K-loop and stores zeros.
 __global__ __launch_bounds__(kThreads, 1) void dw_p4_kernel(
     const uint16_t* __restrict__ P, int ldp, const uint16_t* __restrict__ Q, int ldq, int qoff,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int E, int M, int N,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int E, int M, int N, int rows,
     float* __restrict__ C) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const int tid = threadIdx.x;
@@ -867,8 +868,9 @@ __global__ __launch_bounds__(kThreads, 1) void dw_p4_kernel(
         const int e = tile / (MT * NT);
         const int rem = tile - e * MT * NT;
         const int m0 = (rem / NT) * 256, n0 = (rem - (rem / NT) * NT) * 256;
-        const int cnt = uniform(counts[e]), r0 = uniform(offsets[e]);
-        const int ksn = max(4, (cnt + 127) / 128 * 4);  // a multiple of 4 K-steps
+        const int r0 = min(max(uniform(offsets[e]), 0), rows);
+        const int cnt = min(max(uniform(counts[e]), 0), rows - r0);
+        const int ksn = (cnt + 127) / 128 * 4;  // a multiple of 4 K-steps; 0 for an expert without rows
         const rsrc_t rp = make_rsrc(P + (size_t)r0 * ldp, (uint32_t)cnt * (uint32_t)ldp * 2u);
         const rsrc_t rq = make_rsrc(Q + (size_t)r0 * ldq + qoff, (uint32_t)cnt * (uint32_t)ldq * 2u);
         uint32_t p_vo[4], q_vo[4];
@@ -896,6 +898,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_p4_kernel(
             for (int ni = 0; ni < 4; ++ni)
                 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+        if (ksn > 0) {  // (uniform over the workgroup: one expert per tile)
         bf16x8 af[2][4], bfr[2][4];
         auto load_frags = [&](int soff, int ks, int buf) {
             #pragma unroll
@@ -961,6 +964,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_p4_kernel(
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         // Every wave is done reading the stages before the next tile refills them.
         __syncthreads();
+        }
         // acc[mi][ni] element q*4 + jj of lane l: row wm*128 + mi*32 + l%32,
         // column wn*128 + ni*32 + q*8 + (l/32)*4 + jj of the tile.
         float* cbase = C + ((size_t)e * M + m0 + wm * 128 + l32) * N + n0 + wn * 128 + lh * 4;
@@ -1221,20 +1225,24 @@ hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows,
     return hipGetLastError();
 }
 
-bool dw_p4_ok(int dtype, int M, int N, int rows, int ldp, int ldq) {
+// The kernel numbers its 256 x 256 tiles with an int, and a workgroup's last
+// tile index (before it finds no more work) reaches past the tile count by up
+// to one grid.
+bool dw_p4_ok(int dtype, int E, int M, int N, int rows, int ldp, int ldq) {
     const long long ld = ldp > ldq ? ldp : ldq;
     return dtype == 1 && M % 256 == 0 && N % 256 == 0 && ldp % 8 == 0 && ldq % 8 == 0 &&
-           ((long long)rows + 128) * ld * 2 < (1LL << 31);
+           ((long long)rows + 128) * ld * 2 < (1LL << 31) &&
+           (long long)E * (M / 256) * (N / 256) + ffn_grid() < (1LL << 31);
 }
 
 hipError_t launch_dw_p4(const void* P, int ldp, const void* Q, int ldq, int qoff, const int32_t* counts,
                         const int32_t* offsets, int E, int M, int N, int rows, float* dW, hipStream_t s) {
-    if (!dw_p4_ok(1, M, N, rows, ldp, ldq) || qoff % 8 != 0 || qoff + N > ldq) return hipErrorInvalidValue;
+    if (!dw_p4_ok(1, E, M, N, rows, ldp, ldq) || qoff % 8 != 0 || qoff + N > ldq) return hipErrorInvalidValue;
     const hipError_t aerr =
         hipFuncSetAttribute((const void*)dw_p4_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
     if (aerr != hipSuccess) return aerr;
     hipLaunchKernelGGL(dw_p4_kernel, dim3(ffn_grid()), dim3(kThreads), kP4Lds, s, static_cast<const uint16_t*>(P),
-                       ldp, static_cast<const uint16_t*>(Q), ldq, qoff, counts, offsets, E, M, N, dW);
+                       ldp, static_cast<const uint16_t*>(Q), ldq, qoff, counts, offsets, E, M, N, rows, dW);
     return hipGetLastError();
 }
 

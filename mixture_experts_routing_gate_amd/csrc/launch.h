@@ -65,7 +65,7 @@ hipError_t launch_ffn_bt(const void* A, const void* B0, const void* B1, int kb, 
 // Expert-weight gradients on the pipelined kernel: dW[e] (M x N fp32) = sum over
 // e's rows r of P[r, 0:M]^T Q[r, qoff:qoff+N]; bf16, where dw_p4_ok(), else
 // hipErrorInvalidValue (rows = the total row count, for the offset range).
-bool dw_p4_ok(int dtype, int M, int N, int rows, int ldp, int ldq);
+bool dw_p4_ok(int dtype, int E, int M, int N, int rows, int ldp, int ldq);
 hipError_t launch_dw_p4(const void* P, int ldp, const void* Q, int ldq, int qoff, const int32_t* counts,
                         const int32_t* offsets, int E, int M, int N, int rows, float* dW, hipStream_t s);
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,

@@ -117,7 +117,8 @@ size_t forward_ws(int T, int d, int E, int K, int n, int dtype) {
     b += align_up(A * 4) * 2;                          // topk_idx, topk_w
     b += align_up(E * 4) + align_up((E + 1) * 4);      // counts, offsets
     b += align_up(A * 4) * 2;                          // sorted_pair, inv
-    b += align_up(A * d * s) * 2 + align_up(A * n * s);  // Xp, Y, Act
+    // Xp only where the SwiGLU GEMM cannot gather the X rows itself
+    b += (ffn_gather_ok(dtype, T, d, n) ? 0 : align_up(A * d * s)) + align_up(A * d * s) + align_up(A * n * s);  // Xp, Y, Act
     b += align_up(ffn_split_bytes(dtype, d, n));        // split tail of the grouped GEMMs
     return b;
 }
@@ -449,7 +450,8 @@ int moe_forward(const void* X, const float* logits, const void* W1, const void* 
     int32_t* ws_off = c.take<int32_t>(E + 1);
     int32_t* ws_sp = c.take<int32_t>(A);
     int32_t* ws_inv = c.take<int32_t>(A);
-    void* Xp = c.take<char>(A * d * sz);
+    const bool gather = ffn_gather_ok(dtype, T, d, n);
+    void* Xp = gather ? nullptr : c.take<char>(A * d * sz);
     void* Yb = c.take<char>(A * d * sz);
     void* Act = c.take<char>(A * n * sz);
     const size_t split_bytes = ffn_split_bytes(dtype, d, n);
@@ -471,7 +473,7 @@ int moe_forward(const void* X, const float* logits, const void* W1, const void* 
         HIPCHECK(launch_scan(blk, B, E, counts, offsets, blkbase, s, tickets, nt));
         HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s));
     }
-    if (ffn_gather_ok(dtype, T, d, n)) {
+    if (gather) {
         // no permuted copy of X: the SwiGLU GEMM gathers its rows through sorted_pair
         HIPCHECK(launch_ffn(X, W1, W3, W2, dtype, (int)A, d, E, n, counts, offsets, Act, Yb, part, true, s,
                             sorted_pair, K, T));

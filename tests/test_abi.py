@@ -38,9 +38,15 @@ def test_workspace_sizes(lib):
     assert lib.moe_route_workspace_bytes(0, 8, 2) == 0
     assert lib.moe_route_workspace_bytes(16, 8, 9) == 0
     assert lib.moe_permute_workspace_bytes(8192, 8, 2) >= 2 * 32 * 8 * 4
-    # forward holds Xp, Y and Act at least
+    # forward holds Y and Act at least; Xp only where the SwiGLU GEMM cannot gather X rows
+    # (bf16 with d % 256 == 0 gathers; d % 256 == 128 and fp32 take the permuted copy)
     T, d, E, K, n = 8192, 4096, 8, 2, 14336
-    assert lib.moe_forward_workspace_bytes(T, d, E, K, n, moe.MOE_BF16) >= T * K * (2 * d + n) * 2
+    A = T * K
+    gathered = lib.moe_forward_workspace_bytes(T, d, E, K, n, moe.MOE_BF16)
+    assert A * (d + n) * 2 <= gathered < A * (2 * d + n) * 2
+    copied = lib.moe_forward_workspace_bytes(T, d + 128, E, K, n, moe.MOE_BF16)
+    assert copied >= A * (2 * (d + 128) + n) * 2
+    assert lib.moe_forward_workspace_bytes(256, 128, 8, 2, 256, moe.MOE_F32) >= 512 * (2 * 128 + 256) * 4
     assert lib.moe_forward_workspace_bytes(T, 100, E, K, n, moe.MOE_BF16) == 0  # d not a multiple of 128
     assert lib.moe_forward_workspace_bytes(T, d, E, K, n, 7) == 0               # unknown dtype
 
