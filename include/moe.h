@@ -123,6 +123,26 @@ int moe_route(const float* logits, int T, int E, int K, int32_t* topk_idx, float
               int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_route_noalloc -- moe_route for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same semantics, arguments (less the workspace), kernels
+ * and results as moe_route.
+ * Scratch: the per-chunk expert counts live in a static device array of
+ *   MOE_ROUTE_NOALLOC_SCRATCH_BYTES (1 MiB) that each GPU the library runs on
+ *   holds until the process ends; its address is looked up on the first call
+ *   on a device.  No call allocates or frees memory.  A chunk is 256 tokens
+ *   (1024 when T > 65536), and ceil(T / chunk) * E * 4 bytes must fit the
+ *   scratch (e.g. T = 262144 with E = 256, or T = 2^20 with E = 256), else
+ *   MOE_ERR_UNSUPPORTED and nothing is launched.
+ * Concurrency: every call on a GPU shares that GPU's scratch, so calls that
+ *   overlap on one GPU (on different streams, or from different threads on
+ *   different streams) race.  Calls ordered on one stream are safe.
+ */
+#define MOE_ROUTE_NOALLOC_SCRATCH_BYTES (1u << 20)
+int moe_route_noalloc(const float* logits, int T, int E, int K, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                      int32_t* offsets, void* stream);
+
+/*
  * moe_permute -- step 3: token rows into expert-contiguous order.
  *   [P2] section 6: each token row is repeated once per selected expert;
  *   [P4] section 1 (gather) and section 2.2 (intermediates grouped by expert).

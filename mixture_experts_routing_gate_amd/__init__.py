@@ -52,6 +52,7 @@ def load_library() -> ctypes.CDLL:
         "moe_router_workspace_bytes": ([I, I, I], Z),
         "moe_router": ([P, I, I, I, I, P, P, P, P, Z, P], I),
         "moe_route": ([P, I, I, I, P, P, P, P, P, Z, P], I),
+        "moe_route_noalloc": ([P, I, I, I, P, P, P, P, P], I),
         "moe_permute": ([P, I, I, I, I, I, P, P, P, P, P, Z, P], I),
         "moe_grouped_ffn": ([P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, Z, P], I),
         "moe_ffn_up": ([P, P, P, I, I, I, I, I, I, P, P, P, P, Z, P], I),
@@ -157,6 +158,22 @@ def moe_route(logits: torch.Tensor, K: int, out=None, ws: torch.Tensor | None = 
     _check(lib.moe_route(_dev(logits, "logits", torch.float32), T, E, K, idx.data_ptr(), w.data_ptr(),
                          counts.data_ptr(), offsets.data_ptr(), ws.data_ptr(), nws, _stream(dev)), "moe_route")
     return idx, w, counts, offsets
+
+
+def moe_route_noalloc(logits: torch.Tensor, K: int, out):
+    """Steps 1-2 with the library's static scratch instead of a workspace.  `out` is the
+    (topk_idx [T,K] i32, topk_w [T,K] f32, counts [E] i32, offsets [E+1] i32) tuple written into."""
+    lib = load_library()
+    T, E = logits.shape
+    idx, w, counts, offsets = out
+    for t, shape, dt, name in ((idx, (T, K), torch.int32, "topk_idx"), (w, (T, K), torch.float32, "topk_w"),
+                               (counts, (E,), torch.int32, "counts"), (offsets, (E + 1,), torch.int32, "offsets")):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        _dev(t, name, dt)
+    _check(lib.moe_route_noalloc(_dev(logits, "logits", torch.float32), T, E, K, idx.data_ptr(), w.data_ptr(),
+                                 counts.data_ptr(), offsets.data_ptr(), _stream(logits.device)), "moe_route_noalloc")
+    return out
 
 
 def moe_permute(X: torch.Tensor, topk_idx: torch.Tensor, E: int):

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 
@@ -192,6 +193,45 @@ size_t forward_tr_ws(int T, int d, int E, int K, int n, int M, int dtype) {
 
 std::atomic<int> g_cu_count[64];
 
+// Scratch of moe_route_noalloc: the gate's per-chunk expert counts, in a
+// file-scope device array that every GPU the library runs on holds until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it only names a stand-in, not device memory): the array's address on
+// each device is looked up once, with that device current, and kept here.
+constexpr size_t kNoAllocScratchInts = MOE_ROUTE_NOALLOC_SCRATCH_BYTES / sizeof(int32_t);
+__device__ __align__(256) int32_t scratch[kNoAllocScratchInts];
+
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's address of `scratch`, looked up on the first call on the
+// device; MOE_OK or an error status.
+int noalloc_scratch(int32_t** out) {
+    int dev = -1;
+    const hipError_t derr = hipGetDevice(&dev);
+    if (derr != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(derr));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table covers", dev,
+                    kMaxDevices);
+    int32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            void* addr = nullptr;
+            const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || addr == nullptr)
+                return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                            hipGetErrorString(e));
+            p = static_cast<int32_t*>(addr);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MOE_OK;
+}
+
 }  // namespace
 
 int device_cu_count() {
@@ -270,6 +310,29 @@ int moe_route(const float* logits, int T, int E, int K, int32_t* topk_idx, float
     hipStream_t s = static_cast<hipStream_t>(stream);
     Carver c(ws);
     int32_t* blk = c.take<int32_t>((size_t)num_chunks(T) * E);
+    HIPCHECK(launch_gate(logits, T, E, K, topk_idx, topk_w, blk, s));
+    HIPCHECK(launch_scan(blk, num_chunks(T), E, counts, offsets, nullptr, s));
+    return MOE_OK;
+}
+
+int moe_route_noalloc(const float* logits, int T, int E, int K, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                      int32_t* offsets, void* stream) {
+    CHECK(check_tek(T, E, K));
+    NONNULL(logits);
+    NONNULL(topk_idx);
+    NONNULL(topk_w);
+    NONNULL(counts);
+    NONNULL(offsets);
+    const size_t need = (size_t)num_chunks(T) * E;
+    if (need > kNoAllocScratchInts)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "moe_route_noalloc: %d chunks of %d tokens x E=%d need %zu bytes of scratch, above its %zu",
+                    num_chunks(T), chunk_tokens(T), E, need * sizeof(int32_t), (size_t)MOE_ROUTE_NOALLOC_SCRATCH_BYTES);
+    int32_t* blk = nullptr;
+    CHECK(noalloc_scratch(&blk));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // The gate writes every chunk's E counts before the scan reads them, so
+    // what an earlier call left in the scratch is never read.
     HIPCHECK(launch_gate(logits, T, E, K, topk_idx, topk_w, blk, s));
     HIPCHECK(launch_scan(blk, num_chunks(T), E, counts, offsets, nullptr, s));
     return MOE_OK;
