@@ -211,6 +211,7 @@ def main():
     rt_ms, _ = event_time_ms(torch, lambda: moe.moe_router(g["X"], Wr, rb, ws=rws), 20)
     rt_b2b = b2b_time_ms(torch, lambda: moe.moe_router(g["X"], Wr, rb, ws=rws))
     router_bytes = T * d * 2 + d * E * 4 + T * E * 4
+    layer_x = layer_from_x(cfg, g, Wr, rb, moe, torch, dev, args, r_ms, rt_ms)
     p_b2b = b2b_time_ms(torch, lambda: moe.moe_permute(g["X"], idx, E))
     c_b2b = b2b_time_ms(torch, lambda: moe.moe_combine(Y, w, inv))
     s = 2  # bf16 bytes
@@ -289,10 +290,12 @@ def main():
                    "load": load_stats(counts_h, A, E)},
         "gate": gate,
         "gate_small": gate_small,
+        "layer_from_x": layer_x,
         "hbm_copy": hbm_copy,
         "steps_us": {
             "router": {"us": rt_ms * 1e3, "us_back_to_back": rt_b2b * 1e3,
                        "frac_hbm_back_to_back": router_bytes / (rt_b2b * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "route_x": layer_x.pop("route_x"),
             "route": {"us": r_ms * 1e3, "GB/s": route_bytes / (r_ms * 1e-3) / 1e9},
             "permute": {"us": p_ms * 1e3, "GB/s": perm_bytes / (p_ms * 1e-3) / 1e9,
                         "frac_hbm": perm_bytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -324,6 +327,42 @@ def main():
         out["other_workloads"] = {name: other_workload(name, moe, synth, torch, np, dev)
                                   for name in ("dsv3", "fine")}
     print(json.dumps(out), flush=True)
+
+
+def layer_from_x(cfg, g, Wr, rb, moe, torch, dev, args, route_ms, router_ms):
+    """The layer from the tokens and the router weights (moe_forward_x: the router
+    projection fused with the gate, no logits round trip), per step as the headline
+    is timed, and moe_route_x alone beside moe_router + moe_route."""
+    T, d, E, K, n = cfg.T, cfg.d, cfg.E, cfg.K, cfg.n
+    xplan = moe.ForwardXPlan(T, d, E, K, n, cfg.torch_dtype, dev)
+
+    def step_x():
+        xplan(g["X"], Wr, rb, g["W1"], g["W3"], g["W2"])
+
+    for _ in range(args.warmup):
+        step_x()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_x()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    lib = moe.load_library()
+    ws = torch.empty(lib.moe_route_x_workspace_bytes(T, d, E, K, 1), dtype=torch.uint8, device=dev)
+    out = moe.moe_route_x(g["X"], Wr, rb, K, want_logits=False, ws=ws)
+    rx_ms, _ = event_time_ms(torch, lambda: moe.moe_route_x(g["X"], Wr, rb, K, ws=ws, out=out), 20)
+    rx_b2b = b2b_time_ms(torch, lambda: moe.moe_route_x(g["X"], Wr, rb, K, ws=ws, out=out))
+    fused = bool(E <= 64 and d % 256 == 0)
+    res = {"what": "moe_forward_x: the layer from X, Wr (and the bias) -- the router projection "
+                   + ("fused with the gate (no logits round trip)" if fused else "then the gate"),
+           "ms_per_step": round(ms, 4), "TFLOPS": 6.0 * T * K * d * n / (ms * 1e-3) / 1e12,
+           "route_x": {"us": rx_ms * 1e3, "us_back_to_back": rx_b2b * 1e3, "fused": fused,
+                       "router_plus_route_us": (router_ms + route_ms) * 1e3,
+                       "note": "moe_route_x (split of Wr + the fused router-gate kernel + the scan) against "
+                               "moe_router then moe_route, single calls"}}
+    del xplan, ws, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def other_workload(name, moe, synth, torch, np, dev, steps=5):

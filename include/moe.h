@@ -246,6 +246,52 @@ int moe_forward(const void* X, const float* logits, const void* W1, const void* 
                 int32_t* sorted_pair, int32_t* inv, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_route_x -- the router projection and steps 1-2 from the tokens: logits
+ * = X Wr (+ bias) as moe_router computes them, then the gate, histogram and
+ * offsets of moe_route on those logits.
+ *   [P1] section 2.1: one fused pass from the logit computation through the
+ *   softmax to the top-k; [P2] section 6: the gate logits are a linear layer;
+ *   [P4] section 1: the K best of E scores per token.
+ * Fused where bf16 X, d % 256 == 0 and E <= 64: one kernel computes the
+ *   logits of a 32-token tile on MFMA and runs the gate on them from LDS, so
+ *   the logits never travel through memory (unless `logits` asks for them).
+ *   Elsewhere the router and the gate run one after the other, through the
+ *   caller's `logits` or workspace room.
+ * In:  X [T,d] (dtype), Wr [d,E] fp32, bias [E] fp32 or NULL.
+ * Out: topk_idx [T,K], topk_w [T,K], counts [E], offsets [E+1] as moe_route;
+ *      logits [T,E] fp32 (optional, NULL = not written) equal, bit for bit,
+ *      to what moe_router writes for the same arguments, and the routing is
+ *      that of moe_route on them (weights within 1e-5 relative).
+ * Workspace: moe_route_x_workspace_bytes(T,d,E,K,dtype) bytes (the split
+ *      weights and the expert counts, rewritten on every call).
+ * Sizes: those of moe_route and moe_router.
+ */
+size_t moe_route_x_workspace_bytes(int T, int d, int E, int K, int dtype);
+int moe_route_x(const void* X, int dtype, int T, int d, int E, int K, const float* Wr, const float* bias,
+                float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, void* ws,
+                size_t ws_bytes, void* stream);
+
+/*
+ * moe_forward_x -- the whole layer from the tokens and the router weights:
+ * moe_route_x in place of moe_route, then moe_forward's steps 3-5.
+ *   [P1] section 2.1 (the fused gate starts from the logit computation) and
+ *   [P4] section 1 (the layer).
+ * In:  X [T,d], Wr [d,E] fp32, bias [E] fp32 or NULL, W1, W3 [E,d,n],
+ *      W2 [E,n,d].
+ * Out: out [T,d]; the results of moe_forward given the logits moe_router
+ *      writes for X, Wr and bias.
+ * Optional outputs (may be NULL): logits [T,E] as moe_route_x, and those of
+ *      moe_forward.
+ * Workspace: moe_forward_x_workspace_bytes(T,d,E,K,n,dtype) bytes.
+ * Sizes and errors: those of moe_forward and moe_router.
+ */
+size_t moe_forward_x_workspace_bytes(int T, int d, int E, int K, int n, int dtype);
+int moe_forward_x(const void* X, const float* Wr, const float* bias, const void* W1, const void* W3, const void* W2,
+                  int dtype, int T, int d, int E, int K, int n, void* out, float* logits, int32_t* topk_idx,
+                  float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* inv, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/*
  * Token Rounding -- the routing variant of [P4] section 3.  Section 3.1: the
  * per-expert counts of top-K routing are rounded to whole tiles of M rows and
  * a second sort by score picks which tokens each expert drops or takes on.

@@ -59,6 +59,10 @@ def load_library() -> ctypes.CDLL:
         "moe_ffn_down": ([P, P, I, I, I, I, I, I, P, P, P, P, Z, P], I),
         "moe_combine": ([P, P, P, I, I, I, I, P, P], I),
         "moe_forward": ([P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P], I),
+        "moe_route_x_workspace_bytes": ([I, I, I, I, I], Z),
+        "moe_route_x": ([P, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P], I),
+        "moe_forward_x_workspace_bytes": ([I, I, I, I, I, I], Z),
+        "moe_forward_x": ([P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, Z, P], I),
         "moe_token_round_max_rows": ([I, I, I, I], L),
         "moe_token_round_workspace_bytes": ([I, I, I, I], Z),
         "moe_token_round": ([P, P, P, I, I, I, I, I, P, P, P, L, P, P, P, Z, P], I),
@@ -311,6 +315,81 @@ def moe_forward(X: torch.Tensor, logits: torch.Tensor, W1: torch.Tensor, W3: tor
     E, _, n = W1.shape
     plan = ForwardPlan(T, d, E, K, n, X.dtype, X.device)
     plan(X, logits, W1, W3, W2)
+    return plan.out, plan
+
+
+def moe_route_x(X: torch.Tensor, Wr: torch.Tensor, bias: torch.Tensor | None, K: int, want_logits: bool = True,
+                ws: torch.Tensor | None = None, out=None):
+    """Router projection and steps 1-2 from the tokens.  X [T,d], Wr [d,E] f32, bias [E] f32 or None ->
+    (topk_idx [T,K] i32, topk_w [T,K] f32, counts [E] i32, offsets [E+1] i32, logits [T,E] f32 or None).
+    `out` (optional) is such a tuple to write into and `ws` a workspace of moe_route_x_workspace_bytes bytes,
+    so that repeated calls allocate nothing."""
+    lib = load_library()
+    T, d = X.shape
+    E = Wr.shape[1]
+    dev = X.device
+    dt = dtype_code(X.dtype)
+    nws = lib.moe_route_x_workspace_bytes(T, d, E, K, dt)
+    if nws == 0:
+        raise MoEError(MOE_ERR_UNSUPPORTED, "moe_route_x_workspace_bytes", lib.moe_last_error().decode())
+    if ws is None:
+        ws = _workspace(nws, dev)
+    elif ws.numel() < nws:
+        raise ValueError(f"ws must hold {nws} bytes")
+    if out is None:
+        out = (torch.empty((T, K), dtype=torch.int32, device=dev), torch.empty((T, K), dtype=torch.float32, device=dev),
+               torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None)
+    idx, w, counts, offsets, logits = out
+    for t, shape, tdt, name in ((idx, (T, K), torch.int32, "topk_idx"), (w, (T, K), torch.float32, "topk_w"),
+                                (counts, (E,), torch.int32, "counts"), (offsets, (E + 1,), torch.int32, "offsets")):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        _dev(t, name, tdt)
+    if logits is not None and tuple(logits.shape) != (T, E):
+        raise ValueError(f"logits must have shape {(T, E)}")
+    _check(lib.moe_route_x(_dev(X, "X"), dt, T, d, E, K, _dev(Wr, "Wr", torch.float32),
+                           0 if bias is None else _dev(bias, "bias", torch.float32),
+                           0 if logits is None else logits.data_ptr(), idx.data_ptr(), w.data_ptr(),
+                           counts.data_ptr(), offsets.data_ptr(), _dev(ws, "ws"), nws, _stream(dev)), "moe_route_x")
+    return idx, w, counts, offsets, logits
+
+
+class ForwardXPlan(ForwardPlan):
+    """Preallocated outputs and workspace for repeated moe_forward_x calls (the layer from X and the router
+    weights); `logits` is filled only when want_logits is set."""
+
+    def __init__(self, T: int, d: int, E: int, K: int, n: int, dtype: torch.dtype, device, want_logits: bool = False):
+        super().__init__(T, d, E, K, n, dtype, device)
+        lib = load_library()
+        self.ws_bytes = lib.moe_forward_x_workspace_bytes(T, d, E, K, n, dtype_code(dtype))
+        if self.ws_bytes == 0:
+            raise MoEError(MOE_ERR_UNSUPPORTED, "moe_forward_x_workspace_bytes", lib.moe_last_error().decode())
+        self.ws = _workspace(self.ws_bytes, self.device)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=self.device) if want_logits else None
+
+    def __call__(self, X, Wr, bias, W1, W3, W2):
+        lib = load_library()
+        dt = self.dtype
+        _check(lib.moe_forward_x(_dev(X, "X", dt), _dev(Wr, "Wr", torch.float32),
+                                 0 if bias is None else _dev(bias, "bias", torch.float32), _dev(W1, "W1", dt),
+                                 _dev(W3, "W3", dt), _dev(W2, "W2", dt), dtype_code(dt), self.T, self.d, self.E,
+                                 self.K, self.n, self.out.data_ptr(),
+                                 0 if self.logits is None else self.logits.data_ptr(), self.topk_idx.data_ptr(),
+                                 self.topk_w.data_ptr(), self.counts.data_ptr(), self.offsets.data_ptr(),
+                                 self.sorted_pair.data_ptr(), self.inv.data_ptr(), self.ws.data_ptr(),
+                                 self.ws_bytes, _stream(self.device)), "moe_forward_x")
+        return self.out
+
+
+def moe_forward_x(X: torch.Tensor, Wr: torch.Tensor, bias: torch.Tensor | None, W1: torch.Tensor, W3: torch.Tensor,
+                  W2: torch.Tensor, K: int, want_logits: bool = True):
+    """Whole layer from X and the router weights.  Returns (out [T,d], plan) -- the plan holds the routing
+    outputs and, with want_logits, the logits."""
+    T, d = X.shape
+    E, _, n = W1.shape
+    plan = ForwardXPlan(T, d, E, K, n, X.dtype, X.device, want_logits)
+    plan(X, Wr, bias, W1, W3, W2)
     return plan.out, plan
 
 

@@ -26,15 +26,24 @@ hipError_t launch_scan(const int32_t* blk, int B, int E, int32_t* counts, int32_
 
 // Step 3.
 hipError_t launch_chunk_hist(const int32_t* idx, int T, int E, int K, int32_t* blk, hipStream_t s);
+// sub_tokens (0 = chunk_tokens(T)): the token count of one row of blk /
+// blkbase, a divisor of chunk_tokens(T) (the fused router-gate keeps counts
+// per 32-token tile: kRouterGateTokens).
 hipError_t launch_rank(const int32_t* idx, int T, int E, int K, const int32_t* blkbase,
-                       int32_t* sorted_pair, int32_t* inv, hipStream_t s);
+                       int32_t* sorted_pair, int32_t* inv, hipStream_t s, int sub_tokens = 0);
 // Scan and rank in one launch: each rank workgroup scans blk[B,E] itself
 // (worth it while B*E is small, see scan_rank_fused()); counts and offsets are
 // written when not null.
 hipError_t launch_scan_rank(const int32_t* idx, int T, int E, int K, const int32_t* blk, int32_t* counts,
                             int32_t* offsets, int32_t* sorted_pair, int32_t* inv, int* zero, int nzero,
-                            hipStream_t s);
-inline bool scan_rank_fused(int T, int E) { return (long long)num_chunks(T) * E <= 16384; }
+                            hipStream_t s, int sub_tokens = 0);
+inline int count_rows(int T, int sub_tokens) {
+    const int st = sub_tokens > 0 ? sub_tokens : chunk_tokens(T);
+    return (T + st - 1) / st;
+}
+inline bool scan_rank_fused(int T, int E, int sub_tokens = 0) {
+    return (long long)count_rows(T, sub_tokens) * E <= 16384;
+}
 hipError_t launch_copy_rows(const void* X, size_t row_bytes, int T, int K, const int32_t* inv,
                             void* Xp, hipStream_t s);
 
@@ -84,6 +93,15 @@ bool ffn_gather_ok(int dtype, int T, int d, int n);
 size_t router_split_bytes(int dtype, int d, int E);
 hipError_t launch_router(const void* X, int dtype, int T, int d, int E, const float* Wr, const float* bias,
                          float* logits, void* split, hipStream_t s);
+// The router projection fused with the gate (steps 0-1 in one pass), where
+// router_gate_ok(): bf16 X, d % 256 == 0, E <= 64.  Writes topk_idx, topk_w,
+// the expert counts of each kRouterGateTokens-token tile into blk
+// [ceil(T / kRouterGateTokens), E], and the logits when `logits` is not null.
+// `split` as for launch_router.
+constexpr int kRouterGateTokens = 32;
+bool router_gate_ok(int dtype, int d, int E);
+hipError_t launch_router_gate(const void* X, int T, int d, int E, int K, const float* Wr, const float* bias,
+                              float* logits, int32_t* idx, float* w, int32_t* blk, void* split, hipStream_t s);
 
 // Step 5.
 hipError_t launch_combine(const void* Y, const float* w, const int32_t* inv, int dtype, int T, int d,

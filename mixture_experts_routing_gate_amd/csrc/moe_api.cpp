@@ -110,11 +110,12 @@ size_t permute_ws(int T, int E) {
            align_up((E + 1) * sizeof(int32_t));
 }
 
-size_t forward_ws(int T, int d, int E, int K, int n, int dtype) {
+// sub_tokens: tokens per row of the expert histogram (0: chunk_tokens(T)).
+size_t forward_ws(int T, int d, int E, int K, int n, int dtype, int sub_tokens = 0) {
     const size_t A = (size_t)T * K;
     const size_t s = elem_bytes(dtype);
     size_t b = 0;
-    b += 2 * align_up((size_t)num_chunks(T) * E * 4);  // blk, blkbase
+    b += 2 * align_up((size_t)count_rows(T, sub_tokens) * E * 4);  // blk, blkbase
     b += align_up(A * 4) * 2;                          // topk_idx, topk_w
     b += align_up(E * 4) + align_up((E + 1) * 4);      // counts, offsets
     b += align_up(A * 4) * 2;                          // sorted_pair, inv
@@ -122,6 +123,27 @@ size_t forward_ws(int T, int d, int E, int K, int n, int dtype) {
     b += (ffn_gather_ok(dtype, T, d, n) ? 0 : align_up(A * d * s)) + align_up(A * d * s) + align_up(A * n * s);  // Xp, Y, Act
     b += align_up(ffn_split_bytes(dtype, d, n));        // split tail of the grouped GEMMs
     return b;
+}
+
+// The router front end of the calls that start from X (moe_route_x,
+// moe_forward_x): the bf16 split of Wr, then room for the logits where the
+// projection is not fused with the gate.  Tokens per histogram row after it.
+bool route_x_fused(int dtype, int d, int E) { return router_gate_ok(dtype, d, E); }
+int route_x_rows_tokens(int dtype, int d, int E) { return route_x_fused(dtype, d, E) ? kRouterGateTokens : 0; }
+size_t route_x_front_ws(int T, int d, int E, int dtype) {
+    size_t b = align_up(router_split_bytes(dtype, d, E));
+    if (!route_x_fused(dtype, d, E)) b += align_up((size_t)T * E * 4);
+    return b;
+}
+
+// Checks of the router arguments shared by moe_router and the calls from X.
+int check_router(int T, int d, int E) {
+    if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1 (got %d)", T);
+    if (d < 1) return fail(MOE_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+    if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1 (got %d)", E);
+    if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E=%d exceeds the supported maximum %d", E, kMaxE);
+    if ((long long)T * E >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*E must be < 2^31");
+    return MOE_OK;
 }
 
 // Workspace of moe_backward_data, in carving order.
@@ -439,11 +461,7 @@ int moe_ffn_down(const void* Act, const void* W2, int dtype, int T, int d, int E
 
 int moe_router(const void* X, int dtype, int T, int d, int E, const float* Wr, const float* bias,
                float* logits, void* ws, size_t ws_bytes, void* stream) {
-    if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1 (got %d)", T);
-    if (d < 1) return fail(MOE_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
-    if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1 (got %d)", E);
-    if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E=%d exceeds the supported maximum %d", E, kMaxE);
-    if ((long long)T * E >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*E must be < 2^31");
+    CHECK(check_router(T, d, E));
     CHECK(check_dtype(dtype));
     NONNULL(X);
     NONNULL(Wr);
@@ -475,36 +493,79 @@ int moe_combine(const void* Y, const float* topk_w, const int32_t* inv, int dtyp
     return MOE_OK;
 }
 
-int moe_forward(const void* X, const float* logits, const void* W1, const void* W3, const void* W2,
-                int dtype, int T, int d, int E, int K, int n, void* out, int32_t* topk_idx,
-                float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* inv,
-                void* ws, size_t ws_bytes, void* stream) {
+size_t moe_route_x_workspace_bytes(int T, int d, int E, int K, int dtype) {
+    if (check_tek(T, E, K) != MOE_OK || check_router(T, d, E) != MOE_OK || check_dtype(dtype) != MOE_OK) return 0;
+    return route_x_front_ws(T, d, E, dtype) +
+           align_up((size_t)count_rows(T, route_x_rows_tokens(dtype, d, E)) * E * sizeof(int32_t));
+}
+
+size_t moe_forward_x_workspace_bytes(int T, int d, int E, int K, int n, int dtype) {
+    if (check_tek(T, E, K) != MOE_OK || check_router(T, d, E) != MOE_OK || check_dtype(dtype) != MOE_OK ||
+        check_dim("d", d, dtype) != MOE_OK || check_dim("n", n, dtype) != MOE_OK)
+        return 0;
+    return route_x_front_ws(T, d, E, dtype) + forward_ws(T, d, E, K, n, dtype, route_x_rows_tokens(dtype, d, E));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Steps 0-1 of the calls from X into topk_idx / topk_w and the expert counts
+// blk (rows of route_x_rows_tokens() tokens): fused where route_x_fused(),
+// else moe_router's kernels into `lg` (the caller's logits or workspace room)
+// and the gate.  `front` is the workspace part route_x_front_ws() sizes.
+int route_x_front(const void* X, int dtype, int T, int d, int E, int K, const float* Wr, const float* bias,
+                  float* logits, int32_t* topk_idx, float* topk_w, int32_t* blk, void* front, hipStream_t s) {
+    Carver c(front);
+    void* split = c.take<char>(router_split_bytes(dtype, d, E));
+    if (route_x_fused(dtype, d, E)) {
+        HIPCHECK(launch_router_gate(X, T, d, E, K, Wr, bias, logits, topk_idx, topk_w, blk, split, s));
+    } else {
+        float* room = c.take<float>((size_t)T * E);
+        float* lg = logits != nullptr ? logits : room;
+        HIPCHECK(launch_router(X, dtype, T, d, E, Wr, bias, lg, router_split_bytes(dtype, d, E) ? split : nullptr, s));
+        HIPCHECK(launch_gate(lg, T, E, K, topk_idx, topk_w, blk, s));
+    }
+    return MOE_OK;
+}
+
+// moe_forward (logits given) and moe_forward_x (Wr given: the router runs
+// first, fused with the gate where it can be).
+int forward_impl(const char* name, const void* X, const float* logits_in, const float* Wr, const float* bias,
+                 float* logits_out, const void* W1, const void* W3, const void* W2, int dtype, int T, int d, int E,
+                 int K, int n, void* out, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                 int32_t* sorted_pair, int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
+    const bool from_x = Wr != nullptr;
     CHECK(check_tek(T, E, K));
     CHECK(check_dtype(dtype));
     CHECK(check_dim("d", d, dtype));
     CHECK(check_dim("n", n, dtype));
     NONNULL(X);
-    NONNULL(logits);
+    if (!from_x) NONNULL(logits_in);
+    if (from_x) CHECK(check_router(T, d, E));
     NONNULL(W1);
     NONNULL(W3);
     NONNULL(W2);
     NONNULL(out);
-    for (const void* p : {(const void*)topk_idx, (const void*)topk_w, (const void*)counts,
-                          (const void*)offsets, (const void*)sorted_pair, (const void*)inv})
+    for (const void* p : {(const void*)topk_idx, (const void*)topk_w, (const void*)counts, (const void*)offsets,
+                          (const void*)sorted_pair, (const void*)inv, (const void*)logits_out, (const void*)bias})
         if (p != nullptr && !aligned16(p))
-            return fail(MOE_ERR_INVALID_ARG, "optional outputs must be 16-byte aligned");
+            return fail(MOE_ERR_INVALID_ARG, "optional arguments must be 16-byte aligned");
     if ((long long)T * K * (long long)(d > n ? d : n) >= (1LL << 40))
         return fail(MOE_ERR_UNSUPPORTED, "T*K*max(d,n) must be < 2^40");
-    const size_t need = forward_ws(T, d, E, K, n, dtype);
+    const int st = from_x ? route_x_rows_tokens(dtype, d, E) : 0;  // tokens per histogram row
+    const size_t front = from_x ? route_x_front_ws(T, d, E, dtype) : 0;
+    const size_t need = front + forward_ws(T, d, E, K, n, dtype, st);
     if (ws == nullptr || ws_bytes < need)
-        return fail(MOE_ERR_WORKSPACE, "moe_forward needs %zu workspace bytes (got %zu)", need, ws_bytes);
+        return fail(MOE_ERR_WORKSPACE, "%s needs %zu workspace bytes (got %zu)", name, need, ws_bytes);
     if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "ws must be 16-byte aligned");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t A = (size_t)T * K;
     const size_t sz = elem_bytes(dtype);
-    const int B = num_chunks(T);
+    const int B = count_rows(T, st);
     Carver c(ws);
+    void* front_ws = c.take<char>(front);
     int32_t* blk = c.take<int32_t>((size_t)B * E);
     int32_t* blkbase = c.take<int32_t>((size_t)B * E);
     int32_t* ws_idx = c.take<int32_t>(A);
@@ -526,15 +587,16 @@ int moe_forward(const void* X, const float* logits, const void* W1, const void* 
     if (!sorted_pair) sorted_pair = ws_sp;
     if (!inv) inv = ws_inv;
 
-    HIPCHECK(launch_gate(logits, T, E, K, topk_idx, topk_w, blk, s));
+    if (from_x) CHECK(route_x_front(X, dtype, T, d, E, K, Wr, bias, logits_out, topk_idx, topk_w, blk, front_ws, s));
+    else HIPCHECK(launch_gate(logits_in, T, E, K, topk_idx, topk_w, blk, s));
     // the scan also clears the grouped GEMMs' claim counters (no launches of their own)
     int* tickets = ffn_tickets(part);
     const int nt = tickets != nullptr ? ffn_ticket_ints() : 0;
-    if (scan_rank_fused(T, E)) {
-        HIPCHECK(launch_scan_rank(topk_idx, T, E, K, blk, counts, offsets, sorted_pair, inv, tickets, nt, s));
+    if (scan_rank_fused(T, E, st)) {
+        HIPCHECK(launch_scan_rank(topk_idx, T, E, K, blk, counts, offsets, sorted_pair, inv, tickets, nt, s, st));
     } else {
         HIPCHECK(launch_scan(blk, B, E, counts, offsets, blkbase, s, tickets, nt));
-        HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s));
+        HIPCHECK(launch_rank(topk_idx, T, E, K, blkbase, sorted_pair, inv, s, st));
     }
     if (gather) {
         // no permuted copy of X: the SwiGLU GEMM gathers its rows through sorted_pair
@@ -546,6 +608,56 @@ int moe_forward(const void* X, const float* logits, const void* W1, const void* 
     }
     HIPCHECK(launch_combine(Yb, topk_w, inv, dtype, T, d, K, out, s));
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const void* X, const float* logits, const void* W1, const void* W3, const void* W2,
+                int dtype, int T, int d, int E, int K, int n, void* out, int32_t* topk_idx,
+                float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* inv,
+                void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl("moe_forward", X, logits, nullptr, nullptr, nullptr, W1, W3, W2, dtype, T, d, E, K, n, out,
+                        topk_idx, topk_w, counts, offsets, sorted_pair, inv, ws, ws_bytes, stream);
+}
+
+int moe_route_x(const void* X, int dtype, int T, int d, int E, int K, const float* Wr, const float* bias,
+                float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, void* ws,
+                size_t ws_bytes, void* stream) {
+    CHECK(check_tek(T, E, K));
+    CHECK(check_router(T, d, E));
+    CHECK(check_dtype(dtype));
+    NONNULL(X);
+    NONNULL(Wr);
+    NONNULL(topk_idx);
+    NONNULL(topk_w);
+    NONNULL(counts);
+    NONNULL(offsets);
+    for (const void* p : {(const void*)logits, (const void*)bias})
+        if (p != nullptr && !aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "logits and bias must be 16-byte aligned");
+    const int st = route_x_rows_tokens(dtype, d, E);
+    const size_t front = route_x_front_ws(T, d, E, dtype);
+    const size_t need = front + align_up((size_t)count_rows(T, st) * E * sizeof(int32_t));
+    if (ws == nullptr || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "moe_route_x needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Carver c(ws);
+    void* front_ws = c.take<char>(front);
+    int32_t* blk = c.take<int32_t>((size_t)count_rows(T, st) * E);
+    CHECK(route_x_front(X, dtype, T, d, E, K, Wr, bias, logits, topk_idx, topk_w, blk, front_ws, s));
+    HIPCHECK(launch_scan(blk, count_rows(T, st), E, counts, offsets, nullptr, s));
+    return MOE_OK;
+}
+
+int moe_forward_x(const void* X, const float* Wr, const float* bias, const void* W1, const void* W3, const void* W2,
+                  int dtype, int T, int d, int E, int K, int n, void* out, float* logits, int32_t* topk_idx,
+                  float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* inv, void* ws,
+                  size_t ws_bytes, void* stream) {
+    if (Wr == nullptr) return fail(MOE_ERR_INVALID_ARG, "Wr must not be NULL");
+    return forward_impl("moe_forward_x", X, nullptr, Wr, bias, logits, W1, W3, W2, dtype, T, d, E, K, n, out,
+                        topk_idx, topk_w, counts, offsets, sorted_pair, inv, ws, ws_bytes, stream);
 }
 
 long long moe_token_round_max_rows(int T, int E, int K, int M) {

@@ -41,14 +41,17 @@ __global__ __launch_bounds__(kThreads) void chunk_hist_kernel(const int32_t* __r
 // Position of (t,k) = base(chunk,e) + earlier sub-chunks + earlier waves +
 // popcount(mask[w][e] & lanes below).
 //
-// base(chunk,e) comes from blkbase when it is given.  Otherwise (small B*E)
-// every workgroup does the scan of step 2 itself from the per-chunk counts
-// blk[B,E]: thread e adds expert e over all chunks (its count) and over the
-// chunks before this one, then an exclusive scan over experts gives offsets.
-// Workgroup 0 writes counts and offsets when they are not null.  The sums are
-// of integers, so every workgroup gets the same values in any order.
+// The counts may be kept per sub-chunk: `sub` rows of blk (or blkbase) per
+// chunk of CH tokens (the fused router-gate counts 32-token tiles).
+// base(chunk,e) comes from blkbase (its row chunk*sub) when it is given.
+// Otherwise (small B*E) every workgroup does the scan of step 2 itself from
+// the counts blk[B,E]: thread e adds expert e over all B rows (its count) and
+// over the rows before this chunk's first, then an exclusive scan over experts
+// gives offsets.  Workgroup 0 writes counts and offsets when they are not
+// null.  The sums are of integers, so every workgroup gets the same values in
+// any order.
 __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restrict__ idx, int T, int E,
-                                                        int K, int CH,
+                                                        int K, int CH, int sub,
                                                         const int32_t* __restrict__ blkbase,
                                                         const int32_t* __restrict__ blk, int B,
                                                         int32_t* __restrict__ counts,
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
     if (chunk == 0)  // state for later kernels on the stream
         for (int i = tid; i < nzero; i += kThreads) zero[i] = 0;
     if (blkbase != nullptr) {
-        for (int e = tid; e < E; e += kThreads) run[e] = blkbase[(size_t)chunk * E + e];
+        for (int e = tid; e < E; e += kThreads) run[e] = blkbase[(size_t)chunk * sub * E + e];
     } else {  // E <= 256 == kThreads: thread e owns expert e
         constexpr int kBatch = 16;
         int tot = 0, below = 0;
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
                 for (int i = 0; i < kBatch; ++i) {
                     const int v = (b0 + i < B) ? x[i] : 0;
                     tot += v;
-                    below += (b0 + i < chunk) ? v : 0;
+                    below += (b0 + i < chunk * sub) ? v : 0;
                 }
             }
         }
@@ -207,9 +210,10 @@ hipError_t launch_chunk_hist(const int32_t* idx, int T, int E, int K, int32_t* b
 }
 
 hipError_t launch_rank(const int32_t* idx, int T, int E, int K, const int32_t* blkbase,
-                       int32_t* sorted_pair, int32_t* inv, hipStream_t s) {
+                       int32_t* sorted_pair, int32_t* inv, hipStream_t s, int sub_tokens) {
+    const int ST = sub_tokens > 0 ? sub_tokens : chunk_tokens(T);
     hipLaunchKernelGGL(rank_kernel, dim3(num_chunks(T)), dim3(kThreads), 0, s, idx, T, E, K,
-                       chunk_tokens(T), blkbase, static_cast<const int32_t*>(nullptr), 0,
+                       chunk_tokens(T), chunk_tokens(T) / ST, blkbase, static_cast<const int32_t*>(nullptr), 0,
                        static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr), sorted_pair, inv,
                        static_cast<int*>(nullptr), 0);
     return hipGetLastError();
@@ -217,10 +221,11 @@ hipError_t launch_rank(const int32_t* idx, int T, int E, int K, const int32_t* b
 
 hipError_t launch_scan_rank(const int32_t* idx, int T, int E, int K, const int32_t* blk, int32_t* counts,
                             int32_t* offsets, int32_t* sorted_pair, int32_t* inv, int* zero, int nzero,
-                            hipStream_t s) {
+                            hipStream_t s, int sub_tokens) {
+    const int ST = sub_tokens > 0 ? sub_tokens : chunk_tokens(T);
     hipLaunchKernelGGL(rank_kernel, dim3(num_chunks(T)), dim3(kThreads), 0, s, idx, T, E, K,
-                       chunk_tokens(T), static_cast<const int32_t*>(nullptr), blk, num_chunks(T), counts,
-                       offsets, sorted_pair, inv, zero, zero != nullptr ? nzero : 0);
+                       chunk_tokens(T), chunk_tokens(T) / ST, static_cast<const int32_t*>(nullptr), blk,
+                       (T + ST - 1) / ST, counts, offsets, sorted_pair, inv, zero, zero != nullptr ? nzero : 0);
     return hipGetLastError();
 }
 

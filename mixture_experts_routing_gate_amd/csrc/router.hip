@@ -135,6 +135,156 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t* _
     }
 }
 
+// The router projection fused with the gate (page [P1] section 2.1: logit
+// computation, softmax and top-k in one pass; page [P4] section 1: the K best
+// of E scores per token), for E <= 64.  A workgroup computes the logits of one
+// tile of 32 tokens exactly as router_mfma_kernel does (the same MFMA order
+// over k within each wave's quarter of d, the four waves' sums added in wave
+// order, then the bias), so they equal moe_router's logits bit for bit; they
+// never leave the workgroup unless `logits` asks for them.  From LDS, LPT
+// lanes per token (8 experts each) then take K rounds of a group argmax: the
+// largest logit, the lower expert index among equal ones (-0.0 == +0.0), best
+// first.  Weights exp(l_k - l_0) / sum_j exp(l_j - l_0), the sum in rank
+// order.  The tile's expert counts go to blk[tile, E] (integer LDS atomics).
+template <int NB>
+__global__ __launch_bounds__(kThreads) void router_gate_kernel(
+    const uint16_t* __restrict__ X, int T, int d, const uint16_t* __restrict__ hi, const uint16_t* __restrict__ lo,
+    const float* __restrict__ bias, int E, int K, float* __restrict__ logits, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ blk) {
+    constexpr int U = 4;
+    constexpr int EP = 32 * NB;   // padded expert count
+    constexpr int LPT = EP / 8;   // gate lanes per token
+    constexpr int TT = kRouterGateTokens;
+    static_assert(TT == 32, "one 32-row MFMA token group per tile");
+    __shared__ f32x16 red[4][NB][kWave];
+    __shared__ float lgs[TT][EP + 1];
+    __shared__ int hist[EP];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int tile = blockIdx.x;
+    const int t0 = tile * TT;
+    if (t0 >= T) return;
+    if (tid < EP) hist[tid] = 0;
+    // rows past T are computed and discarded
+    const uint16_t* xr = X + (size_t)min(t0 + l32, T - 1) * d + lh * 8;
+    const size_t woff = (size_t)l32 * d + lh * 8;
+    const int kq = d / 4;
+    const int kb = wave * kq;
+
+    f32x16 acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
+    for (int k0 = kb; k0 < kb + kq; k0 += 16 * U) {
+        bf16x8 xf[U], hf[U][NB], lf[U][NB];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + u * 16;
+            xf[u] = *reinterpret_cast<const bf16x8*>(xr + k);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if (NB > 1 || l32 < E) {
+                    hf[u][j] = *reinterpret_cast<const bf16x8*>(hi + woff + (size_t)j * 32 * d + k);
+                    lf[u][j] = *reinterpret_cast<const bf16x8*>(lo + woff + (size_t)j * 32 * d + k);
+                } else {
+                    hf[u][j] = bf16x8{};
+                    lf[u][j] = bf16x8{};
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf[u][j], xf[u], acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[u][j], xf[u], acc[j], 0, 0, 0);
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) red[wave][j][lane] = acc[j];
+    __syncthreads();
+    if (wave < NB) {  // wave j finishes expert block j
+        const int j = wave;
+        f32x16 sm = red[0][j][lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) sm += red[w][j][lane];
+        const int t = t0 + l32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e = j * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+            const float v = e < E ? sm[i] + (bias != nullptr ? bias[e] : 0.0f) : 0.0f;
+            lgs[l32][e] = v;
+            if (logits != nullptr && t < T && e < E) logits[(size_t)t * E + e] = v;
+        }
+    }
+    __syncthreads();
+
+    if (tid < TT * LPT) {  // whole waves: LPT * 32 is 128 or 256 lanes
+        const int tk = tid / LPT, g = tid % LPT;
+        const int t = t0 + tk;
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = lgs[tk][g * 8 + j];
+        constexpr int kNone = 0x7fffffff;
+        unsigned taken = 0u;
+        float sv[8];
+        int si[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            sv[r] = 0.0f;
+            si[r] = 0;
+            if (r < K) {
+                float bv = 0.0f;
+                int bi = kNone;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {  // ascending index: strict > keeps the lower one
+                    const int e = g * 8 + j;
+                    const bool ok = e < E && !((taken >> j) & 1u);
+                    if (ok && (bi == kNone || v[j] > bv)) {
+                        bv = v[j];
+                        bi = e;
+                    }
+                }
+#pragma unroll
+                for (int o = 1; o < LPT; o <<= 1) {
+                    const float ov = __shfl_xor(bv, o, kWave);
+                    const int oi = __shfl_xor(bi, o, kWave);
+                    if (oi != kNone && (bi == kNone || ov > bv || (ov == bv && oi < bi))) {
+                        bv = ov;
+                        bi = oi;
+                    }
+                }
+                sv[r] = bv;
+                si[r] = bi;
+                if (bi >= g * 8 && bi < g * 8 + 8) taken |= 1u << (bi - g * 8);
+            }
+        }
+        float ex[8];
+        float S = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            ex[r] = r < K ? expf(sv[r] - sv[0]) : 0.0f;
+            S += ex[r];
+        }
+        const float rS = __builtin_amdgcn_rcpf(S);
+        if (t < T) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if (r < K && r % LPT == g) {
+                    topk_idx[(size_t)t * K + r] = si[r];
+                    topk_w[(size_t)t * K + r] = ex[r] * rS;
+                    atomicAdd(&hist[si[r]], 1);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < E) blk[(size_t)tile * E + tid] = hist[tid];
+}
+
 // One thread per (token, expert), fp32 FMAs over d in index order.
 MOE_DEV float load_x(const float* p) { return *p; }
 MOE_DEV float load_x(const uint16_t* p) { return bf16_to_f32(*p); }
@@ -165,6 +315,28 @@ size_t router_split_bytes(int dtype, int d, int E) {
     const int eb = 32 * router_nb(E);
     const size_t e_pad = (size_t)((E + eb - 1) / eb) * eb;
     return 2 * e_pad * (size_t)d * sizeof(uint16_t);
+}
+
+bool router_gate_ok(int dtype, int d, int E) { return router_mfma_ok(dtype, d) && E <= 64; }
+
+hipError_t launch_router_gate(const void* X, int T, int d, int E, int K, const float* Wr, const float* bias,
+                              float* logits, int32_t* idx, float* w, int32_t* blk, void* split, hipStream_t s) {
+    if (!router_gate_ok(1, d, E) || K < 1 || K > 8 || K > E) return hipErrorInvalidValue;
+    const int nb = router_nb(E);
+    const int e_pad = 32 * nb;
+    uint16_t* hi = static_cast<uint16_t*>(split);
+    uint16_t* lo = hi + (size_t)e_pad * d;
+    const size_t n = (size_t)e_pad * d;
+    const unsigned sgrid = (unsigned)std::min<size_t>((n + kThreads - 1) / kThreads, 4096);
+    hipLaunchKernelGGL(router_split_kernel, dim3(sgrid), dim3(kThreads), 0, s, Wr, d, E, e_pad, hi, lo);
+    const dim3 grid((unsigned)((T + kRouterGateTokens - 1) / kRouterGateTokens));
+    if (nb == 1)
+        hipLaunchKernelGGL(router_gate_kernel<1>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(X), T, d,
+                           hi, lo, bias, E, K, logits, idx, w, blk);
+    else
+        hipLaunchKernelGGL(router_gate_kernel<2>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(X), T, d,
+                           hi, lo, bias, E, K, logits, idx, w, blk);
+    return hipGetLastError();
 }
 
 hipError_t launch_router(const void* X, int dtype, int T, int d, int E, const float* Wr, const float* bias,
