@@ -55,6 +55,13 @@ def parse():
                          "for a kernel trace, and print its time")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a plain copy of known size and each step once (for rocprofv3 --pmc) and exit")
+    ap.add_argument("--probe", choices=["mixtral", "dsv3", "fine", "gate_l"],
+                    help="run the steps of one workload a few times (the router, moe_route, moe_permute, "
+                         "moe_ffn_up, moe_ffn_down, moe_combine, then moe_forward), each call after a 512 MiB "
+                         "read flush with --cold, for a rocprofv3 kernel trace or counter pass, and exit")
+    ap.add_argument("--cold", action="store_true", help="with --probe: a read flush before every call")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="a plain 512 MiB device copy, for calibrating FETCH_SIZE / WRITE_SIZE, and exit")
     return ap.parse_args()
 
 
@@ -73,6 +80,15 @@ def event_time_ms(torch, fn, iters, flush=None):
         e.synchronize()
         times.append(s.elapsed_time(e))
     return statistics.median(times), times
+
+
+def make_flush(torch, dev):
+    """A 512 MiB read (a sum into one float): evicts earlier data from L2 and the
+    256 MB Infinity Cache without leaving dirty lines for the timed call to write
+    back (a write flush would)."""
+    buf = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    res = torch.empty(1, dtype=torch.float32, device=dev)
+    return lambda: torch.sum(buf, 0, keepdim=True, out=res)
 
 
 def b2b_time_ms(torch, fn, n=20, reps=3):
@@ -140,6 +156,43 @@ def traffic_probe(moe, synth, torch, dev):
     print(json.dumps({"traffic_probe": "done", "copy_bytes_each_way": 2 * n}), flush=True)
 
 
+def workload_probe(name, cold, moe, synth, torch, dev, reps=3):
+    """Each step of one workload `reps` times (after one warm-up round), for a
+    rocprofv3 kernel trace or counter pass; with `cold`, a 512 MiB read before
+    every call.  Prints one line per round (progress for long profiled runs)."""
+    cfg = synth.CONFIGS[name]
+    g = synth.make_inputs(cfg, dev, seed=0)
+    flush = make_flush(torch, dev) if cold else (lambda: None)
+    if cfg.gate_only:
+        out = moe.moe_route(g["logits"], cfg.K)
+        for r in range(reps + 1):
+            flush()
+            moe.moe_route(g["logits"], cfg.K, out=out)
+            torch.cuda.synchronize()
+            print(json.dumps({"probe": name, "round": r}), flush=True)
+        return
+    Wr, rb = synth.make_router(cfg, dev, seed=0)
+    plan = moe.ForwardPlan(cfg.T, cfg.d, cfg.E, cfg.K, cfg.n, cfg.torch_dtype, dev)
+    for r in range(reps + 1):
+        flush()
+        moe.moe_router(g["X"], Wr, rb)
+        flush()
+        idx, w, counts, offsets = moe.moe_route(g["logits"], cfg.K)
+        flush()
+        sp, inv, Xp = moe.moe_permute(g["X"], idx, cfg.E)
+        flush()
+        Act = moe.moe_ffn_up(Xp, g["W1"], g["W3"], counts, offsets, cfg.K)
+        flush()
+        Y = moe.moe_ffn_down(Act, g["W2"], counts, offsets, cfg.K)
+        flush()
+        moe.moe_combine(Y, w, inv)
+        flush()
+        plan(g["X"], g["logits"], g["W1"], g["W3"], g["W2"])
+        torch.cuda.synchronize()
+        del Xp, Act, Y
+        print(json.dumps({"probe": name, "round": r}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -161,6 +214,17 @@ def main():
     torch.cuda.set_device(dev)
     if args.traffic_probe:
         traffic_probe(moe, synth, torch, dev)
+        return
+    if args.copy_probe:
+        n = 256 << 20  # 512 MiB of bf16
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe": "done", "bytes_each_way": 2 * n}), flush=True)
+        return
+    if args.probe:
+        workload_probe(args.probe, args.cold, moe, synth, torch, dev)
         return
     if args.backward_probe:
         c = synth.CONFIGS["mixtral"]
@@ -198,12 +262,14 @@ def main():
     f_ms, _ = event_time_ms(torch, lambda: moe.moe_grouped_ffn(Xp, g["W1"], g["W3"], g["W2"], counts, offsets, K),
                             max(5, args.steps // 2))
     # The dominant kernel alone: the SwiGLU GEMM (one launch), then the down GEMM.
-    up_ms, _ = event_time_ms(torch, lambda: moe.moe_ffn_up(Xp, g["W1"], g["W3"], counts, offsets, K),
-                             max(5, args.steps // 2))
+    up_ms, up_times = event_time_ms(torch, lambda: moe.moe_ffn_up(Xp, g["W1"], g["W3"], counts, offsets, K),
+                                    max(5, args.steps // 2))
+    up_mean_ms = statistics.mean(up_times)
     dn_ms, _ = event_time_ms(torch, lambda: moe.moe_ffn_down(Act, g["W2"], counts, offsets, K),
                              max(5, args.steps // 2))
     up_flops = 4.0 * A * d * n
     up_tflops = up_flops / (up_ms * 1e-3) / 1e12
+    up_tflops_mean = up_flops / (up_mean_ms * 1e-3) / 1e12
     c_ms, _ = event_time_ms(torch, lambda: moe.moe_combine(Y, w, inv), 20)
     # Router projection upstream of the gate (logits = X Wr for this workload).
     Wr, rb = synth.make_router(cfg, dev, seed=0)
@@ -214,6 +280,16 @@ def main():
     layer_x = layer_from_x(cfg, g, Wr, rb, moe, torch, dev, args, r_ms, rt_ms)
     p_b2b = b2b_time_ms(torch, lambda: moe.moe_permute(g["X"], idx, E))
     c_b2b = b2b_time_ms(torch, lambda: moe.moe_combine(Y, w, inv))
+    # Cold: the same 512 MiB read before every call as for the gate, so that the
+    # steps' working sets (about 200 MB here) are not served from the 256 MB
+    # Infinity Cache; outputs and workspace preallocated.
+    flush = make_flush(torch, dev)
+    p_out = (torch.empty_like(sp), torch.empty_like(inv), torch.empty_like(Xp))
+    p_ws = torch.empty(moe.load_library().moe_permute_workspace_bytes(T, E, K), dtype=torch.uint8, device=dev)
+    c_out = torch.empty((T, d), dtype=cfg.torch_dtype, device=dev)
+    p_cold, _ = event_time_ms(torch, lambda: moe.moe_permute(g["X"], idx, E, out=p_out, ws=p_ws), 20, flush=flush)
+    c_cold, _ = event_time_ms(torch, lambda: moe.moe_combine(Y, w, inv, out=c_out), 20, flush=flush)
+    del p_out, p_ws, c_out
     s = 2  # bf16 bytes
     perm_bytes = T * (s * d * (1 + K) + 12 * K)
     comb_bytes = T * (s * d * (K + 1) + 8 * K)
@@ -227,14 +303,11 @@ def main():
     # logits from L2 and the 256 MB Infinity Cache.
     gcfg = synth.CONFIGS["gate_l"]
     glg = synth.make_inputs(gcfg, dev, seed=0)["logits"]
-    flush_buf = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-    flush_out = torch.empty(1, dtype=torch.float32, device=dev)
     g_out = moe.moe_route(glg, gcfg.K)  # outputs and workspace reused: no allocation between the events
     g_ws = torch.empty(max(moe.load_library().moe_route_workspace_bytes(gcfg.T, gcfg.E, gcfg.K), 1),
                        dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-    g_ms, _ = event_time_ms(torch, lambda: moe.moe_route(glg, gcfg.K, out=g_out, ws=g_ws), 20,
-                            flush=lambda: torch.sum(flush_buf, 0, keepdim=True, out=flush_out))
+    g_ms, _ = event_time_ms(torch, lambda: moe.moe_route(glg, gcfg.K, out=g_out, ws=g_ws), 20, flush=flush)
     # warm: 20 calls back to back on the same logits (steady state, no launch gaps)
     gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     gs.record()
@@ -260,7 +333,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": gate_bytes / (g_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": gate_bytes / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "traffic": kernel_traffic("gate_l", "gate_kernel")}}
-    del flush_buf, flush_out
+    del flush
 
     # Practical HBM ceiling: a plain 1 GiB device-to-device copy (torch copy_),
     # 20 copies back to back, best of 3; bytes = read + write.
@@ -297,23 +370,29 @@ def main():
                        "frac_hbm_back_to_back": router_bytes / (rt_b2b * 1e-3) / 1e9 / PEAK_HBM_GBS},
             "route_x": layer_x.pop("route_x"),
             "route": {"us": r_ms * 1e3, "GB/s": route_bytes / (r_ms * 1e-3) / 1e9},
-            "permute": {"us": p_ms * 1e3, "GB/s": perm_bytes / (p_ms * 1e-3) / 1e9,
-                        "frac_hbm": perm_bytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "permute": {"us": p_ms * 1e3, "us_cold": p_cold * 1e3, "GB/s_cold": perm_bytes / (p_cold * 1e-3) / 1e9,
+                        "frac_hbm": perm_bytes / (p_cold * 1e-3) / 1e9 / PEAK_HBM_GBS,
                         "us_back_to_back": p_b2b * 1e3,
-                        "frac_hbm_back_to_back": perm_bytes / (p_b2b * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                        "frac_hbm_back_to_back": perm_bytes / (p_b2b * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "note": "frac_hbm: one call (three launches) after a 512 MiB read flush; back to back "
+                                "the working set partly stays in the Infinity Cache (context only)"},
             "grouped_ffn": {"us": f_ms * 1e3, "TFLOPS": ffn_tflops},
             "ffn_up": {"us": up_ms * 1e3, "TFLOPS": up_tflops},
             "ffn_down": {"us": dn_ms * 1e3, "TFLOPS": 2.0 * A * d * n / (dn_ms * 1e-3) / 1e12},
-            "combine": {"us": c_ms * 1e3, "GB/s": comb_bytes / (c_ms * 1e-3) / 1e9,
-                        "frac_hbm": comb_bytes / (c_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "combine": {"us": c_ms * 1e3, "us_cold": c_cold * 1e3, "GB/s_cold": comb_bytes / (c_cold * 1e-3) / 1e9,
+                        "frac_hbm": comb_bytes / (c_cold * 1e-3) / 1e9 / PEAK_HBM_GBS,
                         "us_back_to_back": c_b2b * 1e3,
-                        "frac_hbm_back_to_back": comb_bytes / (c_b2b * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                        "frac_hbm_back_to_back": comb_bytes / (c_b2b * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "note": "frac_hbm: one call after a 512 MiB read flush; back to back: context only"},
         },
         "roofline": {"kernel": "ffn_p4_kernel<true, false> (moe_ffn_up: Act = SiLU(Xp W1) * (Xp W3), one launch)",
-                     "bound": "mfma", "achieved": round(up_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(up_tflops / PEAK_BF16_TFLOPS, 4),
+                     "bound": "mfma", "achieved": round(up_tflops_mean, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(up_tflops_mean / PEAK_BF16_TFLOPS, 4),
                      "traffic": kernel_traffic("mixtral", "ffn_up"),
-                     "algorithmic_flops_per_launch": up_flops, "us_per_launch": up_ms * 1e3},
+                     "algorithmic_flops_per_launch": up_flops, "us_per_launch_mean": up_mean_ms * 1e3,
+                     "us_per_launch_median": up_ms * 1e3, "launches_timed": len(up_times),
+                     "note": "achieved = 4*T*K*d*n FLOPs / the mean of single moe_ffn_up calls, each between "
+                             "two HIP events on the library's stream (the GEMM launch and its split-tail fixup)"},
     }
 
     if not args.no_other_workloads:
@@ -519,13 +598,32 @@ def token_rounding(c, g, plan_topk, moe, torch, np, dev, steps=5, M=256):
     return res
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, g, budget_s, np, torch, synth):
-    """The oracle's per-token layer loop, as it stands, on a bounded token sample."""
+    """The oracle, as it stands: its route (softmax, top-K, histogram, offsets)
+    and permutation over all T, timed alone, and its per-token layer loop on a
+    bounded token sample."""
     import oracle
     cores = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
     X = synth.to_numpy(g["X"])
     lg = synth.to_numpy(g["logits"])
+    route_s = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        idx, _, _, _ = oracle.route(lg, cfg.K)
+        oracle.permute(idx, cfg.E)
+        route_s.append(time.perf_counter() - t0)
+    route_s = statistics.median(route_s)
     W1, W3, W2 = (synth.to_numpy(g[k]) for k in ("W1", "W3", "W2"))
     rng = np.random.default_rng(0)
     per_tok = 6.0 * cfg.K * cfg.d * cfg.n
@@ -540,10 +638,13 @@ def cpu_baseline(cfg, g, budget_s, np, torch, synth):
     dt2 = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": per_tok * ntok2 / dt2 / 1e12, "unit": "TFLOPS", "cores": min(threads, cores),
-            "kind": "oracle",
-            "sample": f"{ntok2} of {cfg.T} tokens of the mixtral-shaped layer through the oracle's per-token "
-                      f"loop (route + {cfg.K} expert SwiGLU MLPs + combine, fp64 accumulation), "
-                      f"{dt2:.1f} s wall; scaled to active TFLOPS of those tokens"}
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "route_s_all_tokens": route_s, "route_Gtokens_per_s": cfg.T / route_s / 1e9,
+            "layer_s_per_token": dt2 / ntok2, "layer_s_all_tokens_estimate": dt2 / ntok2 * cfg.T,
+            "sample": f"route + permutation: all {cfg.T} tokens (median of 3); layer: {ntok2} of {cfg.T} tokens "
+                      f"of the mixtral-shaped layer through the oracle's per-token loop (route + {cfg.K} expert "
+                      f"SwiGLU MLPs + combine, fp64 accumulation), {dt2:.1f} s wall; value = active TFLOPS of "
+                      f"those tokens"}
 
 
 if __name__ == "__main__":

@@ -67,7 +67,11 @@ const char* moe_status_string(int status);
 const char* moe_last_error(void);
 
 /* Workspace sizes in bytes (device memory, 256-byte aligned start) for the
- * calls that need one.  Return 0 for invalid sizes. */
+ * calls that need one.  Return 0 for invalid sizes.
+ * moe_workspace_bytes: one workspace that serves every forward-path call on
+ * these sizes -- moe_route, moe_permute, moe_grouped_ffn (with its split),
+ * moe_ffn_up, moe_ffn_down and moe_forward (the largest of their needs). */
+size_t moe_workspace_bytes(int T, int d, int E, int K, int n, int dtype);
 size_t moe_route_workspace_bytes(int T, int E, int K);
 size_t moe_permute_workspace_bytes(int T, int E, int K);
 size_t moe_forward_workspace_bytes(int T, int d, int E, int K, int n, int dtype);

@@ -45,6 +45,7 @@ def load_library() -> ctypes.CDLL:
     sig = {
         "moe_status_string": ([I], ctypes.c_char_p),
         "moe_last_error": ([], ctypes.c_char_p),
+        "moe_workspace_bytes": ([I, I, I, I, I, I], Z),
         "moe_route_workspace_bytes": ([I, I, I], Z),
         "moe_permute_workspace_bytes": ([I, I, I], Z),
         "moe_forward_workspace_bytes": ([I, I, I, I, I, I], Z),
@@ -180,17 +181,28 @@ def moe_route_noalloc(logits: torch.Tensor, K: int, out):
     return out
 
 
-def moe_permute(X: torch.Tensor, topk_idx: torch.Tensor, E: int):
-    """Step 3.  X [T,d], topk_idx [T,K] -> (sorted_pair [T*K] i32, inv [T*K] i32, Xp [T*K,d])."""
+def moe_permute(X: torch.Tensor, topk_idx: torch.Tensor, E: int, out=None, ws: torch.Tensor | None = None):
+    """Step 3.  X [T,d], topk_idx [T,K] -> (sorted_pair [T*K] i32, inv [T*K] i32, Xp [T*K,d]).
+    `out` (optional) is such a tuple to write into and `ws` a workspace of moe_permute_workspace_bytes
+    bytes, so that repeated calls allocate nothing."""
     lib = load_library()
     T, d = X.shape
     K = topk_idx.shape[1]
     dev = X.device
-    sp = torch.empty(T * K, dtype=torch.int32, device=dev)
-    inv = torch.empty(T * K, dtype=torch.int32, device=dev)
-    Xp = torch.empty((T * K, d), dtype=X.dtype, device=dev)
+    if out is None:
+        out = (torch.empty(T * K, dtype=torch.int32, device=dev), torch.empty(T * K, dtype=torch.int32, device=dev),
+               torch.empty((T * K, d), dtype=X.dtype, device=dev))
+    sp, inv, Xp = out
+    for t, shape, tdt, name in ((sp, (T * K,), torch.int32, "sorted_pair"), (inv, (T * K,), torch.int32, "inv"),
+                                (Xp, (T * K, d), X.dtype, "Xp")):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        _dev(t, name, tdt)
     nws = lib.moe_permute_workspace_bytes(T, E, K)
-    ws = _workspace(nws, dev)
+    if ws is None:
+        ws = _workspace(nws, dev)
+    elif ws.numel() < nws:
+        raise ValueError(f"ws must hold {nws} bytes")
     _check(lib.moe_permute(_dev(X, "X"), dtype_code(X.dtype), T, d, E, K, _dev(topk_idx, "topk_idx", torch.int32),
                            sp.data_ptr(), inv.data_ptr(), Xp.data_ptr(), ws.data_ptr(), nws, _stream(dev)),
            "moe_permute")
@@ -264,13 +276,17 @@ def moe_ffn_down(Act: torch.Tensor, W2: torch.Tensor, counts: torch.Tensor, offs
     return Y
 
 
-def moe_combine(Y: torch.Tensor, topk_w: torch.Tensor, inv: torch.Tensor):
-    """Step 5.  Y [T*K,d], topk_w [T,K] f32, inv [T*K] i32 -> out [T,d]."""
+def moe_combine(Y: torch.Tensor, topk_w: torch.Tensor, inv: torch.Tensor, out: torch.Tensor | None = None):
+    """Step 5.  Y [T*K,d], topk_w [T,K] f32, inv [T*K] i32 -> out [T,d] (written into `out` when given)."""
     lib = load_library()
     T, K = topk_w.shape
     d = Y.shape[1]
     dev = Y.device
-    out = torch.empty((T, d), dtype=Y.dtype, device=dev)
+    if out is None:
+        out = torch.empty((T, d), dtype=Y.dtype, device=dev)
+    elif tuple(out.shape) != (T, d) or out.dtype != Y.dtype:
+        raise ValueError(f"out must be [{T}, {d}] of {Y.dtype}")
+    _dev(out, "out")
     _check(lib.moe_combine(_dev(Y, "Y"), _dev(topk_w, "topk_w", torch.float32), _dev(inv, "inv", torch.int32),
                            dtype_code(Y.dtype), T, d, K, out.data_ptr(), _stream(dev)), "moe_combine")
     return out

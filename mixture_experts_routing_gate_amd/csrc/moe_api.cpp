@@ -289,6 +289,15 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_last_error; }
 
+size_t moe_workspace_bytes(int T, int d, int E, int K, int n, int dtype) {
+    if (check_tek(T, E, K) != MOE_OK || check_dtype(dtype) != MOE_OK || check_dim("d", d, dtype) != MOE_OK ||
+        check_dim("n", n, dtype) != MOE_OK)
+        return 0;
+    size_t b = forward_ws(T, d, E, K, n, dtype);
+    for (const size_t x : {route_ws(T, E), permute_ws(T, E), ffn_split_bytes(dtype, d, n)}) b = x > b ? x : b;
+    return b;
+}
+
 size_t moe_route_workspace_bytes(int T, int E, int K) {
     if (check_tek(T, E, K) != MOE_OK) return 0;
     return route_ws(T, E);

@@ -47,6 +47,15 @@ def test_workspace_sizes(lib):
     copied = lib.moe_forward_workspace_bytes(T, d + 128, E, K, n, moe.MOE_BF16)
     assert copied >= A * (2 * (d + 128) + n) * 2
     assert lib.moe_forward_workspace_bytes(256, 128, 8, 2, 256, moe.MOE_F32) >= 512 * (2 * 128 + 256) * 4
+    # one workspace for every forward-path call
+    for args in ((T, d, E, K, n, moe.MOE_BF16), (256, 128, 8, 2, 256, moe.MOE_F32), (70001, 256, 256, 2, 128, 1)):
+        Tt, dd, Ee, Kk, nn, dt = args
+        allw = lib.moe_workspace_bytes(*args)
+        assert allw >= lib.moe_forward_workspace_bytes(*args) > 0
+        assert allw >= lib.moe_route_workspace_bytes(Tt, Ee, Kk)
+        assert allw >= lib.moe_permute_workspace_bytes(Tt, Ee, Kk)
+        assert allw >= lib.moe_ffn_workspace_bytes(dd, nn, dt)
+    assert lib.moe_workspace_bytes(T, 100, E, K, n, moe.MOE_BF16) == 0
     assert lib.moe_forward_workspace_bytes(T, 100, E, K, n, moe.MOE_BF16) == 0  # d not a multiple of 128
     assert lib.moe_forward_workspace_bytes(T, d, E, K, n, 7) == 0               # unknown dtype
 
