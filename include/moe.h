@@ -381,8 +381,9 @@ int moe_forward_tr(const void* X, const float* logits, const void* W1, const voi
  * In:  X [T,d], W1/W3 [E,d,n], W2 [E,n,d] and dout [T,d] in dtype; logits
  *      [T,E] fp32.  Sizes and limits as moe_forward.
  * Out: dX [T,d] (dtype), dlogits [T,E] fp32, dw [T,K] fp32 (may be NULL).
- *      bf16 intermediates (h1, h3, dA, dh) are stored rounded to bf16; the
- *      sums are fp32.
+ *      bf16 intermediates (h1, h3, dA, dh) are rounded to bf16 (dA in
+ *      registers: the SwiGLU backward and dS run in the epilogue of the GEMM
+ *      that forms it); the sums are fp32.
  * Workspace: moe_backward_data_workspace_bytes(T,d,E,K,n,dtype) bytes, 16-byte
  *      aligned; it holds the routing, expert-sorted copies of X and dout and
  *      the intermediates, all rewritten on every call.  For fp32, or for bf16

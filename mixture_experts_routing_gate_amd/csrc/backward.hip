@@ -12,9 +12,12 @@
 //   dXp = [dh1 | dh3] [W1[e]^T ; W3[e]^T]   (grouped GEMM, K = 2n)
 //   dX[t] = sum_k dXp[row of (t, k)]   (the combine with unit weights)
 //   dlogits[t, idx_k] = w_k (dS_k - sum_j w_j dS_j), 0 for experts not chosen.
-// The GEMMs are the forward's grouped kernels on transposed weight copies;
-// this file holds the kernels that are new: the weight transpose, the SwiGLU
-// backward with dS, the logit gradient, a fill, and the weight gradients
+// The GEMMs are the forward's grouped kernels (reading the weights as stored,
+// k-contiguous, or transposed copies where that mode does not apply); with
+// bf16 the SwiGLU backward and dS run in the dA GEMM's epilogue (ffn.hip), and
+// this file adds the row weights and the fixed-order dS reduction for it.  It
+// also holds the kernels that are new: the weight transpose, the SwiGLU
+// backward with dS as its own pass, the logit gradient, a fill, and the weight gradients
 //   dW1[e] = Xp^T dh1, dW3[e] = Xp^T dh3, dW2[e] = (w a)^T dY
 // summed over each expert's rows (its own kernel: the reduction runs over the
 // ragged rows, so tiles are indexed by expert rather than by row).
@@ -178,6 +181,30 @@ __global__ __launch_bounds__(256) void swiglu_bwd_bf16_kernel(const uint16_t* __
     }
     ds = group_sum<kWave>(ds);
     if (lane == 0) dS_tk[tk] = ds;
+}
+
+// wrow[p] = topk_w[sorted_pair[p]]: the routing weight of each expert-sorted row.
+__global__ __launch_bounds__(256) void row_weights_kernel(const float* __restrict__ topk_w,
+                                                          const int32_t* __restrict__ sorted_pair, int rows,
+                                                          float* __restrict__ wrow) {
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p < rows) wrow[p] = topk_w[sorted_pair[p]];
+}
+
+// One wave per row: dS of row p = the sum of its nparts parts, added in part
+// order (each lane a strided run, then a butterfly: deterministic), written to
+// dS_tk[sorted_pair[p]].
+__global__ __launch_bounds__(256) void ds_reduce_kernel(const float* __restrict__ ds_part, int nparts,
+                                                        const int32_t* __restrict__ sorted_pair, int rows,
+                                                        float* __restrict__ dS_tk) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int p = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (p >= rows) return;
+    const float* src = ds_part + (size_t)p * nparts;
+    float ds = 0.0f;
+    for (int j = lane; j < nparts; j += kWave) ds += src[j];
+    ds = group_sum<kWave>(ds);
+    if (lane == 0) dS_tk[sorted_pair[p]] = ds;
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -383,6 +410,21 @@ hipError_t launch_dw(const void* P, int ldp, const void* Q, int ldq, int qoff, c
                            static_cast<const float*>(P), ldp, static_cast<const float*>(Q), ldq, qoff, counts,
                            offsets, E, M, N, rows, dW);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_row_weights(const float* topk_w, const int32_t* sorted_pair, int rows, float* wrow, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(row_weights_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, topk_w, sorted_pair,
+                       rows, wrow);
+    return hipGetLastError();
+}
+
+hipError_t launch_ds_reduce(const float* ds_part, int nparts, const int32_t* sorted_pair, int rows, float* dS_tk,
+                            hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(ds_reduce_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, ds_part, nparts,
+                       sorted_pair, rows, dS_tk);
     return hipGetLastError();
 }
 

@@ -430,6 +430,166 @@ MOE_DEV void store_rows_short(const f32x16 (&a)[2], int mi, uint16_t* __restrict
     }
 }
 
+// The SwiGLU backward fused into the epilogue of dA = dY W2^T (page [P4]
+// section 2.2: dH and dS formed in the epilogue of the GEMM that produces dA,
+// so that dA never travels through memory).  For each element of a tile,
+// with h1, h3 the stored pre-activations of the same row and column and w the
+// row's routing weight: sig = 1 / (1 + e^-h1), s = h1 sig,
+//   dh1 = w dA h3 sig (1 + h1 (1 - sig)),  dh3 = w dA s,  aw = w s h3,
+// and dS of the row = sum over all n columns of dA s h3, gathered as one fp32
+// partial per 64 columns (ds_part[row, col / 64], in column order inside the
+// 64) and added in column-block order by a later kernel.  dA is rounded to
+// bf16 first, as when it is stored.
+struct BwdEpi {
+    const uint16_t* H1;    // [rows, n]
+    const uint16_t* H3;    // [rows, n]
+    uint16_t* dH;          // [rows, 2n]: dh1 | dh3
+    uint16_t* aw;          // [rows, n] or null
+    const float* wrow;     // [rows]: routing weight of each expert-sorted row
+    float* ds_part;        // [rows, n / 64]
+};
+
+// 8 consecutive columns (one 16-byte piece) of a row: dA bits in `ga`, h1 and
+// h3 bits in a1, a3.  Returns the dS contribution summed in column order.
+MOE_DEV float swiglu_bwd_piece(const u32x4& ga, const u32x4& a1, const u32x4& a3, float w, u32x4& o1, u32x4& o3,
+                               u32x4& oa) {
+    float ds = 0.0f;
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float r1[2], r3[2], ra[2];
+        #pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const float h1 = bf16_to_f32((uint16_t)(a1[i] >> (16 * hh)));
+            const float h3 = bf16_to_f32((uint16_t)(a3[i] >> (16 * hh)));
+            const float g = bf16_to_f32((uint16_t)(ga[i] >> (16 * hh)));
+            // the hardware reciprocal and exponential, as in the forward's SiLU
+            // (the results are rounded to bf16 right after)
+            const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-h1));
+            const float s1 = h1 * sig;
+            ds = fmaf(g, s1 * h3, ds);
+            const float wg = w * g;
+            r1[hh] = wg * h3 * sig * (1.0f + h1 * (1.0f - sig));
+            r3[hh] = wg * s1;
+            ra[hh] = w * (s1 * h3);
+        }
+        o1[i] = pack_bf16x2(r1[0], r1[1]);
+        o3[i] = pack_bf16x2(r3[0], r3[1]);
+        oa[i] = pack_bf16x2(ra[0], ra[1]);
+    }
+    return ds;
+}
+
+// store_rows_lds<false>'s staging, then the SwiGLU backward on each staged
+// 16-byte piece instead of a store of dA, for the four 32-row slices of the
+// wave's quadrant.  The H1, H3 pieces and row weights of slice mi + 1 are
+// requested before slice mi is computed, so that their latency overlaps it.
+// Lanes 16q..16q+15 hold one row's 128 columns (8 per lane); each half of them
+// (64 columns) adds its dS parts with three butterfly steps, and the first
+// lane of the half writes the slot.
+MOE_DEV void bwd_rows_lds(const f32x16 (&acc)[4][4], char* smem, int r0, int rows_valid, int n0, int N, int wave,
+                          int wm, int wn, const BwdEpi& ep) {
+    int lane = __lane_id();
+    __asm__ volatile("" : "+v"(lane));
+    const int l32 = lane & 31, lh = lane >> 5;
+    constexpr int CH = 16, RPI = kWave / CH, NI = 32 / RPI;
+    auto row_at = [&](int r) -> char* { return smem + (r >> 4) * 16384 + wave * 4096 + (r & 15) * 256; };
+    auto swz = [](int r, int c) { return c ^ (r & 15); };
+    const int c = lane % CH;
+    const int col = n0 + wn * 128 + c * 8;
+    const int nslots = N / 64;
+    const int slot = (n0 + wn * 128) / 64 + (c >> 3);
+    u32x4 a1[2][NI], a3[2][NI];
+    float w[2][NI];
+    auto fetch = [&](int mi, int buf) {
+        #pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int m = wm * 128 + mi * 32 + i * RPI + lane / CH;
+            const size_t row = (size_t)(r0 + min(m, rows_valid - 1));  // clamped: rows past the tile are not stored
+            a1[buf][i] = *reinterpret_cast<const u32x4*>(ep.H1 + row * N + col);
+            a3[buf][i] = *reinterpret_cast<const u32x4*>(ep.H3 + row * N + col);
+            w[buf][i] = ep.wrow[row];
+        }
+    };
+    fetch(0, 0);
+    #pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int buf = mi & 1;
+        if (mi + 1 < 4) fetch(mi + 1, buf ^ 1);
+        char* wr = row_at(l32);
+        #pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint2 pk;
+                pk.x = pack_bf16x2(acc[mi][ni][q * 4], acc[mi][ni][q * 4 + 1]);
+                pk.y = pack_bf16x2(acc[mi][ni][q * 4 + 2], acc[mi][ni][q * 4 + 3]);
+                *reinterpret_cast<uint2*>(wr + swz(l32, ni * 4 + q) * 16 + lh * 8) = pk;
+            }
+        }
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        u32x4 ga[NI];
+        #pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int r = i * RPI + lane / CH;
+            ga[i] = *reinterpret_cast<const u32x4*>(row_at(r) + swz(r, c) * 16);
+        }
+        #pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int m = wm * 128 + mi * 32 + i * RPI + lane / CH;
+            const size_t row = (size_t)(r0 + m);
+            u32x4 o1, o3, oa;
+            float ds = swiglu_bwd_piece(ga[i], a1[buf][i], a3[buf][i], w[buf][i], o1, o3, oa);
+            ds += __shfl_xor(ds, 1, kWave);
+            ds += __shfl_xor(ds, 2, kWave);
+            ds += __shfl_xor(ds, 4, kWave);
+            if (m < rows_valid) {
+                *reinterpret_cast<u32x4*>(ep.dH + row * 2 * N + col) = o1;
+                *reinterpret_cast<u32x4*>(ep.dH + row * 2 * N + N + col) = o3;
+                if (ep.aw != nullptr) *reinterpret_cast<u32x4*>(ep.aw + row * N + col) = oa;
+                if ((c & 7) == 0) ep.ds_part[row * nslots + slot] = ds;
+            }
+        }
+    }
+}
+
+// The same for a short tile (store_rows_short<false>'s layout): lane l holds
+// row mi*32 + l%32 and, in 4-column pieces, half of this wave's 64 columns;
+// the two lanes of a row add their dS parts.
+MOE_DEV void bwd_rows_short(const f32x16 (&a)[2], int mi, int r0, int rows_valid, int n0, int N, int wave,
+                            const BwdEpi& ep) {
+    int lane = __lane_id();
+    __asm__ volatile("" : "+v"(lane));
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int m = mi * 32 + l32;
+    const size_t row = (size_t)(r0 + min(m, rows_valid - 1));
+    const float w = ep.wrow[row];
+    float ds = 0.0f;
+    #pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+        #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int col = n0 + wave * 64 + ni * 32 + q * 8 + lh * 4;
+            const uint2 h1 = *reinterpret_cast<const uint2*>(ep.H1 + row * N + col);
+            const uint2 h3 = *reinterpret_cast<const uint2*>(ep.H3 + row * N + col);
+            u32x4 ga, a1, a3, o1, o3, oa;
+            ga[0] = pack_bf16x2(a[ni][q * 4], a[ni][q * 4 + 1]);
+            ga[1] = pack_bf16x2(a[ni][q * 4 + 2], a[ni][q * 4 + 3]);
+            ga[2] = 0u;
+            ga[3] = 0u;
+            a1 = u32x4{h1.x, h1.y, 0u, 0u};
+            a3 = u32x4{h3.x, h3.y, 0u, 0u};
+            ds += swiglu_bwd_piece(ga, a1, a3, w, o1, o3, oa);
+            if (m < rows_valid) {
+                *reinterpret_cast<uint2*>(ep.dH + row * 2 * N + col) = uint2{o1[0], o1[1]};
+                *reinterpret_cast<uint2*>(ep.dH + row * 2 * N + N + col) = uint2{o3[0], o3[1]};
+                if (ep.aw != nullptr) *reinterpret_cast<uint2*>(ep.aw + row * N + col) = uint2{oa[0], oa[1]};
+            }
+        }
+    }
+    ds += __shfl_xor(ds, 32, kWave);
+    if (m < rows_valid && lh == 0) ep.ds_part[row * (N / 64) + (n0 + wave * 64) / 64] = ds;
+}
+
 // Slot layout: per wave 16 fragments of 16 floats per lane, as float4 vectors
 // [wave][fragment][quarter][lane], so that each store and load is 1 KB per wave.
 MOE_DEV size_t part_index(int wave, int f, int q, int lane) {
@@ -442,13 +602,14 @@ MOE_DEV size_t part_index(int wave, int f, int q, int lane) {
 // A's (256 rows of the N side, 64 bytes of K each) and its fragments are read
 // like A's, so the backward multiplies by W2^T and [W1^T ; W3^T] without
 // transposing the weights first.
-template <bool DUAL, bool BT = false>
+template <bool DUAL, bool BT = false, bool BWD = false>
 __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     uint16_t* __restrict__ C, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     int E, int Kd, int N, int rows, float* __restrict__ part, int* __restrict__ ticket_ctr,
-    const int32_t* __restrict__ gather, int gK, int xrows, int kb) {
+    const int32_t* __restrict__ gather, int gK, int xrows, int kb, BwdEpi bwd) {
     static_assert(!(DUAL && BT), "the k-contiguous B is for the plain GEMM");
+    static_assert(!(DUAL && BWD), "the SwiGLU backward epilogue follows the plain GEMM");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     constexpr int OUTW = DUAL ? 128 : 256;
@@ -746,7 +907,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
 
                 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi) {
-                    if constexpr (PART) {
+                    if constexpr (BWD) {
+                        if (mi == 0) bwd_rows_lds(acc, smem, r0, rows_valid, n0, N, wave, wm, wn, bwd);
+                    } else if constexpr (PART) {
                         f32x4* dst =
                             reinterpret_cast<f32x4*>(part + (size_t)pslot * kPartFloats) + part_index(wave, mi * 4, 0, __lane_id());
                         #pragma unroll
@@ -835,11 +998,16 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                 __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 if (tickets != nullptr) j_next = take();
                 #pragma unroll
-                for (int mi = 0; mi < MI; ++mi) store_rows_short<DUAL>(acc[mi], mi, C, r0, rows_valid, n0, N, wave);
+                for (int mi = 0; mi < MI; ++mi) {
+                    if constexpr (BWD) bwd_rows_short(acc[mi], mi, r0, rows_valid, n0, N, wave, bwd);
+                    else store_rows_short<DUAL>(acc[mi], mi, C, r0, rows_valid, n0, N, wave);
+                }
             }
         };
         using Full = std::integral_constant<int, 0>;
-        if (pslot >= 0) run_tile(std::true_type{}, Full{});
+        if (pslot >= 0) {
+            if constexpr (!BWD) run_tile(std::true_type{}, Full{});  // (no split tail with the fused epilogue)
+        }
         else if (rows_valid <= 32) run_tile(std::false_type{}, std::integral_constant<int, 1>{});
         else if (rows_valid <= 64) run_tile(std::false_type{}, std::integral_constant<int, 2>{});
         else if (rows_valid <= 128) run_tile(std::false_type{}, std::integral_constant<int, 4>{});
@@ -1197,20 +1365,22 @@ int* ffn_tickets(float* part) { return part ? reinterpret_cast<int*>(part + (siz
 int ffn_ticket_ints() { return 2 * kTicketInts; }
 
 // One pipelined GEMM (SwiGLU or plain), then the fixup of its split tail.
-template <bool DUAL, bool BT = false>
+// BWD: the SwiGLU-backward epilogue (`bwd`) instead of a store of C; no split.
+template <bool DUAL, bool BT = false, bool BWD = false>
 static hipError_t launch_pipelined(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                                    const int32_t* counts, const int32_t* offsets, int E, int Kd, int N, int rows,
                                    float* part, bool tickets_zeroed, const int32_t* gather, int gK, int xrows,
-                                   hipStream_t s, int kb = 0) {
-    const hipError_t aerr = hipFuncSetAttribute((const void*)ffn_p4_kernel<DUAL, BT>,
+                                   hipStream_t s, int kb = 0, const BwdEpi& bwd = BwdEpi{}) {
+    if (BWD && part != nullptr) return hipErrorInvalidValue;
+    const hipError_t aerr = hipFuncSetAttribute((const void*)ffn_p4_kernel<DUAL, BT, BWD>,
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
     if (aerr != hipSuccess) return aerr;
     const int G = ffn_grid();
     int* tickets = part != nullptr ? ffn_tickets(part) + (DUAL ? 0 : kTicketInts) : nullptr;
     if (tickets != nullptr && !tickets_zeroed)
         hipLaunchKernelGGL(zero_ints, dim3(1), dim3(kTicketInts), 0, s, tickets, kTicketInts);
-    hipLaunchKernelGGL((ffn_p4_kernel<DUAL, BT>), dim3(G), dim3(kThreads), kP4Lds, s, A, B0, B1, C, counts, offsets,
-                       E, Kd, N, rows, part, tickets, gather, gK, xrows, kb);
+    hipLaunchKernelGGL((ffn_p4_kernel<DUAL, BT, BWD>), dim3(G), dim3(kThreads), kP4Lds, s, A, B0, B1, C, counts,
+                       offsets, E, Kd, N, rows, part, tickets, gather, gK, xrows, kb, bwd);
     if (part != nullptr)
         hipLaunchKernelGGL(ffn_split_fixup<DUAL>, dim3(G), dim3(kThreads), 0, s, part, C, counts, offsets, E, Kd, N,
                            rows, G);
@@ -1303,6 +1473,21 @@ hipError_t launch_ffn_bt(const void* A, const void* B0, const void* B1, int kb, 
     return launch_pipelined<false, true>(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B0),
                                          static_cast<const uint16_t*>(B1), static_cast<uint16_t*>(C), counts, offsets,
                                          E, Kd, N, rows, part, tickets_zeroed, nullptr, 1, 1, s, kb);
+}
+
+// dA = A B0^T per expert (B0 as for launch_ffn_bt with Kd = kb) with the
+// SwiGLU backward fused into the epilogue (BwdEpi): writes dH = [dh1 | dh3],
+// w * act (when aw is not null) and the dS parts ds_part [rows, N / 64];
+// dA itself is not stored.  Pipelined kernel only (ffn_bt_ok(1, N, kb, kb)).
+hipError_t launch_ffn_bt_swiglu_bwd(const void* A, const void* B0, int kb, int rows, int N, int E,
+                                    const int32_t* counts, const int32_t* offsets, const void* H1, const void* H3,
+                                    void* dH, void* aw, const float* wrow, float* ds_part, hipStream_t s) {
+    if (!ffn_bt_ok(1, N, kb, kb)) return hipErrorInvalidValue;
+    const BwdEpi ep{static_cast<const uint16_t*>(H1), static_cast<const uint16_t*>(H3), static_cast<uint16_t*>(dH),
+                    static_cast<uint16_t*>(aw), wrow, ds_part};
+    return launch_pipelined<false, true, true>(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B0),
+                                               nullptr, nullptr, counts, offsets, E, kb, N, rows, nullptr, false,
+                                               nullptr, 1, 1, s, kb, ep);
 }
 
 hipError_t launch_ffn(const void* Xp, const void* W1, const void* W3, const void* W2, int dtype,

@@ -71,6 +71,20 @@ bool ffn_bt_ok(int dtype, int N, int Kd, int kb);
 hipError_t launch_ffn_bt(const void* A, const void* B0, const void* B1, int kb, int dtype, int rows, int N, int E,
                          int Kd, const int32_t* counts, const int32_t* offsets, void* C, float* part,
                          bool tickets_zeroed, hipStream_t s);
+// dA = A B0^T per expert (B0 [E, N, kb], k-contiguous, as launch_ffn_bt with
+// Kd = kb) with the SwiGLU backward in the GEMM's epilogue: for each element,
+// from H1, H3 [rows, N] and the row's routing weight wrow[rows], writes
+// dH [rows, 2N] = [dh1 | dh3], aw [rows, N] = w * act (when not null) and one
+// fp32 dS part per row and 64 columns, ds_part [rows, N / 64]; dA is not
+// stored.  bf16, where ffn_bt_ok(1, N, kb, kb), else hipErrorInvalidValue.
+hipError_t launch_ffn_bt_swiglu_bwd(const void* A, const void* B0, int kb, int rows, int N, int E,
+                                    const int32_t* counts, const int32_t* offsets, const void* H1, const void* H3,
+                                    void* dH, void* aw, const float* wrow, float* ds_part, hipStream_t s);
+// Per expert-sorted row p: wrow[p] = topk_w[sorted_pair[p]]; and the dS of each
+// row from its parts, added in part order: dS_tk[sorted_pair[p]] = sum_j ds_part[p, j].
+hipError_t launch_row_weights(const float* topk_w, const int32_t* sorted_pair, int rows, float* wrow, hipStream_t s);
+hipError_t launch_ds_reduce(const float* ds_part, int nparts, const int32_t* sorted_pair, int rows, float* dS_tk,
+                            hipStream_t s);
 // Expert-weight gradients on the pipelined kernel: dW[e] (M x N fp32) = sum over
 // e's rows r of P[r, 0:M]^T Q[r, qoff:qoff+N]; bf16, where dw_p4_ok(), else
 // hipErrorInvalidValue (rows = the total row count, for the offset range).

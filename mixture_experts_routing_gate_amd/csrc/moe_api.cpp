@@ -901,10 +901,19 @@ int backward_impl(const char* name, const void* X, const float* logits, const vo
     // pre-activations H1 = Xp W1, H3 = Xp W3; dA = dY W2^T (grouped, per expert)
     HIPCHECK(launch_ffn_down(Xp, W1, dtype, (int)A, n, E, d, counts, offsets, H1, part, false, s));
     HIPCHECK(launch_ffn_down(Xp, W3, dtype, (int)A, n, E, d, counts, offsets, H3, part, false, s));
-    if (bt_da) HIPCHECK(launch_ffn_bt(dY, W2, nullptr, d, dtype, (int)A, n, E, d, counts, offsets, dA, part, false, s));
-    else HIPCHECK(launch_ffn_down(dY, W2t, dtype, (int)A, n, E, d, counts, offsets, dA, part, false, s));
-    // SwiGLU backward and dS (and w * act for dW2)
-    HIPCHECK(launch_swiglu_bwd(H1, H3, dA, w, sorted_pair, dtype, (int)A, n, dH, dS, aw, s));
+    if (bt_da) {
+        // dA = dY W2^T with the SwiGLU backward and dS in the GEMM's epilogue
+        // (dA is never stored; its buffer holds the row weights and dS parts)
+        float* wrow = static_cast<float*>(dA);
+        float* ds_part = wrow + align_up(A * sizeof(float)) / sizeof(float);
+        HIPCHECK(launch_row_weights(w, sorted_pair, (int)A, wrow, s));
+        HIPCHECK(launch_ffn_bt_swiglu_bwd(dY, W2, d, (int)A, n, E, counts, offsets, H1, H3, dH, aw, wrow, ds_part, s));
+        HIPCHECK(launch_ds_reduce(ds_part, n / 64, sorted_pair, (int)A, dS, s));
+    } else {
+        HIPCHECK(launch_ffn_down(dY, W2t, dtype, (int)A, n, E, d, counts, offsets, dA, part, false, s));
+        // SwiGLU backward and dS (and w * act for dW2)
+        HIPCHECK(launch_swiglu_bwd(H1, H3, dA, w, sorted_pair, dtype, (int)A, n, dH, dS, aw, s));
+    }
     if (weights) {
         // dW1 = Xp^T dh1, dW3 = Xp^T dh3, dW2 = (w act)^T dY, over each expert's rows
         HIPCHECK(launch_dw(Xp, d, dH, 2 * n, 0, counts, offsets, dtype, E, d, n, (int)A, dW1, s));
