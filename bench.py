@@ -62,6 +62,11 @@ def parse():
     ap.add_argument("--cold", action="store_true", help="with --probe: a read flush before every call")
     ap.add_argument("--copy-probe", action="store_true",
                     help="a plain 512 MiB device copy, for calibrating FETCH_SIZE / WRITE_SIZE, and exit")
+    ap.add_argument("--blas-ref", action="store_true",
+                    help="time the mixtral-shaped grouped GEMMs against hipBLASLt (torch.matmul per expert) on the "
+                         "same rows and weights, each at steady state, and exit")
+    ap.add_argument("--ref-seconds", type=float, default=1.0,
+                    help="with --blas-ref: back-to-back run before each timing")
     return ap.parse_args()
 
 
@@ -193,6 +198,74 @@ def workload_probe(name, cold, moe, synth, torch, dev, reps=3):
         print(json.dumps({"probe": name, "round": r}), flush=True)
 
 
+def blas_reference(moe, synth, torch, dev, seconds, iters=10):
+    """The mixtral-shaped grouped GEMMs next to hipBLASLt, reached through
+    torch.matmul with one GEMM per expert, on the same expert-sorted rows and
+    weights.  The weights are given as stored (n-contiguous) and, for
+    hipBLASLt only, also as k-contiguous copies made beforehand.  The card's
+    clock settles under its power cap within about a second of sustained
+    work, so each candidate first runs back to back for `seconds`, and then
+    the median of `iters` event-timed calls is taken.  The rounds alternate
+    the candidates twice."""
+    cfg = synth.CONFIGS["mixtral"]
+    T, d, E, K, n = cfg.T, cfg.d, cfg.E, cfg.K, cfg.n
+    A = T * K
+    g = synth.make_inputs(cfg, dev, seed=0)
+    idx, w, counts, offsets = moe.moe_route(g["logits"], K)
+    sp, inv, Xp = moe.moe_permute(g["X"], idx, E)
+    W1, W3, W2 = g["W1"], g["W3"], g["W2"]
+    W1t, W3t, W2t = (W.transpose(1, 2).contiguous() for W in (W1, W3, W2))
+    off = offsets.cpu().tolist()
+    segs = [(e, off[e], off[e + 1]) for e in range(E) if off[e + 1] > off[e]]
+    ws = moe.load_library().moe_ffn_workspace_bytes(d, n, moe.dtype_code(Xp.dtype))
+    ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    Act = moe.moe_ffn_up(Xp, W1, W3, counts, offsets, K, ws=ws)
+    Y = moe.moe_ffn_down(Act, W2, counts, offsets, K, ws=ws)
+    H1 = torch.empty(A, n, dtype=Xp.dtype, device=dev)
+    H3 = torch.empty_like(H1)
+    Yb = torch.empty(A, d, dtype=Xp.dtype, device=dev)
+
+    def blas_up(kc):
+        for e, a, b in segs:
+            torch.matmul(Xp[a:b], W1t[e].T if kc else W1[e], out=H1[a:b])
+            torch.matmul(Xp[a:b], W3t[e].T if kc else W3[e], out=H3[a:b])
+
+    def blas_down(kc):
+        for e, a, b in segs:
+            torch.matmul(Act[a:b], W2t[e].T if kc else W2[e], out=Yb[a:b])
+
+    cands = {
+        "up": (4.0 * A * d * n, {
+            "ours": lambda: moe.moe_ffn_up(Xp, W1, W3, counts, offsets, K, ws=ws, out=Act),
+            "hipblaslt_n": lambda: blas_up(False),
+            "hipblaslt_k": lambda: blas_up(True)}),
+        "down": (2.0 * A * d * n, {
+            "ours": lambda: moe.moe_ffn_down(Act, W2, counts, offsets, K, ws=ws, out=Y),
+            "hipblaslt_n": lambda: blas_down(False),
+            "hipblaslt_k": lambda: blas_down(True)}),
+    }
+    res = {}
+    for rnd in range(2):
+        for gemm, (flops, fns) in cands.items():
+            for name, fn in fns.items():
+                t_end = time.perf_counter() + seconds
+                while time.perf_counter() < t_end:
+                    for _ in range(5):
+                        fn()
+                    torch.cuda.synchronize()
+                ms, _ = event_time_ms(torch, fn, iters)
+                r = res.setdefault(gemm, {}).setdefault(name, {"ms": []})
+                r["ms"].append(round(ms, 4))
+                print(json.dumps({"blas_ref_round": rnd, "gemm": gemm, "candidate": name, "ms": round(ms, 4)}),
+                      flush=True)
+    for gemm, (flops, _) in cands.items():
+        for name, r in res[gemm].items():
+            r["tflops"] = [round(flops / (m * 1e-3) / 1e12, 1) for m in r["ms"]]
+            r["frac_of_bf16_peak"] = [round(t / 2500.0, 4) for t in r["tflops"]]
+    return {"workload": "mixtral T=8192 d=4096 E=8 K=2 n=14336 bf16", "steady_state_seconds": seconds,
+            "iters": iters, "gemms": res}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -225,6 +298,9 @@ def main():
         return
     if args.probe:
         workload_probe(args.probe, args.cold, moe, synth, torch, dev)
+        return
+    if args.blas_ref:
+        print(json.dumps({"blas_ref": blas_reference(moe, synth, torch, dev, args.ref_seconds)}), flush=True)
         return
     if args.backward_probe:
         c = synth.CONFIGS["mixtral"]

@@ -245,14 +245,24 @@ def moe_grouped_ffn(Xp: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, W2: to
     return Act, Y
 
 
+def _out(out, shape, dtype, device, name):
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(out.shape) != tuple(shape) or out.dtype != dtype or not out.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    return out
+
+
 def moe_ffn_up(Xp: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, counts: torch.Tensor,
-               offsets: torch.Tensor, K: int, split: bool = True, ws: torch.Tensor | None = None):
-    """Step 4a.  Xp [T*K,d], W1/W3 [E,d,n] -> Act [T*K,n] = SiLU(Xp W1) * (Xp W3)."""
+               offsets: torch.Tensor, K: int, split: bool = True, ws: torch.Tensor | None = None,
+               out: torch.Tensor | None = None):
+    """Step 4a.  Xp [T*K,d], W1/W3 [E,d,n] -> Act [T*K,n] = SiLU(Xp W1) * (Xp W3)
+    (written into `out` when given)."""
     lib = load_library()
     A, d = Xp.shape
     E, _, n = W1.shape
     dev = Xp.device
-    Act = torch.empty((A, n), dtype=Xp.dtype, device=dev)
+    Act = _out(out, (A, n), Xp.dtype, dev, "out")
     wp, wn = ffn_workspace(d, n, Xp.dtype, dev, split, ws)
     _check(lib.moe_ffn_up(_dev(Xp, "Xp"), _dev(W1, "W1", Xp.dtype), _dev(W3, "W3", Xp.dtype), dtype_code(Xp.dtype),
                           A // K, d, E, K, n, _dev(counts, "counts", torch.int32),
@@ -262,13 +272,13 @@ def moe_ffn_up(Xp: torch.Tensor, W1: torch.Tensor, W3: torch.Tensor, counts: tor
 
 
 def moe_ffn_down(Act: torch.Tensor, W2: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor, K: int,
-                 split: bool = True, ws: torch.Tensor | None = None):
-    """Step 4b.  Act [T*K,n], W2 [E,n,d] -> Y [T*K,d] = Act W2."""
+                 split: bool = True, ws: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """Step 4b.  Act [T*K,n], W2 [E,n,d] -> Y [T*K,d] = Act W2 (written into `out` when given)."""
     lib = load_library()
     A, n = Act.shape
     E, _, d = W2.shape
     dev = Act.device
-    Y = torch.empty((A, d), dtype=Act.dtype, device=dev)
+    Y = _out(out, (A, d), Act.dtype, dev, "out")
     wp, wn = ffn_workspace(d, n, Act.dtype, dev, split, ws)
     _check(lib.moe_ffn_down(_dev(Act, "Act"), _dev(W2, "W2", Act.dtype), dtype_code(Act.dtype), A // K, d, E, K, n,
                             _dev(counts, "counts", torch.int32), _dev(offsets, "offsets", torch.int32),

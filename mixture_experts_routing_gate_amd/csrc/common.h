@@ -20,9 +20,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 MOE_DEV uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// Pack two fp32 into one dword of two bf16 (lo in bits 0..15).
+// Pack two fp32 into one dword of two bf16 (lo in bits 0..15), rounded to
+// nearest even as f32_to_bf16 rounds each.  Written as one two-lane conversion
+// so that it becomes a single v_cvt_pk_bf16_f32 of both operands, not two
+// conversions followed by a shift and an OR.
+typedef float f32x2_cv __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cv __attribute__((ext_vector_type(2)));
 MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_cv{lo, hi}, bf16x2_cv));
 }
 
 // Reductions over aligned groups of G consecutive lanes (G a power of two <= 64).

@@ -187,6 +187,37 @@ MOE_DEV bf16x4 lds_read_tr(const char* l) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
+// v_mfma_f32_16x16x32_bf16 with the accumulator held in AGPRs and tied to the
+// result.  Written as inline assembly because with the builtin the register
+// allocator leaves dst and srcC apart in a loop of 64 accumulators and then
+// shuffles them through copies at every step.  The compiler does not see these
+// as MFMAs, so the waits it would insert around them are made by hand: the
+// first K-step uses the zero-accumulator form (no VALU write of the
+// accumulators precedes an MFMA that reads them), the loaded operands reach
+// the MFMAs straight from LDS reads (waited for by the compiler, which tracks
+// the asm operands), and mfma16_drain separates the last MFMA from any read of
+// its results by more wait states than the MFMA's passes.
+MOE_DEV void mfma16(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+    __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+MOE_DEV void mfma16_first(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+    __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+}
+MOE_DEV void mfma16_drain(f32x4 (&acc)[8][8]) {
+    __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[0][4]),
+                       "+a"(acc[0][5]), "+a"(acc[0][6]), "+a"(acc[0][7]), "+a"(acc[1][0]), "+a"(acc[1][1]),
+                       "+a"(acc[1][2]), "+a"(acc[1][3]), "+a"(acc[1][4]), "+a"(acc[1][5]), "+a"(acc[1][6]),
+                       "+a"(acc[1][7]));
+    #pragma unroll
+    for (int mi = 2; mi < 8; mi += 2)
+        __asm__ volatile(""
+                         : "+a"(acc[mi][0]), "+a"(acc[mi][1]), "+a"(acc[mi][2]), "+a"(acc[mi][3]), "+a"(acc[mi][4]),
+                           "+a"(acc[mi][5]), "+a"(acc[mi][6]), "+a"(acc[mi][7]), "+a"(acc[mi + 1][0]),
+                           "+a"(acc[mi + 1][1]), "+a"(acc[mi + 1][2]), "+a"(acc[mi + 1][3]), "+a"(acc[mi + 1][4]),
+                           "+a"(acc[mi + 1][5]), "+a"(acc[mi + 1][6]), "+a"(acc[mi + 1][7]));
+}
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel with a 5-stage LDS pipeline (used when d % 256 == 0 and
 // n % 128 == 0).  Tiles of 256 x 256 per CU, 4 waves of 128 x 128, K advancing
@@ -304,36 +335,37 @@ MOE_DEV SplitPlan split_plan(int total, int G, int KT, bool enabled) {
 }
 constexpr int kPartFloats = 256 * 256;  // one 256 x 256 fp32 tile per slot
 
-// Output of one 32-row slice mi of a wave's 128 x 128 quadrant from its four
-// accumulators: bf16, rows past rows_valid skipped; with DUAL, the pairs
-// (ni, ni + 2) are (W1 part, W3 part) and give SiLU(W1 part) * (W3 part).
+// Output of one 32-row slice sl of a wave's 128 x 128 quadrant (row blocks
+// 2sl, 2sl+1 of 16) from the 16x16x32 accumulators a[mm][ni]: lane l holds row
+// l%16 of block mm and output columns ni*16 + 4*(l/16) .. +3; bf16, rows past
+// rows_valid skipped.  With DUAL, a[mm][ni] (ni < 4) is the W1 part and
+// a[mm][ni + 4] the W3 part of the same columns, giving SiLU(W1 part) * (W3 part).
 // (The lane index is re-derived here rather than kept live from the kernel's
 // start: after the K-loop registers are scarce, and a spilled lane index would
 // cost a scratch reload per tile.)
 template <bool DUAL>
-MOE_DEV void store_rows(const f32x16 (&a)[4], int mi, uint16_t* __restrict__ C, int r0, int rows_valid, int n0,
+MOE_DEV void store_rows(const f32x4 (&a)[2][8], int sl, uint16_t* __restrict__ C, int r0, int rows_valid, int n0,
                         int N, int wm, int wn) {
     int lane = __lane_id();
     __asm__ volatile("" : "+v"(lane));  // keeps the row math here instead of hoisted (and spilled)
-    const int l32 = lane & 31, lh = lane >> 5;
-    const int m = wm * 128 + mi * 32 + l32;
-    if (m < rows_valid) {
-        uint16_t* crow = C + (size_t)(r0 + m) * N;
-        #pragma unroll
-        for (int ni = 0; ni < (DUAL ? 2 : 4); ++ni) {
+    const int s16 = lane & 15, g16 = lane >> 4;
+    #pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+        const int m = wm * 128 + sl * 32 + mm * 16 + s16;
+        if (m < rows_valid) {
+            uint16_t* crow = C + (size_t)(r0 + m) * N + n0 + (DUAL ? wn * 64 : wn * 128) + 4 * g16;
             #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int ni = 0; ni < (DUAL ? 4 : 8); ++ni) {
                 float v[4];
                 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    v[j] = a[ni][q * 4 + j];
-                    if (DUAL) v[j] = silu_mul(v[j], a[ni + 2][q * 4 + j]);
+                    v[j] = a[mm][ni][j];
+                    if (DUAL) v[j] = silu_mul(v[j], a[mm][ni + 4][j]);
                 }
-                const int col = n0 + (DUAL ? wn * 64 + ni * 32 : wn * 128 + ni * 32) + q * 8 + lh * 4;
                 uint2 pk;
                 pk.x = pack_bf16x2(v[0], v[1]);
                 pk.y = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<uint2*>(crow + col) = pk;
+                *reinterpret_cast<uint2*>(crow + ni * 16) = pk;
             }
         }
     }
@@ -344,43 +376,53 @@ MOE_DEV void store_rows(const f32x16 (&a)[4], int mi, uint16_t* __restrict__ C, 
 // the parts of it that only this wave's DMAs fill, so no other wave's reads
 // or loads touch them -- and read back as 16-byte pieces of whole row
 // segments, so that each store instruction writes 4 rows of 256 bytes (8 rows
-// of 128 bytes for the SwiGLU GEMM) instead of 32 rows of 16 bytes.  Staged
+// of 128 bytes for the SwiGLU GEMM) instead of 64 pieces of 8 bytes.  Staged
 // rows are XOR-swizzled by 16-byte piece so that writes and reads are free of
 // bank conflicts.  Every wave must be done reading the stages, and this wave's
 // own loads into them must be complete.
+// Staged row r: SwiGLU rows at wave*4K + r*128; otherwise rows 0..15 at
+// wave*4K + r*256 and rows 16..31 at 16K + wave*4K + (r-16)*256.
 template <bool DUAL>
-MOE_DEV void store_rows_lds(const f32x16 (&a)[4], int mi, char* smem, uint16_t* __restrict__ C, int r0,
-                            int rows_valid, int n0, int N, int wave, int wm, int wn) {
-    int lane = __lane_id();
-    __asm__ volatile("" : "+v"(lane));
-    const int l32 = lane & 31, lh = lane >> 5;
-    constexpr int CH = DUAL ? 8 : 16;   // 16-byte pieces per staged row (64 or 128 columns)
-    constexpr int RPI = kWave / CH;     // rows per store instruction
-    // Staged row r: SwiGLU rows at wave*4K + r*128; otherwise rows 0..15 at
-    // wave*4K + r*256 and rows 16..31 at 16K + wave*4K + (r-16)*256.
-    auto row_at = [&](int r) -> char* {
-        return DUAL ? smem + wave * 4096 + r * 128
-                    : smem + (r >> 4) * 16384 + wave * 4096 + (r & 15) * 256;
-    };
-    auto swz = [](int r, int c) { return DUAL ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15)); };
-    char* wr = row_at(l32);
+MOE_DEV char* staged_row(char* smem, int wave, int r) {
+    return DUAL ? smem + wave * 4096 + r * 128 : smem + (r >> 4) * 16384 + wave * 4096 + (r & 15) * 256;
+}
+template <bool DUAL>
+MOE_DEV int staged_swz(int r, int c) { return DUAL ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15)); }
+
+// Writes slice sl of the accumulators to the staging rows, rounded to bf16 (with
+// DUAL, SiLU(W1 part) * (W3 part) first).  Lane l writes row (l%16) of each
+// block, 8 bytes per column block: staged columns ni*16 + 4*(l/16) .. +3.
+template <bool DUAL>
+MOE_DEV void stage_slice(const f32x4 (&acc)[8][8], int sl, char* smem, int wave, int s16, int g16) {
     #pragma unroll
-    for (int ni = 0; ni < (DUAL ? 2 : 4); ++ni) {
+    for (int mm = 0; mm < 2; ++mm) {
+        const int r = mm * 16 + s16;
+        char* wr = staged_row<DUAL>(smem, wave, r);
         #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int ni = 0; ni < (DUAL ? 4 : 8); ++ni) {
             float v[4];
             #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                v[j] = a[ni][q * 4 + j];
-                if (DUAL) v[j] = silu_mul(v[j], a[ni + 2][q * 4 + j]);
+                v[j] = acc[2 * sl + mm][ni][j];
+                if (DUAL) v[j] = silu_mul(v[j], acc[2 * sl + mm][ni + 4][j]);
             }
             uint2 pk;
             pk.x = pack_bf16x2(v[0], v[1]);
             pk.y = pack_bf16x2(v[2], v[3]);
-            const int c = ni * 4 + q;  // column (ni*32 + q*8 + lh*4) / 8
-            *reinterpret_cast<uint2*>(wr + swz(l32, c) * 16 + lh * 8) = pk;
+            const int c = ni * 2 + (g16 >> 1);  // 16-byte piece of the staged row
+            *reinterpret_cast<uint2*>(wr + staged_swz<DUAL>(r, c) * 16 + (g16 & 1) * 8) = pk;
         }
     }
+}
+
+template <bool DUAL>
+MOE_DEV void store_rows_lds(const f32x4 (&acc)[8][8], int sl, char* smem, uint16_t* __restrict__ C, int r0,
+                            int rows_valid, int n0, int N, int wave, int wm, int wn) {
+    int lane = __lane_id();
+    __asm__ volatile("" : "+v"(lane));
+    constexpr int CH = DUAL ? 8 : 16;   // 16-byte pieces per staged row (64 or 128 columns)
+    constexpr int RPI = kWave / CH;     // rows per store instruction
+    stage_slice<DUAL>(acc, sl, smem, wave, lane & 15, lane >> 4);
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int c = lane % CH;
     const int colb = n0 + (DUAL ? wn * 64 : wn * 128) + c * 8;
@@ -388,12 +430,12 @@ MOE_DEV void store_rows_lds(const f32x16 (&a)[4], int mi, char* smem, uint16_t* 
     #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
         const int r = i * RPI + lane / CH;
-        val[i] = *reinterpret_cast<const u32x4*>(row_at(r) + swz(r, c) * 16);
+        val[i] = *reinterpret_cast<const u32x4*>(staged_row<DUAL>(smem, wave, r) + staged_swz<DUAL>(r, c) * 16);
     }
     #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
         const int r = i * RPI + lane / CH;
-        const int m = wm * 128 + mi * 32 + r;
+        const int m = wm * 128 + sl * 32 + r;
         if (m < rows_valid) *reinterpret_cast<u32x4*>(C + (size_t)(r0 + m) * N + colb) = val[i];
     }
 }
@@ -486,14 +528,13 @@ MOE_DEV float swiglu_bwd_piece(const u32x4& ga, const u32x4& a1, const u32x4& a3
 // Lanes 16q..16q+15 hold one row's 128 columns (8 per lane); each half of them
 // (64 columns) adds its dS parts with three butterfly steps, and the first
 // lane of the half writes the slot.
-MOE_DEV void bwd_rows_lds(const f32x16 (&acc)[4][4], char* smem, int r0, int rows_valid, int n0, int N, int wave,
+MOE_DEV void bwd_rows_lds(const f32x4 (&acc)[8][8], char* smem, int r0, int rows_valid, int n0, int N, int wave,
                           int wm, int wn, const BwdEpi& ep) {
     int lane = __lane_id();
     __asm__ volatile("" : "+v"(lane));
-    const int l32 = lane & 31, lh = lane >> 5;
     constexpr int CH = 16, RPI = kWave / CH, NI = 32 / RPI;
-    auto row_at = [&](int r) -> char* { return smem + (r >> 4) * 16384 + wave * 4096 + (r & 15) * 256; };
-    auto swz = [](int r, int c) { return c ^ (r & 15); };
+    auto row_at = [&](int r) -> char* { return staged_row<false>(smem, wave, r); };
+    auto swz = [](int r, int c) { return staged_swz<false>(r, c); };
     const int c = lane % CH;
     const int col = n0 + wn * 128 + c * 8;
     const int nslots = N / 64;
@@ -515,17 +556,7 @@ MOE_DEV void bwd_rows_lds(const f32x16 (&acc)[4][4], char* smem, int r0, int row
     for (int mi = 0; mi < 4; ++mi) {
         const int buf = mi & 1;
         if (mi + 1 < 4) fetch(mi + 1, buf ^ 1);
-        char* wr = row_at(l32);
-        #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint2 pk;
-                pk.x = pack_bf16x2(acc[mi][ni][q * 4], acc[mi][ni][q * 4 + 1]);
-                pk.y = pack_bf16x2(acc[mi][ni][q * 4 + 2], acc[mi][ni][q * 4 + 3]);
-                *reinterpret_cast<uint2*>(wr + swz(l32, ni * 4 + q) * 16 + lh * 8) = pk;
-            }
-        }
+        stage_slice<false>(acc, mi, smem, wave, lane & 15, lane >> 4);
         __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         u32x4 ga[NI];
         #pragma unroll
@@ -590,10 +621,11 @@ MOE_DEV void bwd_rows_short(const f32x16 (&a)[2], int mi, int r0, int rows_valid
     if (m < rows_valid && lh == 0) ep.ds_part[row * (N / 64) + (n0 + wave * 64) / 64] = ds;
 }
 
-// Slot layout: per wave 16 fragments of 16 floats per lane, as float4 vectors
-// [wave][fragment][quarter][lane], so that each store and load is 1 KB per wave.
-MOE_DEV size_t part_index(int wave, int f, int q, int lane) {
-    return ((size_t)((wave * 16 + f) * 4 + q) * kWave + lane);
+// Slot layout: per wave the 8 x 8 accumulator blocks of 4 floats per lane, as
+// float4 vectors [wave][row block][column block][lane], so that each store and
+// load is 1 KB per wave.
+MOE_DEV size_t part_index(int wave, int mi, int ni, int lane) {
+    return ((size_t)((wave * 8 + mi) * 8 + ni) * kWave + lane);
 }
 
 // BT (plain GEMM only): B is given k-contiguous, as the transpose of each
@@ -631,29 +663,37 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     int* const tickets = (ticket_ctr != nullptr && 8 * count_short_tiles(counts, E, NT, rows, lane) > total)
                              ? ticket_ctr : nullptr;
 
-    // LDS fragment addresses (byte offsets into a stage).
-    // A row r, k-chunk c of 8 elements sits at r*64 + ((c ^ ((r/4)%4)) * 16).
-    const int arow = wm * 128 + l32;
-    int a_rd[2];
-    #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) a_rd[ks] = arow * 64 + (((ks * 2 + lh) ^ ((arow >> 2) & 3)) << 4);
-    // B k-row k, column n of half h sits at 16K + h*8K + k*256 + (((n/8) ^ 4*(k%4)) * 16) + (n%8)*2.
+    // LDS fragment addresses (byte offsets into a stage).  Whole tiles run on
+    // v_mfma_f32_16x16x32_bf16, where lane l supplies row (or output column)
+    // l%16 of a 16-wide block at k = 8*(l/16) .. 8*(l/16)+7 of the step's 32.
+    // Under the card's power cap this form sustains a higher clock than
+    // 32x32x16 for the same work (measured with both on register data:
+    // 2.02 against 1.77 GHz at 96% MFMA busy).  Short tiles use 32x32x16.
+    // A row r, k-chunk c of 8 elements sits at r*64 + ((c ^ ((r/4)%4)) * 16);
+    // fragment mi (rows wm*128 + mi*16 ..) at a16_rd + mi*1024.
+    const int a16_rd = (wm * 128 + s16) * 64 + ((g16 ^ ((s16 >> 2) & 3)) << 4);
+    // B k-row k, column n of half h sits at 16K + h*8K + k*256 + (n%8)*2 +
+    // ((n/8) ^ 4*(k%4) ^ 2*((k/8)%2)) * 16.  The transposing read gives lane l
+    // column l%16 of a 16-column block at four consecutive k-rows: lane c of a
+    // 16-lane group addresses k-row c/4 and columns 4*(c%4) .. +3.  The XOR
+    // terms keep the 16-byte pieces that one read instruction touches in
+    // distinct banks.
     const int b_x = (s16 >> 2) << 2;
-    const int b_c = (g16 & 1) * 2 + ((s16 & 3) >> 1);
-    const int b_lane = 16384 + ((g16 >> 1) * 8 + (s16 >> 2)) * 256 + (s16 & 1) * 8;
-    int b_rd[4];
+    const int b16_lane = 16384 + (g16 * 8 + (s16 >> 2)) * 256 + (s16 & 1) * 8;
+    int b16_rd[8];
     #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-        const int half = DUAL ? (ni >> 1) : wn;
-        const int nn = DUAL ? (wn * 64 + (ni & 1) * 32) : ni * 32;
-        b_rd[ni] = b_lane + half * 8192 + ((((nn >> 3) ^ b_x) + b_c) << 4);
+    for (int ni = 0; ni < 8; ++ni) {
+        const int half = DUAL ? (ni >> 2) : wn;
+        const int nn = DUAL ? (wn * 64 + (ni & 3) * 16) : ni * 16;
+        b16_rd[ni] = b16_lane + half * 8192 + ((((nn >> 3) ^ b_x ^ ((g16 & 1) << 1)) + ((s16 & 3) >> 1)) << 4);
     }
     // BT: B row (output column) c, k-chunk q sits at 16K + c*64 + ((q ^ ((c/4)%4)) * 16),
-    // as A's rows do; fragment ni of sub-step ks at bt_rd[ks] + ni*32*64.
-    int bt_rd[2];
-    #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-        bt_rd[ks] = 16384 + (wn * 128 + l32) * 64 + (((ks * 2 + lh) ^ ((l32 >> 2) & 3)) << 4);
+    // as A's rows do; fragment ni at bt16_rd + ni*1024.
+    const int bt16_rd = 16384 + (wn * 128 + s16) * 64 + ((g16 ^ ((s16 >> 2) & 3)) << 4);
+    // Short tiles (32x32x16): lane l covers column l%32 at k = 8*(l/32) .. +7 of a
+    // 16-k sub-step, so its k-rows have bit 3 = l/32.
+    const int b_c = ((g16 & 1) * 2 + ((s16 & 3) >> 1)) ^ ((g16 >> 1) << 1);
+    const int b_lane = 16384 + ((g16 >> 1) * 8 + (s16 >> 2)) * 256 + (s16 & 1) * 8;
 
     const uint32_t lds_base = uniform((int)(uint32_t)(uintptr_t)(lds_void*)smem);
     const int G = gridDim.x;
@@ -745,7 +785,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                     gather != nullptr ? (uint32_t)min(max(gather[r0 + rr], 0) / gK, xrows - 1) : (uint32_t)rr;
                 a_vo[i] = (arow * (uint32_t)Kd + ch * 8) * 2u;
                 const int kr = (wave & 1) * 16 + i * 4 + (lane >> 4);
-                const int bc = (lane & 15) ^ ((kr & 3) << 2);
+                const int bc = (lane & 15) ^ ((kr & 3) << 2) ^ (((kr >> 3) & 1) << 1);
                 const int col = (DUAL ? n0 : n0 + half * 128) + bc * 8;
                 b_vo[i] = BT ? ((uint32_t)(n0 + r) * (uint32_t)kb + ch * 8) * 2u
                              : ((uint32_t)kr * (uint32_t)N + col) * 2u;
@@ -769,36 +809,37 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
             };
 
             if constexpr (MI == 0) {
-                f32x16 acc[4][4];
-                #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni)
-                        #pragma unroll
-                        for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
-
-                bf16x8 af[2][4], bfr[2][4];
-                auto load_frags = [&](int soff, int ks, int buf) {
-                    const char* sa = smem + soff + a_rd[ks];
-                    #pragma unroll
-                    for (int mi = 0; mi < 4; ++mi) af[buf][mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * 64);
-                    #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        if constexpr (BT) {
-                            bfr[buf][ni] = *reinterpret_cast<const bf16x8*>(smem + soff + bt_rd[ks] + ni * 32 * 64);
-                        } else {
-                            const char* pb = smem + soff + b_rd[ni] + ks * 16 * 256;
-                            const bf16x4 h0 = lds_read_tr(pb);
-                            const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
-                            bfr[buf][ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-                        }
+                // acc[mi][ni]: rows mi*16.. of the wave's 128 by output columns
+                // ni*16.. of its 128 (SwiGLU: ni < 4 the W1 part, ni >= 4 the W3
+                // part of the same columns).  A step of K = 32 is one MFMA per
+                // block, in two halves (column blocks 0..3, then 4..7), each row
+                // block by row block.  Fragments are reloaded in place one half
+                // ahead: B fragments 4..7 of a step under its first half, and in
+                // the second half, right after row block mi's last MFMA of the
+                // step, that row's A fragment of the next step, along with the
+                // next step's B fragments 0..3.
+                f32x4 acc[8][8];
+                bf16x8 af[8], bfr[8];
+                auto load_a = [&](int soff, int mi) {
+                    af[mi] = *reinterpret_cast<const bf16x8*>(smem + soff + a16_rd + mi * 1024);
+                };
+                auto load_b = [&](int soff, int ni) {
+                    if constexpr (BT) {
+                        bfr[ni] = *reinterpret_cast<const bf16x8*>(smem + soff + bt16_rd + ni * 1024);
+                    } else {
+                        const char* pb = smem + soff + b16_rd[ni];
+                        const bf16x4 h0 = lds_read_tr(pb);
+                        const bf16x4 h1 = lds_read_tr(pb + 4 * 256);
+                        bfr[ni] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
                     }
                 };
-                auto mfma = [&](int buf, int lo, int hi) {
+                // The four MFMAs of row block mi in half h (column blocks 4h .. 4h+3);
+                // with z the accumulators start from zero (the first K-step).
+                auto mfma_row = [&](int h, int mi, bool z) {
                     #pragma unroll
-                    for (int q = lo; q < hi; ++q) {
-                        const int mi = q >> 2, ni = q & 3;
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
+                    for (int j = 0; j < 4; ++j) {
+                        if (z) mfma16_first(acc[mi][4 * h + j], bfr[4 * h + j], af[mi]);
+                        else mfma16(acc[mi][4 * h + j], bfr[4 * h + j], af[mi]);
                     }
                 };
 
@@ -809,95 +850,51 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                 issue(3, 3 * kP4Stage);
                 __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
                 __syncthreads();
-                load_frags(0, 0, 0);
+                #pragma unroll
+                for (int mi = 0; mi < 8; ++mi) load_a(0, mi);
+                #pragma unroll
+                for (int ni = 0; ni < 4; ++ni) load_b(0, ni);
 
+                // One K-step per loop iteration: unrolled, the reloads in place
+                // defeat the register allocator's coalescing of the accumulators.
                 int s_cur = 0;  // byte offset of step kt's stage
-                for (int kt0 = 0; kt0 < ksn; kt0 += 4) {
-                    #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int kt = kt0 + u;
+                auto kstep = [&](int kt, auto first_tag) {
+                    constexpr bool Z = decltype(first_tag)::value;
+                    {
                         const int s_nxt = s_cur == (kP4Stages - 1) * kP4Stage ? 0 : s_cur + kP4Stage;
                         const int s_old = s_cur == 0 ? (kP4Stages - 1) * kP4Stage : s_cur - kP4Stage;
-                        // Step boundary: own DMA of step kt+1 done (16 younger ones may fly).
+                        // Step boundary: own DMA of step kt+1 done (16 younger ones may
+                        // fly), then the barrier.  No wait for this wave's LDS reads: the
+                        // reads still in flight are of step kt+1's stage, and the stage
+                        // refilled below (step kt-1's) was last read by fragments that
+                        // step kt-1's MFMAs have consumed.
                         __builtin_amdgcn_sched_barrier(0);
-                        __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
-                        __syncthreads();
-                        // Refill the stage of step kt-1 with step kt+4.  SwiGLU GEMM: one
-                        // DMA per MFMA right after the barrier.  Plain GEMM: four DMAs
-                        // over the first 8 MFMAs of each sub-step, so that a DMA held
-                        // up by a full address queue delays fewer MFMAs (measured on the
-                        // mixtral-shaped down GEMM: 1.55 -> 1.43 ms; the SwiGLU GEMM was
-                        // unchanged by any placement tried).
+                        __asm__ volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+                        // Refill the stage of step kt-1 with step kt+4: one DMA before
+                        // each of the first four row blocks of each half, so that a DMA
+                        // held up by a full address queue delays few MFMAs.
                         const int kn = min(kt + 4, ksn - 1);
-                        if constexpr (DUAL) {
-                            #pragma unroll
-                            for (int i = 0; i < 8; ++i) {
-                                issue_one(kn, s_old, i);
-                                mfma(0, i, i + 1);
-                                __builtin_amdgcn_sched_barrier(0);
-                            }
-                        } else {
-                            #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                issue_one(kn, s_old, i);
-                                mfma(0, 2 * i, 2 * i + 2);
-                                __builtin_amdgcn_sched_barrier(0);
-                            }
+                        #pragma unroll
+                        for (int mi = 0; mi < 8; ++mi) {
+                            if (mi < 4) issue_one(kn, s_old, mi);
+                            mfma_row(0, mi, Z);
+                            if (mi < 4) load_b(s_cur, 4 + mi);
+                            __builtin_amdgcn_sched_barrier(0);
                         }
-                        // Rest of sub-step 0 while sub-step 1's fragments are read.
-                        load_frags(s_cur, 1, 1);
-                        mfma(0, 8, 16);
-                        // 12 LDS reads per sub-step (8 with BT) spread over the MFMAs.
-                        if constexpr (BT) {
-                            #pragma unroll
-                            for (int i = 0; i < 8; ++i) {
-                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                            }
-                        } else {
-                            #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                            }
-                            #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                            }
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                        constexpr int kReads = BT ? 8 : 12;
-                        if constexpr (DUAL) {
-                            // Sub-step 1 while the next step's sub-step-0 fragments are read.
-                            load_frags(s_nxt, 0, 0);
-                            mfma(1, 0, 16);
-                            #pragma unroll
-                            for (int i = 0; i < kReads; ++i) {
-                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                            }
-                            __builtin_amdgcn_sched_group_barrier(0x008, 16 - kReads, 0);
-                        } else {
-                            // The other four DMAs over sub-step 1's first 8 MFMAs, then
-                            // the next step's sub-step-0 fragments under its last 8.
-                            #pragma unroll
-                            for (int i = 4; i < 8; ++i) {
-                                issue_one(kn, s_old, i);
-                                mfma(1, 2 * (i - 4), 2 * (i - 4) + 2);
-                                __builtin_amdgcn_sched_barrier(0);
-                            }
-                            load_frags(s_nxt, 0, 0);
-                            mfma(1, 8, 16);
-                            #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                __builtin_amdgcn_sched_group_barrier(0x100, kReads / 4, 0);
-                                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                            }
+                        #pragma unroll
+                        for (int mi = 0; mi < 8; ++mi) {
+                            if (mi < 4) issue_one(kn, s_old, 4 + mi);
+                            mfma_row(1, mi, Z);
+                            load_a(s_nxt, mi);
+                            if (mi >= 2 && mi < 6) load_b(s_nxt, mi - 2);
+                            __builtin_amdgcn_sched_barrier(0);
                         }
                         s_cur = s_nxt;
                     }
-                }
+                };
+                kstep(0, std::true_type{});
+                for (int kt = 1; kt < ksn; ++kt) kstep(kt, std::false_type{});
+                mfma16_drain(acc);
                 // The clamped refills of the last steps are still in flight.
                 __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 // Every wave is done reading the stages (the staged epilogue below
@@ -906,21 +903,19 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                 else __syncthreads();
 
                 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
+                for (int sl = 0; sl < 4; ++sl) {  // 32-row slices: row blocks 2sl, 2sl+1
                     if constexpr (BWD) {
-                        if (mi == 0) bwd_rows_lds(acc, smem, r0, rows_valid, n0, N, wave, wm, wn, bwd);
+                        if (sl == 0) bwd_rows_lds(acc, smem, r0, rows_valid, n0, N, wave, wm, wn, bwd);
                     } else if constexpr (PART) {
-                        f32x4* dst =
-                            reinterpret_cast<f32x4*>(part + (size_t)pslot * kPartFloats) + part_index(wave, mi * 4, 0, __lane_id());
+                        f32x4* dst = reinterpret_cast<f32x4*>(part + (size_t)pslot * kPartFloats);
+                        const int ln = __lane_id();
                         #pragma unroll
-                        for (int ni = 0; ni < 4; ++ni)
+                        for (int mm = 0; mm < 2; ++mm)
                             #pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                const f32x16& av = acc[mi][ni];
-                                dst[(ni * 4 + q) * kWave] = f32x4{av[q * 4], av[q * 4 + 1], av[q * 4 + 2], av[q * 4 + 3]};
-                            }
+                            for (int ni = 0; ni < 8; ++ni)
+                                dst[part_index(wave, 2 * sl + mm, ni, ln)] = acc[2 * sl + mm][ni];
                     } else {
-                        store_rows_lds<DUAL>(acc[mi], mi, smem, C, r0, rows_valid, n0, N, wave, wm, wn);
+                        store_rows_lds<DUAL>(acc, sl, smem, C, r0, rows_valid, n0, N, wave, wm, wn);
                     }
                 }
             } else {
@@ -1212,31 +1207,31 @@ __global__ __launch_bounds__(kThreads) void ffn_split_fixup(const float* __restr
     if (sp.S == 1) return;
     // one work unit per (split tile, 32-row slice of every wave's quadrant)
     for (int u = blockIdx.x; u < sp.Tr * 4; u += gridDim.x) {
-        const int i = u >> 2, mi = u & 3;
+        const int i = u >> 2, sl = u & 3;
         TileGeom tg;
         if (!tile_geom(counts, offsets, E, NT, OUTW, rows, lane, sp.R * G + i, tg)) return;
         if (tg.rows_valid <= 0) continue;
         const f32x4* src = reinterpret_cast<const f32x4*>(part + (size_t)i * sp.S * kPartFloats);
-        f32x16 acc[4];
+        f32x4 acc[2][8];
         #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int mm = 0; mm < 2; ++mm)
             #pragma unroll
-            for (int c = 0; c < 16; ++c) acc[ni][c] = 0.0f;
+            for (int ni = 0; ni < 8; ++ni) acc[mm][ni] = f32x4{};
         for (int j = 0; j < sp.S; ++j) {  // parts in slot order
-            f32x4 v[16];
+            f32x4 v[2][8];
             #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
+            for (int mm = 0; mm < 2; ++mm)
                 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    v[ni * 4 + q] = src[(size_t)j * (kPartFloats / 4) + part_index(wave, mi * 4 + ni, q, lane)];
+                for (int ni = 0; ni < 8; ++ni)
+                    v[mm][ni] = src[(size_t)j * (kPartFloats / 4) + part_index(wave, 2 * sl + mm, ni, lane)];
             #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
+            for (int mm = 0; mm < 2; ++mm)
                 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int ni = 0; ni < 8; ++ni)
                     #pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[ni][q * 4 + c] += v[ni * 4 + q][c];
+                    for (int c = 0; c < 4; ++c) acc[mm][ni][c] += v[mm][ni][c];
         }
-        store_rows<DUAL>(acc, mi, C, tg.r0, tg.rows_valid, tg.n0, N, wm, wn);
+        store_rows<DUAL>(acc, sl, C, tg.r0, tg.rows_valid, tg.n0, N, wm, wn);
     }
 }
 
