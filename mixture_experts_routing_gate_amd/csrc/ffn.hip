@@ -1034,17 +1034,17 @@ __global__ __launch_bounds__(kThreads, 1) void dw_p4_kernel(
     const int lane = tid & (kWave - 1);
     const int wave = uniform(tid / kWave);
     const int wm = wave >> 1, wn = wave & 1;
-    const int l32 = lane & 31, lh = lane >> 5;
     const int g16 = lane >> 4, s16 = lane & 15;
-    // Fragment reads: column c of half h of an operand staged at X (P at 0,
-    // Q at 16K) sits at X + h*8K + k*256 + (((c/8) ^ 4*(k%4)) * 16) + (c%8)*2.
+    // Fragment reads (v_mfma_f32_16x16x32_bf16, as the forward kernel's whole
+    // tiles): column c of half h of an operand staged at X (P at 0, Q at 16K)
+    // sits at X + h*8K + k*256 + ((c/8) ^ 4*(k%4) ^ 2*((k/8)%2)) * 16 + (c%8)*2;
+    // lane l reads column l%16 of a 16-column block at k = 8*(l/16) .. +7.
     const int b_x = (s16 >> 2) << 2;
-    const int b_c = (g16 & 1) * 2 + ((s16 & 3) >> 1);
-    const int rd_lane = ((g16 >> 1) * 8 + (s16 >> 2)) * 256 + (s16 & 1) * 8;
-    int p_rd[4], q_rd[4];
+    const int rd_lane = (g16 * 8 + (s16 >> 2)) * 256 + (s16 & 1) * 8;
+    int p_rd[8], q_rd[8];
     #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int piece = ((((i * 32) >> 3) ^ b_x) + b_c) << 4;
+    for (int i = 0; i < 8; ++i) {
+        const int piece = ((((i * 16) >> 3) ^ b_x ^ ((g16 & 1) << 1)) + ((s16 & 3) >> 1)) << 4;
         p_rd[i] = rd_lane + wm * 8192 + piece;
         q_rd[i] = 16384 + rd_lane + wn * 8192 + piece;
     }
@@ -1072,7 +1072,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_p4_kernel(
         #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int kr = (wave & 1) * 16 + i * 4 + (lane >> 4);
-            const int col = (wave >> 1) * 128 + (((lane & 15) ^ ((kr & 3) << 2)) << 3);
+            const int col = (wave >> 1) * 128 + (((lane & 15) ^ ((kr & 3) << 2) ^ (((kr >> 3) & 1) << 1)) << 3);
             p_vo[i] = ((uint32_t)kr * (uint32_t)ldp + (uint32_t)(m0 + col)) * 2u;
             q_vo[i] = ((uint32_t)kr * (uint32_t)ldq + (uint32_t)(n0 + col)) * 2u;
         }
@@ -1086,104 +1086,83 @@ __global__ __launch_bounds__(kThreads, 1) void dw_p4_kernel(
             #pragma unroll
             for (int i = 0; i < 8; ++i) issue_one(kt, soff, i);
         };
-        f32x16 acc[4][4];
-        #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-            #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+        // acc[mi][ni]: rows (M) mi*16.. and columns (N) ni*16.. of the wave's
+        // 128 x 128 quadrant; the K-loop is the forward kernel's whole-tile loop.
+        f32x4 acc[8][8];
         if (ksn > 0) {  // (uniform over the workgroup: one expert per tile)
-        bf16x8 af[2][4], bfr[2][4];
-        auto load_frags = [&](int soff, int ks, int buf) {
+            bf16x8 af[8], bfr[8];
+            auto load_p = [&](int soff, int mi) {
+                const char* pa = smem + soff + p_rd[mi];
+                af[mi] = __builtin_shufflevector(lds_read_tr(pa), lds_read_tr(pa + 4 * 256), 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            auto load_q = [&](int soff, int ni) {
+                const char* pb = smem + soff + q_rd[ni];
+                bfr[ni] = __builtin_shufflevector(lds_read_tr(pb), lds_read_tr(pb + 4 * 256), 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            auto mfma_row = [&](int h, int mi, bool z) {
+                #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (z) mfma16_first(acc[mi][4 * h + j], bfr[4 * h + j], af[mi]);
+                    else mfma16(acc[mi][4 * h + j], bfr[4 * h + j], af[mi]);
+                }
+            };
+            issue(0, 0);
+            issue(1, kP4Stage);
+            issue(2, 2 * kP4Stage);
+            issue(3, 3 * kP4Stage);
+            __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
+            __syncthreads();
             #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const char* pa = smem + soff + p_rd[i] + ks * 16 * 256;
-                af[buf][i] = __builtin_shufflevector(lds_read_tr(pa), lds_read_tr(pa + 4 * 256), 0, 1, 2, 3, 4, 5, 6, 7);
-                const char* pb = smem + soff + q_rd[i] + ks * 16 * 256;
-                bfr[buf][i] = __builtin_shufflevector(lds_read_tr(pb), lds_read_tr(pb + 4 * 256), 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-        };
-        auto mfma = [&](int buf, int lo, int hi) {
+            for (int mi = 0; mi < 8; ++mi) load_p(0, mi);
             #pragma unroll
-            for (int q = lo; q < hi; ++q) {
-                const int mi = q >> 2, ni = q & 3;
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
-            }
-        };
-        // The forward kernel's pipeline: four K-steps in flight, a step's
-        // stage refilled with step + 4 one DMA per MFMA, fragments of the next
-        // sub-step read under the current one's MFMAs.
-        issue(0, 0);
-        issue(1, kP4Stage);
-        issue(2, 2 * kP4Stage);
-        issue(3, 3 * kP4Stage);
-        __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
-        __syncthreads();
-        load_frags(0, 0, 0);
-        int s_cur = 0;
-        for (int kt0 = 0; kt0 < ksn; kt0 += 4) {
-            #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int kt = kt0 + u;
+            for (int ni = 0; ni < 4; ++ni) load_q(0, ni);
+            int s_cur = 0;
+            auto kstep = [&](int kt, auto first_tag) {
+                constexpr bool Z = decltype(first_tag)::value;
                 const int s_nxt = s_cur == (kP4Stages - 1) * kP4Stage ? 0 : s_cur + kP4Stage;
                 const int s_old = s_cur == 0 ? (kP4Stages - 1) * kP4Stage : s_cur - kP4Stage;
+                // Step boundary as in the forward kernel: own DMA of step kt+1 done,
+                // then a bare barrier (reads in flight are of step kt+1's stage).
                 __builtin_amdgcn_sched_barrier(0);
-                __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
-                __syncthreads();
+                __asm__ volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
                 const int kn = min(kt + 4, ksn - 1);
-                // Four DMAs over the first 8 MFMAs of each sub-step (as in the plain
-                // GEMM: a DMA held up by a full address queue delays fewer MFMAs).
                 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    issue_one(kn, s_old, i);
-                    mfma(0, 2 * i, 2 * i + 2);
+                for (int mi = 0; mi < 8; ++mi) {
+                    if (mi < 4) issue_one(kn, s_old, mi);
+                    mfma_row(0, mi, Z);
+                    if (mi < 4) load_q(s_cur, 4 + mi);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                load_frags(s_cur, 1, 1);
-                mfma(0, 8, 16);
                 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                #pragma unroll
-                for (int i = 4; i < 8; ++i) {
-                    issue_one(kn, s_old, i);
-                    __builtin_amdgcn_sched_barrier(0);
-                    mfma(1, 4 * (i - 4), 4 * (i - 4) + 1);
+                for (int mi = 0; mi < 8; ++mi) {
+                    if (mi < 4) issue_one(kn, s_old, 4 + mi);
+                    mfma_row(1, mi, Z);
+                    load_p(s_nxt, mi);
+                    if (mi >= 2 && mi < 6) load_q(s_nxt, mi - 2);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                load_frags(s_nxt, 0, 0);
-                #pragma unroll
-                for (int q = 0; q < 4; ++q) mfma(1, 4 * q + 1, 4 * q + 4);
-                #pragma unroll
-                for (int i = 0; i < 12; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
                 s_cur = s_nxt;
-            }
-        }
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // Every wave is done reading the stages before the next tile refills them.
-        __syncthreads();
-        }
-        // acc[mi][ni] element q*4 + jj of lane l: row wm*128 + mi*32 + l%32,
-        // column wn*128 + ni*32 + q*8 + (l/32)*4 + jj of the tile.
-        float* cbase = C + ((size_t)e * M + m0 + wm * 128 + l32) * N + n0 + wn * 128 + lh * 4;
-        #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+            };
+            kstep(0, std::true_type{});
+            for (int kt = 1; kt < ksn; ++kt) kstep(kt, std::false_type{});
+            mfma16_drain(acc);
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // Every wave is done reading the stages before the next tile refills them.
+            __syncthreads();
+        } else {
             #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
+            for (int mi = 0; mi < 8; ++mi)
                 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x16& av = acc[mi][ni];
-                    *reinterpret_cast<f32x4*>(cbase + (size_t)(mi * 32) * N + ni * 32 + q * 8) =
-                        f32x4{av[q * 4], av[q * 4 + 1], av[q * 4 + 2], av[q * 4 + 3]};
-                }
+                for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = f32x4{};
+        }
+        // acc[mi][ni] element v of lane l: row wm*128 + mi*16 + l%16, column
+        // wn*128 + ni*16 + 4*(l/16) + v of the tile.
+        float* cbase = C + ((size_t)e * M + m0 + wm * 128 + s16) * N + n0 + wn * 128 + 4 * g16;
+        #pragma unroll
+        for (int mi = 0; mi < 8; ++mi)
+            #pragma unroll
+            for (int ni = 0; ni < 8; ++ni)
+                *reinterpret_cast<f32x4*>(cbase + (size_t)(mi * 16) * N + ni * 16) = acc[mi][ni];
     }
 }
 
