@@ -174,7 +174,7 @@ def workload_probe(name, cold, moe, synth, torch, dev, reps=3):
             flush()
             moe.moe_route(g["logits"], cfg.K, out=out)
             torch.cuda.synchronize()
-            print(json.dumps({"probe": name, "round": r}), flush=True)
+            print(json.dumps({"probe": name, "pass": r}), flush=True)
         return
     Wr, rb = synth.make_router(cfg, dev, seed=0)
     plan = moe.ForwardPlan(cfg.T, cfg.d, cfg.E, cfg.K, cfg.n, cfg.torch_dtype, dev)
@@ -195,7 +195,7 @@ def workload_probe(name, cold, moe, synth, torch, dev, reps=3):
         plan(g["X"], g["logits"], g["W1"], g["W3"], g["W2"])
         torch.cuda.synchronize()
         del Xp, Act, Y
-        print(json.dumps({"probe": name, "round": r}), flush=True)
+        print(json.dumps({"probe": name, "pass": r}), flush=True)
 
 
 def blas_reference(moe, synth, torch, dev, seconds, iters=10):
