@@ -317,6 +317,69 @@ MOE_DEV bool tile_geom(const int32_t* __restrict__ counts, const int32_t* __rest
     return true;
 }
 
+// The same schedule held in registers for the whole launch (counts and
+// offsets do not change during it): lane l keeps experts 4l..4l+3's clamped
+// row counts, offsets and tile-range boundaries, so that a tile's geometry
+// costs a few cross-lane operations instead of two rounds of global loads.
+struct SchedRegs {
+    int b[5];    // tile-range boundaries of the lane's experts (b[j] .. b[j+1] for expert 4l+j)
+    int cnt[4];  // their row counts, clamped into [0, rows]
+    int off[4];  // their offsets
+    int total;   // tiles of the whole schedule
+};
+MOE_DEV SchedRegs sched_regs(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int E,
+                             int NT, int rows, int lane) {
+    SchedRegs sr;
+    int v[4];
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane * 4 + j;
+        sr.cnt[j] = e < E ? min(max(counts[e], 0), rows) : 0;
+        sr.off[j] = e < E ? offsets[e] : 0;
+        v[j] = ((sr.cnt[j] + kBM256 - 1) / kBM256) * NT;
+    }
+    const int p3 = v[0] + v[1] + v[2] + v[3];
+    int x = p3;  // inclusive scan of the per-lane totals
+    #pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+    }
+    sr.b[0] = x - p3;
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) sr.b[j + 1] = sr.b[j] + v[j];
+    sr.total = uniform(__shfl(x, kWave - 1, kWave));
+    return sr;
+}
+// tile_geom on the register schedule (wave-uniform results; all lanes call it).
+MOE_DEV bool tile_geom_regs(const SchedRegs& sr, int NT, int OUTW, int rows, int lane, int tile, TileGeom& t) {
+    int hit = -1, st = 0, c = 0, o = 0;
+    #pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (tile >= sr.b[j] && tile < sr.b[j + 1]) {
+            hit = j;
+            st = sr.b[j];
+            c = sr.cnt[j];
+            o = sr.off[j];
+        }
+    const unsigned long long m = __ballot(hit >= 0);
+    if (m == 0ull) return false;
+    const int src = __builtin_ctzll(m);
+    const int e = src * 4 + uniform(__shfl(hit, src, kWave));
+    const int first = uniform(__shfl(st, src, kWave));
+    const int cnt = uniform(__shfl(c, src, kWave));
+    const int off = uniform(__shfl(o, src, kWave));
+    const int mt = (cnt + kBM256 - 1) / kBM256;
+    const int local = tile - first;
+    const int m_tile = local % mt;
+    const int n_tile = local / mt;
+    t.e = e;
+    t.r0 = off + m_tile * kBM256;
+    t.rows_valid = (t.r0 < 0 || t.r0 >= rows) ? 0 : min(min(kBM256, cnt - m_tile * kBM256), rows - t.r0);
+    t.n0 = n_tile * OUTW;
+    return true;
+}
+
 // Split of the last, partial round of tiles over the idle workgroups: with
 // G workgroups and `total` tiles, the first R*G tiles are computed whole and
 // each of the Tr = total - R*G remaining ones in S parts of consecutive K-steps
@@ -653,9 +716,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, lh = lane >> 5;
     const int g16 = lane >> 4, s16 = lane & 15;
-    int total = 0, first = 0;
-    sched_lookup(counts, E, NT, rows, lane, -1, &first, &total);
-    total = uniform(total);
+    const SchedRegs sreg = sched_regs(counts, offsets, E, NT, rows, lane);
+    const int total = sreg.total;
     // Claim tiles from the counters only when at least one tile in eight is
     // short.  With tiles of equal length the fixed order keeps the 32
     // workgroups of an XCD in step along K, so that they share the K-slices
@@ -743,7 +805,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
             pslot = p;
         }
         TileGeom tg;
-        if (!tile_geom(counts, offsets, E, NT, OUTW, rows, lane, tile, tg)) break;
+        if (!tile_geom_regs(sreg, NT, OUTW, rows, lane, tile, tg)) break;
         const int e = tg.e, r0 = tg.r0, rows_valid = tg.rows_valid, n0 = tg.n0;
         if (tickets != nullptr) claim();
         int j_next = j + per_xcd;
