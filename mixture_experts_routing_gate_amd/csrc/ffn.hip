@@ -503,6 +503,34 @@ MOE_DEV void store_rows_lds(const f32x4 (&acc)[8][8], int sl, char* smem, uint16
     }
 }
 
+// The SwiGLU GEMM's pre-activations as they are (for the backward, which needs
+// H1 = Xp W1 and H3 = Xp W3 themselves): slice sl of the W1 part to C and of
+// the W3 part to C + h3_off, bf16.  The slice is staged as the plain GEMM's is
+// (128 staged columns per wave: 0..63 the W1 part, 64..127 the W3 part of the
+// wave's 64 output columns) and read back as 16-byte pieces of row segments.
+MOE_DEV void store_rows_lds_raw(const f32x4 (&acc)[8][8], int sl, char* smem, uint16_t* __restrict__ C,
+                                size_t h3_off, int r0, int rows_valid, int n0, int N, int wave, int wm, int wn) {
+    int lane = __lane_id();
+    __asm__ volatile("" : "+v"(lane));
+    constexpr int CH = 16, RPI = kWave / CH;
+    stage_slice<false>(acc, sl, smem, wave, lane & 15, lane >> 4);
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int c = lane % CH;
+    uint16_t* const dst = (c < 8 ? C : C + h3_off) + n0 + wn * 64 + (c & 7) * 8;
+    u32x4 val[32 / RPI];
+    #pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = i * RPI + lane / CH;
+        val[i] = *reinterpret_cast<const u32x4*>(staged_row<false>(smem, wave, r) + staged_swz<false>(r, c) * 16);
+    }
+    #pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = i * RPI + lane / CH;
+        const int m = wm * 128 + sl * 32 + r;
+        if (m < rows_valid) *reinterpret_cast<u32x4*>(dst + (size_t)(r0 + m) * N) = val[i];
+    }
+}
+
 // Output of row slice mi of a short tile (rows mi*32 .. mi*32+31, all four
 // waves): wave w holds output columns w*32.. (SwiGLU: a[0] the W1 part, a[1]
 // the W3 part) or w*64 + ni*32.. (plain GEMM).
@@ -529,6 +557,30 @@ MOE_DEV void store_rows_short(const f32x16 (&a)[2], int mi, uint16_t* __restrict
                 uint2 pk;
                 pk.x = pack_bf16x2(v[0], v[1]);
                 pk.y = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<uint2*>(crow + col) = pk;
+            }
+        }
+    }
+}
+
+// store_rows_short<true>'s layout without the product: the W1 part (a[0]) to
+// C and the W3 part (a[1]) to C + h3_off.
+MOE_DEV void store_rows_short_raw(const f32x16 (&a)[2], int mi, uint16_t* __restrict__ C, size_t h3_off, int r0,
+                                  int rows_valid, int n0, int N, int wave) {
+    int lane = __lane_id();
+    __asm__ volatile("" : "+v"(lane));
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int m = mi * 32 + l32;
+    if (m < rows_valid) {
+        #pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint16_t* crow = C + (h ? h3_off : 0) + (size_t)(r0 + m) * N;
+            #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = n0 + wave * 32 + q * 8 + lh * 4;
+                uint2 pk;
+                pk.x = pack_bf16x2(a[h][q * 4], a[h][q * 4 + 1]);
+                pk.y = pack_bf16x2(a[h][q * 4 + 2], a[h][q * 4 + 3]);
                 *reinterpret_cast<uint2*>(crow + col) = pk;
             }
         }
@@ -704,7 +756,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
     int E, int Kd, int N, int rows, float* __restrict__ part, int* __restrict__ ticket_ctr,
     const int32_t* __restrict__ gather, int gK, int xrows, int kb, BwdEpi bwd) {
     static_assert(!(DUAL && BT), "the k-contiguous B is for the plain GEMM");
-    static_assert(!(DUAL && BWD), "the SwiGLU backward epilogue follows the plain GEMM");
+    // BWD selects the epilogue the backward needs: for the plain GEMM (dA) the
+    // fused SwiGLU backward, for the SwiGLU GEMM the pre-activations H1, H3
+    // stored as they are (H3 at C + rows * N).
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     constexpr int OUTW = DUAL ? 128 : 256;
@@ -966,7 +1020,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
 
                 #pragma unroll
                 for (int sl = 0; sl < 4; ++sl) {  // 32-row slices: row blocks 2sl, 2sl+1
-                    if constexpr (BWD) {
+                    if constexpr (BWD && DUAL) {
+                        store_rows_lds_raw(acc, sl, smem, C, (size_t)rows * N, r0, rows_valid, n0, N, wave, wm, wn);
+                    } else if constexpr (BWD) {
                         if (sl == 0) bwd_rows_lds(acc, smem, r0, rows_valid, n0, N, wave, wm, wn, bwd);
                     } else if constexpr (PART) {
                         f32x4* dst = reinterpret_cast<f32x4*>(part + (size_t)pslot * kPartFloats);
@@ -1056,7 +1112,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                 if (tickets != nullptr) j_next = take();
                 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi) {
-                    if constexpr (BWD) bwd_rows_short(acc[mi], mi, r0, rows_valid, n0, N, wave, bwd);
+                    if constexpr (BWD && DUAL) store_rows_short_raw(acc[mi], mi, C, (size_t)rows * N, r0, rows_valid, n0, N, wave);
+                    else if constexpr (BWD) bwd_rows_short(acc[mi], mi, r0, rows_valid, n0, N, wave, bwd);
                     else store_rows_short<DUAL>(acc[mi], mi, C, r0, rows_valid, n0, N, wave);
                 }
             }
@@ -1382,6 +1439,8 @@ static bool ffn_pipelined_ok(int d, int n) {
     return d % 256 == 0 && n % 128 == 0 && (long long)d * n * 2 < (1LL << 31);
 }
 
+bool ffn_raw_ok(int dtype, int d, int n) { return dtype == 1 && ffn_pipelined_ok(d, n); }
+
 // Gathered loads address X with 32-bit byte offsets.
 bool ffn_gather_ok(int dtype, int T, int d, int n) {
     return dtype == 1 && ffn_pipelined_ok(d, n) && (long long)T * d * 2 < (1LL << 31);
@@ -1449,6 +1508,16 @@ hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dty
                            rows);
     }
     return hipGetLastError();
+}
+
+// The backward's pre-activations in one launch: H1 = Xp W1 into H and
+// H3 = Xp W3 into H + rows * n (bf16, whole tiles in one piece: no split).
+hipError_t launch_ffn_up_raw(const void* Xp, const void* W1, const void* W3, int rows, int d, int E, int n,
+                             const int32_t* counts, const int32_t* offsets, void* H, hipStream_t s) {
+    if (!ffn_pipelined_ok(d, n)) return hipErrorInvalidValue;
+    return launch_pipelined<true, false, true>(static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
+                                               static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(H), counts,
+                                               offsets, E, d, n, rows, nullptr, false, nullptr, 1, 1, s);
 }
 
 // Step 4b: Y = Act W2.

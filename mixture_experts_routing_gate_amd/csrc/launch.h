@@ -61,6 +61,11 @@ hipError_t launch_ffn_up(const void* Xp, const void* W1, const void* W3, int dty
                          int n, const int32_t* counts, const int32_t* offsets, void* Act, float* part,
                          bool tickets_zeroed, hipStream_t s, const int32_t* gather = nullptr, int gK = 1,
                          int xrows = 0);
+// H1 = Xp W1 into H and H3 = Xp W3 into H + rows * n, bf16, one launch (needs
+// the pipelined kernel's sizes: ffn_raw_ok(1, d, n)).
+bool ffn_raw_ok(int dtype, int d, int n);
+hipError_t launch_ffn_up_raw(const void* Xp, const void* W1, const void* W3, int rows, int d, int E, int n,
+                             const int32_t* counts, const int32_t* offsets, void* H, hipStream_t s);
 hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows, int d, int E, int n,
                            const int32_t* counts, const int32_t* offsets, void* Y, float* part,
                            bool tickets_zeroed, hipStream_t s);

@@ -157,7 +157,7 @@ size_t backward_ws(int T, int d, int E, int K, int n, int dtype, bool weights) {
     b += align_up(A * 4) * 2;                               // sorted_pair, inv
     b += align_up(A * 4) * 2;                               // dS, unit weights
     b += align_up(A * d * s) * 2;                           // Xp (then dXp), dout rows
-    b += align_up(A * n * s) * 3 + align_up(A * 2 * n * s);  // H1, H3, dA, dH
+    b += align_up(2 * A * n * s) + align_up(A * n * s) + align_up(A * 2 * n * s);  // H1|H3, dA, dH
     if (!ffn_bt_ok(dtype, n, d, d)) b += align_up((size_t)E * d * n * s);          // W2^T
     if (!ffn_bt_ok(dtype, d, 2 * n, n)) b += align_up((size_t)E * 2 * d * n * s);  // [W1^T ; W3^T]
     b += align_up(ffn_split_bytes(dtype, 256, 128));        // split tail of the grouped GEMMs
@@ -866,8 +866,8 @@ int backward_impl(const char* name, const void* X, const float* logits, const vo
     float* ones = c.take<float>(A);
     void* Xp = c.take<char>(A * d * sz);  // later dXp
     void* dY = c.take<char>(A * d * sz);
-    void* H1 = c.take<char>(A * n * sz);
-    void* H3 = c.take<char>(A * n * sz);
+    void* H1 = c.take<char>(2 * A * n * sz);  // H1, then H3
+    void* H3 = static_cast<char*>(H1) + A * n * sz;
     void* dA = c.take<char>(A * n * sz);
     void* dH = c.take<char>(A * 2 * n * sz);
     // The bf16 pipelined GEMM reads W2 and W1, W3 k-contiguous as they are;
@@ -899,8 +899,13 @@ int backward_impl(const char* name, const void* X, const float* logits, const vo
                                           (size_t)2 * n * d, (size_t)d, s));
     }
     // pre-activations H1 = Xp W1, H3 = Xp W3; dA = dY W2^T (grouped, per expert)
-    HIPCHECK(launch_ffn_down(Xp, W1, dtype, (int)A, n, E, d, counts, offsets, H1, part, false, s));
-    HIPCHECK(launch_ffn_down(Xp, W3, dtype, (int)A, n, E, d, counts, offsets, H3, part, false, s));
+    if (ffn_raw_ok(dtype, d, n)) {
+        // one launch of the SwiGLU GEMM's kernel, storing both pre-activations
+        HIPCHECK(launch_ffn_up_raw(Xp, W1, W3, (int)A, d, E, n, counts, offsets, H1, s));
+    } else {
+        HIPCHECK(launch_ffn_down(Xp, W1, dtype, (int)A, n, E, d, counts, offsets, H1, part, false, s));
+        HIPCHECK(launch_ffn_down(Xp, W3, dtype, (int)A, n, E, d, counts, offsets, H3, part, false, s));
+    }
     if (bt_da) {
         // dA = dY W2^T with the SwiGLU backward and dS in the GEMM's epilogue
         // (dA is never stored; its buffer holds the row weights and dS parts)
