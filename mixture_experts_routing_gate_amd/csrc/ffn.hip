@@ -1333,6 +1333,71 @@ __global__ __launch_bounds__(kThreads) void ffn_split_fixup(const float* __restr
     }
 }
 
+// The router projection on the SwiGLU GEMM's kernel: A = X (T rows, one
+// "expert"), B0 = hi and B1 = lo, the two bf16 terms of the fp32 router
+// weights ([d, E], E columns).  The launch has fewer than half as many tiles as
+// workgroups, so every tile is split along K and the kernel only leaves fp32
+// partial tiles.  This adds a tile's slots in slot order, for each of its
+// columns the hi part and the lo part, and writes
+// logits[t, c] = (hi sum + lo sum) + bias[c] as fp32.
+__global__ __launch_bounds__(kThreads) void router_fixup(const float* __restrict__ part, float* __restrict__ logits,
+                                                         const float* __restrict__ bias,
+                                                         const int32_t* __restrict__ counts,
+                                                         const int32_t* __restrict__ offsets, int Kd, int N,
+                                                         int rows, int G) {
+    constexpr int OUTW = 128;
+    const int NT = N / OUTW;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int s16 = lane & 15, g16 = lane >> 4;
+    int total = 0, first = 0;
+    sched_lookup(counts, 1, NT, rows, lane, -1, &first, &total);
+    total = uniform(total);
+    const SplitPlan sp = split_plan(total, G, Kd / kP4BK, true);
+    if (sp.R != 0 || sp.S < 2) return;  // not a fully split launch (the host rules it out)
+    for (int u = blockIdx.x; u < sp.Tr * 4; u += gridDim.x) {
+        const int i = u >> 2, sl = u & 3;
+        TileGeom tg;
+        if (!tile_geom(counts, offsets, 1, NT, OUTW, rows, lane, i, tg)) return;
+        if (tg.rows_valid <= 0) continue;
+        const f32x4* src = reinterpret_cast<const f32x4*>(part + (size_t)i * sp.S * kPartFloats);
+        f32x4 acc[2][8];
+        #pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+            #pragma unroll
+            for (int ni = 0; ni < 8; ++ni) acc[mm][ni] = f32x4{};
+        for (int j = 0; j < sp.S; ++j) {  // parts in slot order
+            #pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+                #pragma unroll
+                for (int ni = 0; ni < 8; ++ni) {
+                    const f32x4 v = src[(size_t)j * (kPartFloats / 4) + part_index(wave, 2 * sl + mm, ni, lane)];
+                    #pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[mm][ni][c] += v[c];
+                }
+        }
+        // lane l: row l%16 of block mm, columns ni*16 + 4*(l/16) .. +3 of the
+        // wave's 64 (ni < 4 the hi part, ni + 4 the lo part of the same columns)
+        #pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+            const int m = wm * 128 + sl * 32 + mm * 16 + s16;
+            if (m < tg.rows_valid) {
+                float* orow = logits + (size_t)(tg.r0 + m) * N;
+                #pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const int c = tg.n0 + wn * 64 + ni * 16 + 4 * g16;
+                    f32x4 o;
+                    #pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        o[q] = (acc[mm][ni][q] + acc[mm][ni + 4][q]) + (bias != nullptr ? bias[c + q] : 0.0f);
+                    *reinterpret_cast<f32x4*>(orow + c) = o;
+                }
+            }
+        }
+    }
+}
+
 // Clears the claim counters before a launch of the pipelined kernel.
 __global__ void zero_ints(int* __restrict__ p, int n) {
     if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
@@ -1518,6 +1583,37 @@ hipError_t launch_ffn_up_raw(const void* Xp, const void* W1, const void* W3, int
     return launch_pipelined<true, false, true>(static_cast<const uint16_t*>(Xp), static_cast<const uint16_t*>(W1),
                                                static_cast<const uint16_t*>(W3), static_cast<uint16_t*>(H), counts,
                                                offsets, E, d, n, rows, nullptr, false, nullptr, 1, 1, s);
+}
+
+// The router projection as a fully split SwiGLU-kernel launch (see
+// router_fixup): bf16 X with d % 256 == 0, E % 128 == 0, and at most G/2 tiles
+// of 256 tokens x 128 experts, so that every tile is split in at least two.
+// Only for d >= 4096: the parts' prologues and epilogues and the fixup's pass
+// over the fp32 slots cost about 25 us, which a shorter K does not pay back
+// against the register-tiled kernel.
+bool router_gemm_ok(int T, int d, int E) {
+    if (T < 1 || d < 4096 || !ffn_pipelined_ok(d, E) || (long long)T * d * 2 >= (1LL << 31)) return false;
+    const long long tiles = ((long long)T + kBM256 - 1) / kBM256 * (E / 128);
+    const int G = ffn_grid();
+    return tiles * 2 <= G && d / kP4BK / 4 >= 2;
+}
+
+hipError_t launch_router_gemm(const uint16_t* X, const uint16_t* hi, const uint16_t* lo, int T, int d, int E,
+                              const int32_t* counts, const int32_t* offsets, const float* bias, float* logits,
+                              float* part, bool tickets_zeroed, hipStream_t s) {
+    if (!router_gemm_ok(T, d, E) || part == nullptr) return hipErrorInvalidValue;
+    const hipError_t aerr = hipFuncSetAttribute((const void*)ffn_p4_kernel<true, false, false>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, kP4Lds);
+    if (aerr != hipSuccess) return aerr;
+    const int G = ffn_grid();
+    int* tickets = ffn_tickets(part);
+    if (!tickets_zeroed) hipLaunchKernelGGL(zero_ints, dim3(1), dim3(kTicketInts), 0, s, tickets, kTicketInts);
+    // C is never written: every work item is a split part.
+    hipLaunchKernelGGL((ffn_p4_kernel<true, false, false>), dim3(G), dim3(kThreads), kP4Lds, s, X, hi, lo,
+                       static_cast<uint16_t*>(nullptr), counts, offsets, 1, d, E, T, part, tickets,
+                       static_cast<const int32_t*>(nullptr), 1, T, 0, BwdEpi{});
+    hipLaunchKernelGGL(router_fixup, dim3(G), dim3(kThreads), 0, s, part, logits, bias, counts, offsets, d, E, T, G);
+    return hipGetLastError();
 }
 
 // Step 4b: Y = Act W2.

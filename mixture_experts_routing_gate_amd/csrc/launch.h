@@ -69,6 +69,15 @@ hipError_t launch_ffn_up_raw(const void* Xp, const void* W1, const void* W3, int
 hipError_t launch_ffn_down(const void* Act, const void* W2, int dtype, int rows, int d, int E, int n,
                            const int32_t* counts, const int32_t* offsets, void* Y, float* part,
                            bool tickets_zeroed, hipStream_t s);
+// The router projection logits = X [hi ; lo] summed per column, plus bias, on
+// the SwiGLU GEMM's kernel, where router_gemm_ok(T, d, E): bf16 X [T, d], hi
+// and lo [d, E] bf16, counts = {T} and offsets = {0, T} in device memory, part
+// the split workspace of ffn_split_bytes(1, d, E) bytes (its claim counters
+// cleared first unless `tickets_zeroed`).  Deterministic.
+bool router_gemm_ok(int T, int d, int E);
+hipError_t launch_router_gemm(const uint16_t* X, const uint16_t* hi, const uint16_t* lo, int T, int d, int E,
+                              const int32_t* counts, const int32_t* offsets, const float* bias, float* logits,
+                              float* part, bool tickets_zeroed, hipStream_t s);
 // C = A [B0^T ; B1^T] per expert (rows x N): B0 and B1 are each expert's
 // N x kb row-major matrices, B1 only when Kd = 2 kb (nullptr when Kd = kb).
 // bf16 pipelined kernel only: where ffn_bt_ok(), else hipErrorInvalidValue.

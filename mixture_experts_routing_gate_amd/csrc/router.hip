@@ -13,6 +13,11 @@
 // A prep kernel writes hi and lo transposed ([E_pad, d], k-contiguous) into the
 // workspace, so that both MFMA operands are 16-byte loads per lane.
 //
+// For E a multiple of 128 and few enough tokens (router_gemm_ok), the same
+// split runs on the grouped GEMM's SwiGLU kernel instead: hi and lo stay in
+// Wr's [d, E] layout as its two weight matrices, every 256 x 128 tile is split
+// along K, and a fixup adds the parts and the two terms (launch_router_gemm).
+//
 // fp32 X, or d not a multiple of 256: one thread per output, fp32 fused
 // multiply-adds in index order.
 #include <algorithm>
@@ -38,6 +43,24 @@ __global__ __launch_bounds__(kThreads) void router_split_kernel(const float* __r
         hi[q] = h;
         lo[q] = f32_to_bf16(w - bf16_to_f32(h));
     }
+}
+
+// Wr [d, E] fp32 -> hi, lo [d, E] bf16 (the same layout), the one-expert
+// schedule of the GEMM path (counts = {T}, offsets = {0, T}), and its claim
+// counters cleared (nz <= kThreads ints).
+__global__ __launch_bounds__(kThreads) void router_split_nc_kernel(const float* __restrict__ Wr, size_t n, int T,
+                                                                   uint16_t* __restrict__ hi,
+                                                                   uint16_t* __restrict__ lo,
+                                                                   int32_t* __restrict__ sched,
+                                                                   int* __restrict__ zero, int nz) {
+    for (size_t q = (size_t)blockIdx.x * kThreads + threadIdx.x; q < n; q += (size_t)gridDim.x * kThreads) {
+        const float w = Wr[q];
+        const uint16_t h = f32_to_bf16(w);
+        hi[q] = h;
+        lo[q] = f32_to_bf16(w - bf16_to_f32(h));
+    }
+    if (blockIdx.x == 0 && threadIdx.x < 3) sched[threadIdx.x] = threadIdx.x == 1 ? 0 : T;
+    if (blockIdx.x == 0 && (int)threadIdx.x < nz) zero[threadIdx.x] = 0;
 }
 
 // Workgroup tile: 32*TG tokens x 32*NB experts; the four waves split d into
@@ -310,11 +333,19 @@ bool router_mfma_ok(int dtype, int d) { return dtype == 1 && d % 256 == 0; }
 
 }  // namespace
 
+// The GEMM path's layout: hi, lo [d, E]; 256 bytes for its schedule; the
+// GEMM's split slots.  It is reserved whenever the shapes allow the path (it
+// also depends on T), and it is never smaller than the transposed layout.
+static bool router_gemm_shape(int dtype, int d, int E) { return router_mfma_ok(dtype, d) && router_gemm_ok(1, d, E); }
+static size_t router_hilo_bytes(int d, int E) { return ((2 * (size_t)d * E * sizeof(uint16_t)) + 255) / 256 * 256; }
+
 size_t router_split_bytes(int dtype, int d, int E) {
     if (!router_mfma_ok(dtype, d)) return 0;
     const int eb = 32 * router_nb(E);
     const size_t e_pad = (size_t)((E + eb - 1) / eb) * eb;
-    return 2 * e_pad * (size_t)d * sizeof(uint16_t);
+    const size_t transposed = 2 * e_pad * (size_t)d * sizeof(uint16_t);
+    if (!router_gemm_shape(dtype, d, E)) return transposed;
+    return std::max(transposed, router_hilo_bytes(d, E) + 256 + ffn_split_bytes(1, d, E));
 }
 
 bool router_gate_ok(int dtype, int d, int E) { return router_mfma_ok(dtype, d) && E <= 64; }
@@ -351,6 +382,20 @@ hipError_t launch_router(const void* X, int dtype, int T, int d, int E, const fl
             hipLaunchKernelGGL(router_fma_kernel<float>, grid, dim3(kThreads), 0, s, static_cast<const float*>(X),
                                T, d, Wr, bias, E, logits);
         return hipGetLastError();
+    }
+    if (router_gemm_ok(T, d, E)) {
+        uint16_t* hi = static_cast<uint16_t*>(split);
+        uint16_t* lo = hi + (size_t)d * E;
+        int32_t* sched = reinterpret_cast<int32_t*>(static_cast<char*>(split) + router_hilo_bytes(d, E));
+        float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(sched) + 256);
+        const size_t n = (size_t)d * E;
+        const unsigned sgrid = (unsigned)std::min<size_t>((n + kThreads - 1) / kThreads, 4096);
+        const int nz = ffn_ticket_ints();
+        if (nz > kThreads) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(router_split_nc_kernel, dim3(sgrid), dim3(kThreads), 0, s, Wr, n, T, hi, lo, sched,
+                           ffn_tickets(part), nz);
+        return launch_router_gemm(static_cast<const uint16_t*>(X), hi, lo, T, d, E, sched, sched + 1, bias, logits,
+                                  part, true, s);
     }
     const int nb = router_nb(E);
     const int eb = 32 * nb;

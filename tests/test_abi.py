@@ -121,7 +121,14 @@ def test_combine_and_forward_reject(lib):
 
 def test_router_workspace_and_rejections(lib):
     assert lib.moe_router_workspace_bytes(4096, 8, 1) == 2 * 32 * 4096 * 2     # E padded to 32
-    assert lib.moe_router_workspace_bytes(7168, 256, 1) == 2 * 256 * 7168 * 2
+    # E a multiple of 128: hi and lo [d, E], 256 bytes of schedule, and the split
+    # slots of the grouped GEMM's kernel that then runs the projection
+    assert lib.moe_router_workspace_bytes(7168, 256, 1) == \
+        2 * 256 * 7168 * 2 + 256 + lib.moe_ffn_workspace_bytes(7168, 256, 1)
+    assert lib.moe_router_workspace_bytes(4096, 128, 1) == \
+        2 * 128 * 4096 * 2 + 256 + lib.moe_ffn_workspace_bytes(4096, 128, 1)
+    assert lib.moe_router_workspace_bytes(1536, 128, 1) == 2 * 128 * 1536 * 2   # d < 4096: transposed only
+    assert lib.moe_router_workspace_bytes(4096, 192, 1) == 2 * 192 * 4096 * 2   # E % 128 != 0
     assert lib.moe_router_workspace_bytes(1536, 40, 1) == 2 * 64 * 1536 * 2    # E padded to 64
     assert lib.moe_router_workspace_bytes(128, 8, 0) == 0                      # fp32: no split
     assert lib.moe_router_workspace_bytes(384, 8, 1) == 0                      # d % 256 != 0: no split

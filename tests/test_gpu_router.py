@@ -40,6 +40,14 @@ CASES = [
     (33, 384, 8, "bf16", 0.0),
     (256, 128, 8, "f32", 0.0),
     (1, 1024, 64, "bf16", 0.5),
+    # E a multiple of 128 and d >= 4096: the grouped GEMM's kernel with every
+    # tile split along K (4 parts; 3 parts of uneven length), ragged tokens
+    (8000, 4096, 256, "bf16", 1.5),
+    (16385, 4096, 128, "bf16", 0.0),
+    # the same E with a shorter d, and too many token tiles for that path: the
+    # register-tiled kernel
+    (16385, 256, 128, "bf16", 0.0),
+    (33000, 256, 128, "bf16", 1.0),
 ]
 
 
