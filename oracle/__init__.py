@@ -62,10 +62,11 @@ def _load():
         lib.oracle_tr_layer.argtypes = [P, I, P, P, P, P, P, I, I, I, I, P, I, P]
         lib.oracle_layer_backward.argtypes = [P, I, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P]
         lib.oracle_layer_backward_rows.argtypes = [P, I, P, P, P, P, I, I, I, I, I, P, P, I, P, P, P]
+        lib.oracle_weight_grad_slices.argtypes = [P, I, P, P, P, P, I, I, I, I, I, P, P, P, I, P, P, P]
         for f in (lib.oracle_softmax, lib.oracle_route, lib.oracle_permute, lib.oracle_gather_rows,
                   lib.oracle_expert_ffn, lib.oracle_combine, lib.oracle_layer, lib.oracle_expert_down,
                   lib.oracle_router, lib.oracle_token_round, lib.oracle_tr_combine, lib.oracle_tr_layer,
-                  lib.oracle_layer_backward, lib.oracle_layer_backward_rows):
+                  lib.oracle_layer_backward, lib.oracle_layer_backward_rows, lib.oracle_weight_grad_slices):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -264,6 +265,32 @@ def layer_backward_rows(X, logits, W1, W3, W2, K: int, dout, tokens):
     _check(_load().oracle_layer_backward_rows(_ptr(Xs), dt, _ptr(lg), _ptr(W1s), _ptr(W3s), _ptr(W2s), T, d, E, K,
                                               n, _ptr(g), _ptr(tk), m, _ptr(r["dX"]), _ptr(r["dlogits"]),
                                               _ptr(r["dw"])), "oracle_layer_backward_rows")
+    return r
+
+
+def weight_grad_slices(X, logits, W1, W3, W2, K: int, dout, experts, cols):
+    """Slices of layer_backward()'s weight gradients for pairs (experts[p], cols[p]):
+    a dict of float32 arrays dW1c, dW3c [npair, d] (column cols[p] of dW1 and dW3
+    of expert experts[p]) and dW2r [npair, d] (row cols[p] of its dW2)."""
+    Xs, dt = _storage(X)
+    W1s, d1 = _storage(W1)
+    W3s, d3 = _storage(W3)
+    W2s, d2 = _storage(W2)
+    if not (dt == d1 == d3 == d2):
+        raise ValueError("X and the expert weights must share one storage dtype")
+    lg = _c(logits, np.float32)
+    g = _c(dout, np.float32)
+    ex = _c(experts, np.int32)
+    cl = _c(cols, np.int32)
+    T, d = Xs.shape
+    E, _, n = W1s.shape
+    m = ex.size
+    assert cl.size == m and g.shape == (T, d) and lg.shape == (T, E)
+    r = {"dW1c": np.empty((m, d), np.float32), "dW3c": np.empty((m, d), np.float32),
+         "dW2r": np.empty((m, d), np.float32)}
+    _check(_load().oracle_weight_grad_slices(_ptr(Xs), dt, _ptr(lg), _ptr(W1s), _ptr(W3s), _ptr(W2s), T, d, E, K,
+                                             n, _ptr(g), _ptr(ex), _ptr(cl), m, _ptr(r["dW1c"]), _ptr(r["dW3c"]),
+                                             _ptr(r["dW2r"])), "oracle_weight_grad_slices")
     return r
 
 

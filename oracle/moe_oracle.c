@@ -663,3 +663,80 @@ int oracle_layer_backward_rows(const void* X, int dtype, const float* logits, co
     }
     return bad ? -1 : 0;
 }
+
+/* Slices of the expert-weight gradients, for checks of large layers whose full
+ * gradients the fp64 accumulators of oracle_layer_backward could not hold.
+ * For pair p = (e, j) = (experts[p], cols[p]) it writes column j of dW1[e] and
+ * of dW3[e] (d values each: dW1[e][i][j] for i = 0..d-1) and row j of dW2[e]
+ * (d values: dW2[e][j][c]), into rows p of dW1c, dW3c and dW2r [npair, d].
+ * Same definition and summation order as oracle_layer_backward ([P4] section
+ * 2.2): over the assignments (t, k) with idx[t,k] == e, tokens ascending,
+ *   h1 = x W1[e][:,j], h3 = x W3[e][:,j], sig = 1/(1+e^-h1), s1 = h1 sig,
+ *   a = s1 h3, da = w_k (g W2[e][j,:]^T),
+ *   dh1 = da h3 sig (1 + h1 (1 - sig)), dh3 = da s1,
+ *   dW1[e][:,j] += x dh1,  dW3[e][:,j] += x dh3,  dW2[e][j,:] += w_k a g,
+ * in fp64, rounded once to fp32.  The routing is oracle_route's over all T. */
+int oracle_weight_grad_slices(const void* X, int dtype, const float* logits, const void* W1, const void* W3,
+                              const void* W2, int T, int d, int E, int K, int n, const float* dout,
+                              const int32_t* experts, const int32_t* cols, int npair, float* dW1c, float* dW3c,
+                              float* dW2r) {
+    if (!X || !logits || !W1 || !W3 || !W2 || !dout || !experts || !cols || !dW1c || !dW3c || !dW2r) return -1;
+    if (T < 0 || d < 1 || E < 1 || K < 1 || K > E || n < 1 || npair < 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    for (int p = 0; p < npair; ++p)
+        if (experts[p] < 0 || experts[p] >= E || cols[p] < 0 || cols[p] >= n) return -1;
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * ((size_t)T * K + 1));
+    float* w = (float*)malloc(sizeof(float) * ((size_t)T * K + 1));
+    int32_t* cnt = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    int32_t* off = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+    int rc = (!idx || !w || !cnt || !off) ? -3 : oracle_route(logits, T, E, K, idx, w, cnt, off);
+    int bad = 0;
+    if (rc == 0) {
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+        for (int p = 0; p < npair; ++p) {
+            const int e = experts[p], j = cols[p];
+            const size_t o13 = (size_t)e * d * n, o2 = (size_t)e * n * d;
+            double* acc = (double*)calloc(3 * (size_t)d, sizeof(double));
+            if (!acc) { bad |= 1; continue; }
+            double* g1 = acc;
+            double* g3 = acc + d;
+            double* g2 = acc + 2 * (size_t)d;
+            for (int t = 0; t < T; ++t)
+                for (int k = 0; k < K; ++k) {
+                    if (idx[(size_t)t * K + k] != e) continue;
+                    const size_t xoff = (size_t)t * d;
+                    const float* g = dout + (size_t)t * d;
+                    const double wk = (double)w[(size_t)t * K + k];
+                    double h1 = 0.0, h3 = 0.0, ga = 0.0;
+                    for (int i = 0; i < d; ++i) {
+                        const double xi = load_elem(X, dtype, xoff + i);
+                        h1 += xi * load_elem(W1, dtype, o13 + (size_t)i * n + j);
+                        h3 += xi * load_elem(W3, dtype, o13 + (size_t)i * n + j);
+                    }
+                    for (int c = 0; c < d; ++c) ga += (double)g[c] * load_elem(W2, dtype, o2 + (size_t)j * d + c);
+                    const double sig = 1.0 / (1.0 + exp(-h1));
+                    const double s1 = h1 * sig;
+                    const double a = h1 / (1.0 + exp(-h1)) * h3;
+                    const double da = wk * ga;
+                    const double dh3 = da * s1;
+                    const double dh1 = da * h3 * sig * (1.0 + h1 * (1.0 - sig));
+                    for (int i = 0; i < d; ++i) {
+                        const double xi = load_elem(X, dtype, xoff + i);
+                        g1[i] += xi * dh1;
+                        g3[i] += xi * dh3;
+                    }
+                    for (int c = 0; c < d; ++c) g2[c] += wk * a * (double)g[c];
+                }
+            for (int i = 0; i < d; ++i) {
+                dW1c[(size_t)p * d + i] = (float)g1[i];
+                dW3c[(size_t)p * d + i] = (float)g3[i];
+                dW2r[(size_t)p * d + i] = (float)g2[i];
+            }
+            free(acc);
+        }
+    }
+    free(idx); free(w); free(cnt); free(off);
+    if (rc) return rc;
+    return bad ? -3 : 0;
+}
+

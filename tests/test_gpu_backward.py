@@ -89,7 +89,7 @@ def test_backward_data_full_size(name):
     r = moe.moe_backward_data(g["X"], g["logits"], g["W1"], g["W3"], g["W2"], cfg.K, cuda(Gt))
     torch.cuda.synchronize()
     rng = np.random.default_rng(2)
-    toks = np.array(sorted(set(rng.choice(cfg.T, size=8, replace=False).tolist()) | {0, cfg.T - 1}), np.int32)
+    toks = np.array(sorted(set(rng.choice(cfg.T, size=48, replace=False).tolist()) | {0, cfg.T - 1}), np.int32)
     print(f"[bwd] full {name}: oracle on {toks.size} tokens", flush=True)
     ref = oracle.layer_backward_rows(to_np(g["X"]), to_np(g["logits"]), to_np(g["W1"]), to_np(g["W3"]),
                                      to_np(g["W2"]), cfg.K, Gt.float().numpy(), toks)
@@ -134,7 +134,10 @@ def test_backward_weight_gradients_full_size_identity(name):
     """Full-size layers.  <dW2[e], W2[e]> (Frobenius) equals the sum over
     expert e's assignments of w * dw: dw = <g W2^T, a> and dW2[e] = sum (w a)^T g
     give the same bilinear form, here from two different kernels; experts with
-    no rows get zero gradients.  Plus the data gradients on sampled tokens."""
+    no rows get zero gradients.  Whole columns of dW1 and dW3 and rows of dW2
+    (each a sum over every row of its expert) against the oracle, for the
+    experts with the fewest and the most rows and two more; plus the data
+    gradients on sampled tokens."""
     cfg = synth.CONFIGS[name]
     print(f"[bwd-w] full {name}: generating inputs", flush=True)
     g = synth.make_inputs(cfg, "cuda", 0)
@@ -156,8 +159,25 @@ def test_backward_weight_gradients_full_size_identity(name):
     for k in ("dW1", "dW3", "dW2"):
         assert torch.isfinite(r[k]).all(), k
         assert torch.all(r[k][~live] == 0), f"{k} of an expert with no rows"
+    cnt = counts.cpu().numpy()
+    live_e = np.nonzero(cnt > 0)[0]
+    rs = np.random.default_rng(5)
+    es = sorted({int(live_e[np.argmin(cnt[live_e])]), int(live_e[np.argmax(cnt[live_e])])}
+                | set(rs.choice(live_e, size=2, replace=False).tolist()))
+    js = [0, cfg.n - 1, int(rs.integers(1, cfg.n - 1))]
+    ex = np.repeat(np.array(es, np.int32), len(js))
+    cl = np.tile(np.array(js, np.int32), len(es))
+    print(f"[bwd-w] full {name}: oracle weight-gradient slices, experts {es} (rows "
+          f"{[int(cnt[e]) for e in es]}), columns {js}", flush=True)
+    ref_s = oracle.weight_grad_slices(to_np(g["X"]), to_np(g["logits"]), to_np(g["W1"]), to_np(g["W3"]),
+                                      to_np(g["W2"]), cfg.K, Gt.float().numpy(), ex, cl)
+    exT = torch.from_numpy(ex).long().cuda()
+    clT = torch.from_numpy(cl).long().cuda()
+    check_close(r["dW1"][exT, :, clT], ref_s["dW1c"], cfg.dtype, "dW1 columns")
+    check_close(r["dW3"][exT, :, clT], ref_s["dW3c"], cfg.dtype, "dW3 columns")
+    check_close(r["dW2"][exT, clT, :], ref_s["dW2r"], cfg.dtype, "dW2 rows")
     rng = np.random.default_rng(3)
-    toks = np.array(sorted(set(rng.choice(cfg.T, size=6, replace=False).tolist()) | {0}), np.int32)
+    toks = np.array(sorted(set(rng.choice(cfg.T, size=32, replace=False).tolist()) | {0}), np.int32)
     ref = oracle.layer_backward_rows(to_np(g["X"]), to_np(g["logits"]), to_np(g["W1"]), to_np(g["W3"]),
                                      to_np(g["W2"]), cfg.K, Gt.float().numpy(), toks)
     sel = torch.from_numpy(toks).long().cuda()

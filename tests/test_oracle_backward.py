@@ -9,7 +9,9 @@ dH and dS products of the backward, section 5 measures it).  CPU only.
 - Softmax shift invariance (each token's logit gradient sums to zero), zeros
   for experts a token did not choose, K = 1 (weights fixed at 1), identical
   experts (routing cannot matter), exact linearity in dout, and exact bf16
-  widening."""
+  widening.
+- The variants for large layers (some tokens; slices of the weight gradients)
+  equal the full backward exactly on small inputs."""
 import numpy as np
 import pytest
 
@@ -146,3 +148,28 @@ def test_rows_variant_equals_the_full_backward():
     part = oracle.layer_backward_rows(X, lg, W1, W3, W2, 2, G, toks)
     for k in ("dX", "dlogits", "dw"):
         assert np.array_equal(part[k], full[k][toks]), k
+
+
+@pytest.mark.parametrize("seed,K,E,bf16", [(9, 2, 4, False), (10, 3, 5, True), (11, 1, 6, False)])
+def test_weight_grad_slices_equal_the_full_backward(seed, K, E, bf16):
+    """Every (expert, column) slice: column j of dW1[e] and dW3[e], row j of
+    dW2[e], bit for bit (same fp64 sums in the same order), experts without
+    tokens included (T = 7 with 6 experts and K = 1 leaves some empty)."""
+    X, lg, W1, W3, W2, G = _case(seed, T=7, E=E, K=K)
+    if bf16:
+        import torch
+        X, W1, W3, W2 = (torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+                         for a in (X, W1, W3, W2))
+    full = oracle.layer_backward(X, lg, W1, W3, W2, K, G)
+    n = full["dW1"].shape[2]
+    ex = np.repeat(np.arange(E, dtype=np.int32), n)
+    cl = np.tile(np.arange(n, dtype=np.int32), E)
+    sl = oracle.weight_grad_slices(X, lg, W1, W3, W2, K, G, ex, cl)
+    assert np.array_equal(sl["dW1c"], full["dW1"][ex, :, cl])
+    assert np.array_equal(sl["dW3c"], full["dW3"][ex, :, cl])
+    assert np.array_equal(sl["dW2r"], full["dW2"][ex, cl, :])
+    idx, _, counts, _ = oracle.route(lg, K)
+    if (counts == 0).any():
+        e0 = int(np.nonzero(counts == 0)[0][0])
+        assert not sl["dW1c"][ex == e0].any() and not sl["dW2r"][ex == e0].any()
+
