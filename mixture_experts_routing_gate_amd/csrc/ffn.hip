@@ -319,11 +319,14 @@ MOE_DEV bool tile_geom(const int32_t* __restrict__ counts, const int32_t* __rest
 
 // The same schedule held in registers for the whole launch (counts and
 // offsets do not change during it): lane l keeps experts 4l..4l+3's clamped
-// row counts, offsets and tile-range boundaries, so that a tile's geometry
-// costs a few cross-lane operations instead of two rounds of global loads.
+// row counts and offsets and the first tile of expert 4l, so that a tile's
+// geometry costs a few cross-lane operations instead of two rounds of global
+// loads.  (The other tile-range boundaries are re-derived from the counts
+// when a tile is decoded: nine long-lived registers instead of thirteen keep
+// the SwiGLU epilogue from spilling them.)
 struct SchedRegs {
-    int b[5];    // tile-range boundaries of the lane's experts (b[j] .. b[j+1] for expert 4l+j)
-    int cnt[4];  // their row counts, clamped into [0, rows]
+    int b0;      // first tile of expert 4l
+    int cnt[4];  // row counts of experts 4l..4l+3, clamped into [0, rows]
     int off[4];  // their offsets
     int total;   // tiles of the whole schedule
 };
@@ -345,23 +348,25 @@ MOE_DEV SchedRegs sched_regs(const int32_t* __restrict__ counts, const int32_t* 
         const int y = __shfl_up(x, o, kWave);
         if (lane >= o) x += y;
     }
-    sr.b[0] = x - p3;
-    #pragma unroll
-    for (int j = 0; j < 4; ++j) sr.b[j + 1] = sr.b[j] + v[j];
+    sr.b0 = x - p3;
     sr.total = uniform(__shfl(x, kWave - 1, kWave));
     return sr;
 }
 // tile_geom on the register schedule (wave-uniform results; all lanes call it).
 MOE_DEV bool tile_geom_regs(const SchedRegs& sr, int NT, int OUTW, int rows, int lane, int tile, TileGeom& t) {
     int hit = -1, st = 0, c = 0, o = 0;
+    int lo = sr.b0;  // first tile of expert 4l+j
     #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        if (tile >= sr.b[j] && tile < sr.b[j + 1]) {
+    for (int j = 0; j < 4; ++j) {
+        const int hi = lo + ((sr.cnt[j] + kBM256 - 1) / kBM256) * NT;
+        if (tile >= lo && tile < hi) {
             hit = j;
-            st = sr.b[j];
+            st = lo;
             c = sr.cnt[j];
             o = sr.off[j];
         }
+        lo = hi;
+    }
     const unsigned long long m = __ballot(hit >= 0);
     if (m == 0ull) return false;
     const int src = __builtin_ctzll(m);
@@ -455,6 +460,16 @@ MOE_DEV int staged_swz(int r, int c) { return DUAL ? (c ^ ((r >> 1) & 7)) : (c ^
 // Writes slice sl of the accumulators to the staging rows, rounded to bf16 (with
 // DUAL, SiLU(W1 part) * (W3 part) first).  Lane l writes row (l%16) of each
 // block, 8 bytes per column block: staged columns ni*16 + 4*(l/16) .. +3.
+// An accumulator element read out of its AGPR at this point of the program
+// (the register allocator otherwise copies whole accumulator blocks to VGPRs
+// early, which raises the epilogue's register peak until long-lived values
+// spill).  After the K-loop's drain, so no MFMA hazard is pending.
+MOE_DEV float acc_read(float a) {
+    float v;
+    __asm__ volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
 template <bool DUAL>
 MOE_DEV void stage_slice(const f32x4 (&acc)[8][8], int sl, char* smem, int wave, int s16, int g16) {
     #pragma unroll
@@ -466,14 +481,17 @@ MOE_DEV void stage_slice(const f32x4 (&acc)[8][8], int sl, char* smem, int wave,
             float v[4];
             #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                v[j] = acc[2 * sl + mm][ni][j];
-                if (DUAL) v[j] = silu_mul(v[j], acc[2 * sl + mm][ni + 4][j]);
+                v[j] = acc_read(acc[2 * sl + mm][ni][j]);
+                if (DUAL) v[j] = silu_mul(v[j], acc_read(acc[2 * sl + mm][ni + 4][j]));
             }
             uint2 pk;
             pk.x = pack_bf16x2(v[0], v[1]);
             pk.y = pack_bf16x2(v[2], v[3]);
             const int c = ni * 2 + (g16 >> 1);  // 16-byte piece of the staged row
             *reinterpret_cast<uint2*>(wr + staged_swz<DUAL>(r, c) * 16 + (g16 & 1) * 8) = pk;
+            // (keeps the accumulator reads of the next pieces from being hoisted here,
+            // which would raise the register peak of the epilogue)
+            if constexpr (DUAL) __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
@@ -1035,6 +1053,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_p4_kernel(
                     } else {
                         store_rows_lds<DUAL>(acc, sl, smem, C, r0, rows_valid, n0, N, wave, wm, wn);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
                 // Short tile: every row sits in the first 32 * MI.  The four waves
