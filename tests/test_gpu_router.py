@@ -44,6 +44,8 @@ CASES = [
     # tile split along K (4 parts; 3 parts of uneven length), ragged tokens
     (8000, 4096, 256, "bf16", 1.5),
     (16385, 4096, 128, "bf16", 0.0),
+    # two token tiles, one short (so tiles are claimed), each split in 32 parts
+    (300, 4096, 128, "bf16", 0.5),
     # the same E with a shorter d, and too many token tiles for that path: the
     # register-tiled kernel
     (16385, 256, 128, "bf16", 0.0),
