@@ -10,8 +10,10 @@ input, and an element left unwritten all fail.  The configs take the kernels'
 edge paths: short last tiles (at most 32, 64 or 128 rows), ragged tails,
 empty experts, the split tail and per-XCD tile claiming (with the optional
 grouped-GEMM workspace), the gathered X rows of moe_forward and moe_forward_tr,
-the 128 x 128 kernel (d % 256 != 0) and the fp32 kernels.  These are ordinary
-runs of the kernels on valid inputs; nothing is made to fault."""
+the 128 x 128 kernel (d % 256 != 0) and the fp32 kernels, and both router
+projection paths (the register-tiled kernel and the grouped GEMM's kernel with
+every tile split along K).  These are ordinary runs of the kernels on valid
+inputs; nothing is made to fault."""
 import ctypes
 
 import numpy as np
@@ -230,3 +232,42 @@ def test_backward_canaries(cfg):
                           ("dw", (T, K), torch.float32), ("dW1", (E, d, n), torch.float32),
                           ("dW3", (E, d, n), torch.float32), ("dW2", (E, n, d), torch.float32)):
         _same(bufs[k].view(tdt, shape), r[k], k)
+
+
+ROUTER_CASES = [
+    # (T, d, E, bias variance): the grouped GEMM's kernel (E % 128 == 0, d >= 4096),
+    # with two token tiles (one short, claimed, 32 parts each) and with 16 tiles
+    (300, 4096, 128, 0.5),
+    (2000, 4096, 256, 1.5),
+    # the register-tiled kernel: E a multiple of 128 with a short d, and E padded to 64
+    (1000, 1536, 128, 2.0),
+    (700, 512, 40, 1.0),
+]
+
+
+@pytest.mark.parametrize("T,d,E,bv", ROUTER_CASES, ids=lambda v: str(v))
+def test_router_canaries(T, d, E, bv):
+    """moe_router: the logits and the workspace guarded, X, Wr and the bias
+    unchanged, the logits equal to an unguarded call's bit for bit."""
+    lib = moe.load_library()
+    dev = torch.device("cuda")
+    cfg = synth.MoEConfig("r", T=T, d=d, E=E, K=1, n=128, logits="proj_bias" if bv else "proj", bias_var=bv)
+    X = synth._normal((T, d), 1.0, torch.bfloat16, torch.device("cpu"), synth._gen("cpu", 3, "X")).to(dev)
+    Wr, b = synth.make_router(cfg, "cpu", 3)
+    g = {"X": X, "Wr": Wr.to(dev)}
+    if b is not None:
+        g["bias"] = b.to(dev)
+    copies = {k: v.clone() for k, v in g.items()}
+    wsb = lib.moe_router_workspace_bytes(d, E, 1)
+    bufs = {"logits": Guarded(T * E * 4, dev), "ws": Guarded(wsb, dev)}
+    _ok(lib.moe_router(g["X"].data_ptr(), 1, T, d, E, g["Wr"].data_ptr(),
+                       g["bias"].data_ptr() if "bias" in g else None, bufs["logits"].ptr, bufs["ws"].ptr, wsb,
+                       _stream()), lib, "moe_router")
+    torch.cuda.synchronize()
+    for k, v in bufs.items():
+        v.check(f"moe_router {k}")
+    _inputs_unchanged(g, copies)
+    ref = moe.moe_router(g["X"], g["Wr"], g.get("bias"))
+    torch.cuda.synchronize()
+    _same(bufs["logits"].view(torch.float32, (T, E)), ref, "logits")
+
