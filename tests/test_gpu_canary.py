@@ -271,3 +271,37 @@ def test_router_canaries(T, d, E, bv):
     torch.cuda.synchronize()
     _same(bufs["logits"].view(torch.float32, (T, E)), ref, "logits")
 
+
+@pytest.mark.parametrize("T,d,E,K,bv", [(1000, 512, 40, 4, 1.0), (333, 1024, 8, 2, 0.0), (600, 4096, 256, 8, 1.5)],
+                         ids=lambda v: str(v))
+def test_route_x_canaries(T, d, E, K, bv):
+    """moe_route_x (fused router-gate for E <= 64, router then gate above):
+    logits, routing outputs and workspace guarded, equal to an unguarded call."""
+    lib = moe.load_library()
+    dev = torch.device("cuda")
+    cfg = synth.MoEConfig("rx", T=T, d=d, E=E, K=K, n=128, logits="proj_bias" if bv else "proj", bias_var=bv)
+    X = synth._normal((T, d), 1.0, torch.bfloat16, torch.device("cpu"), synth._gen("cpu", 5, "X")).to(dev)
+    Wr, b = synth.make_router(cfg, "cpu", 5)
+    g = {"X": X, "Wr": Wr.to(dev)}
+    if b is not None:
+        g["bias"] = b.to(dev)
+    copies = {k: v.clone() for k, v in g.items()}
+    wsb = lib.moe_route_x_workspace_bytes(T, d, E, K, 1)
+    A = T * K
+    bufs = {"logits": Guarded(T * E * 4, dev), "idx": Guarded(A * 4, dev), "w": Guarded(A * 4, dev),
+            "counts": Guarded(E * 4, dev), "offsets": Guarded((E + 1) * 4, dev), "ws": Guarded(wsb, dev)}
+    bb = {k: v.ptr for k, v in bufs.items()}
+    _ok(lib.moe_route_x(g["X"].data_ptr(), 1, T, d, E, K, g["Wr"].data_ptr(),
+                        g["bias"].data_ptr() if "bias" in g else None, bb["logits"], bb["idx"], bb["w"],
+                        bb["counts"], bb["offsets"], bb["ws"], wsb, _stream()), lib, "moe_route_x")
+    torch.cuda.synchronize()
+    for k, v in bufs.items():
+        v.check(f"moe_route_x {k}")
+    _inputs_unchanged(g, copies)
+    idx, w, counts, offsets, lg = moe.moe_route_x(g["X"], g["Wr"], g.get("bias"), K)
+    torch.cuda.synchronize()
+    for k, want, shape, tdt in (("logits", lg, (T, E), torch.float32), ("idx", idx, (T, K), torch.int32),
+                                ("w", w, (T, K), torch.float32), ("counts", counts, (E,), torch.int32),
+                                ("offsets", offsets, (E + 1,), torch.int32)):
+        _same(bufs[k].view(tdt, shape), want, k)
+
