@@ -11,7 +11,11 @@
 // both products are accumulated: |w - (hi + lo)| <= 2^-18 |w|, and the
 // products of bf16 X with either term are exact in the fp32 accumulator.
 // A prep kernel writes hi and lo transposed ([E_pad, d], k-contiguous) into the
-// workspace, so that both MFMA operands are 16-byte loads per lane.
+// workspace, so that both MFMA operands are 16-byte pieces of k-contiguous rows.
+// E <= 64: the register-tiled kernel (router_mfma_kernel) loads its operands
+// straight from global memory, and the fused router-gate repeats its
+// arithmetic bit for bit.  E > 64: the tile kernel (router_tile_kernel) stages
+// 128 tokens and 64 experts' hi and lo rows through LDS by DMA, in whole lines.
 //
 // For E a multiple of 128 and few enough tokens (router_gemm_ok), the same
 // split runs on the grouped GEMM's SwiGLU kernel instead: hi and lo stay in
@@ -153,6 +157,126 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t* _
             for (int i = 0; i < 16; ++i) {
                 const int e = e0 + j * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
                 if (e < E) orow[e] = s[i] + (bias != nullptr ? bias[e] : 0.0f);
+            }
+        }
+    }
+}
+
+// Router tile kernel for E > 64 (bf16 X, d % 64 == 0).  Workgroup tile: 128
+// tokens x 64 experts, both terms of the split.  K goes in blocks of 64 through
+// a 4-stage LDS ring filled by DMA.  A 32 KB stage holds 128 X rows and 128
+// weight rows (the tile's 64 hi rows, then its 64 lo rows) of 128 bytes each;
+// the 16-byte pieces of row r are XOR-swizzled by r % 8, so the fragment reads
+// are free of bank conflicts.  A DMA instruction reads 8 whole 128-byte lines,
+// where loading MFMA fragments straight from global memory touches 32 lines
+// for the same 1 KB.  Wave w takes tokens 64 (w / 2) .. +63 (two groups of 32)
+// and experts 32 (w % 2) .. +31; every accumulator takes its k-steps of 16 in
+// ascending order, the hi term before the lo term.
+constexpr int kRtTok = 128, kRtExp = 64, kRtStage = 32768, kRtStages = 4;
+constexpr size_t kRtLds = (size_t)kRtStages * kRtStage;
+
+__global__ __launch_bounds__(kThreads, 1) void router_tile_kernel(const uint16_t* __restrict__ X, int T, int d,
+                                                                  const uint16_t* __restrict__ hi,
+                                                                  const uint16_t* __restrict__ lo,
+                                                                  const float* __restrict__ bias, int E, int n_eg,
+                                                                  float* __restrict__ logits) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = uniform(tid / kWave);
+    const int l32 = lane & 31, lh = lane >> 5;
+    // block b: XCD b % 8, expert group (b / 8) % n_eg, token tile from the rest
+    const int b = blockIdx.x;
+    const int eg = (b >> 3) % n_eg;
+    const int tt = (b & 7) + 8 * ((b >> 3) / n_eg);
+    const int t0 = tt * kRtTok;
+    if (t0 >= T) return;
+    const int e0 = eg * kRtExp;
+    const int nK = d / 64;
+    const uint32_t row_bytes = (uint32_t)d * 2u;
+    const uint32_t lds_base = uniform((int)(uint32_t)(uintptr_t)(lds_void*)smem);
+
+    // DMA: waves 0-1 fill the X half of a stage (pieces 0-15), wave 2 the hi
+    // rows (pieces 16-23), wave 3 the lo rows (pieces 24-31).  Piece q holds
+    // region rows 8q' .. 8q'+7 (q' = q within the wave's matrix); lane L writes
+    // row 8q' + L/8 at LDS piece L % 8, which holds the row's global piece
+    // (L % 8) ^ (L / 8).  X rows past T read as zeros (buffer range).
+    const bool xw = wave < 2;
+    const int tv = min(T - t0, kRtTok);
+    const rsrc_t rs = xw ? make_rsrc(X + (size_t)t0 * d, (uint32_t)tv * row_bytes)
+                         : make_rsrc((wave == 2 ? hi : lo) + (size_t)e0 * d, (uint32_t)kRtExp * row_bytes);
+    const int q0 = xw ? wave * 8 : 0;  // first piece of the wave within its matrix
+    uint32_t voff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        voff[i] = (uint32_t)(8 * (q0 + i) + (lane >> 3)) * row_bytes + (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
+    const uint32_t dst0 = lds_base + (uint32_t)(wave * 8) * 1024u;
+    auto issue = [&](int kb, int st) __attribute__((always_inline)) {
+        const uint32_t ko = (uint32_t)min(kb, nK - 1) * 128u;  // past the end: a harmless reload
+        const uint32_t dst = dst0 + (uint32_t)st * kRtStage;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dma16(rs, dst + i * 1024, voff[i], ko);
+    };
+
+    // Fragments: lane l supplies row l % 32 at k = 8 (l / 32) .. +7 of a 16-k
+    // step, that is piece 2s + l / 32 of the row for step s of a block.
+    const int wt = wave >> 1, we = wave & 1;
+    const int sw = l32 & 7;  // every fragment row here is l32 plus a multiple of 8
+    const int x_rd = (wt * 64 + l32) * 128;
+    const int h_rd = 16384 + (we * 32 + l32) * 128;
+    const int l_rd = 16384 + (64 + we * 32 + l32) * 128;
+
+    f32x16 acc[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[g][i] = 0.0f;
+
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    for (int kb = 0; kb < nK; ++kb) {
+        const int st = kb & (kRtStages - 1);
+        // this wave's pieces of block kb have landed (two blocks stay in flight);
+        // the barrier makes every wave's pieces visible and retires the reads of
+        // block kb - 1, whose stage the refill below overwrites
+        __asm__ volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue(kb + 3, (kb + 3) & (kRtStages - 1));
+        const char* sb = smem + st * kRtStage;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const int pc = ((2 * s4 + lh) ^ sw) << 4;
+            const bf16x8 x0 = *reinterpret_cast<const bf16x8*>(sb + x_rd + pc);
+            const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(sb + x_rd + 32 * 128 + pc);
+            const bf16x8 hf = *reinterpret_cast<const bf16x8*>(sb + h_rd + pc);
+            const bf16x8 lf = *reinterpret_cast<const bf16x8*>(sb + l_rd + pc);
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf, x0, acc[0], 0, 0, 0);
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf, x0, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf, x1, acc[1], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf, x1, acc[1], 0, 0, 0);
+        }
+    }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA outlives the workgroup
+
+    // lane l holds token l % 32 of its group and experts (i/4)*8 + (l/32)*4 + i%4
+    // of its 32-expert block in acc[g][i]
+    const bool vec = (E & 3) == 0;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int t = t0 + wt * 64 + g * 32 + l32;
+        if (t >= T) continue;
+        float* orow = logits + (size_t)t * E;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = e0 + we * 32 + q * 8 + lh * 4;
+            f32x4 v = {acc[g][4 * q], acc[g][4 * q + 1], acc[g][4 * q + 2], acc[g][4 * q + 3]};
+            if (vec && e + 3 < E) {
+                if (bias != nullptr) v += *reinterpret_cast<const f32x4*>(bias + e);
+                *reinterpret_cast<f32x4*>(orow + e) = v;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (e + j < E) orow[e + j] = v[j] + (bias != nullptr ? bias[e + j] : 0.0f);
             }
         }
     }
@@ -406,6 +530,20 @@ hipError_t launch_router(const void* X, int dtype, int T, int d, int E, const fl
     const size_t n = (size_t)e_pad * d;
     const unsigned sgrid = (unsigned)std::min<size_t>((n + kThreads - 1) / kThreads, 4096);
     hipLaunchKernelGGL(router_split_kernel, dim3(sgrid), dim3(kThreads), 0, s, Wr, d, E, e_pad, hi, lo);
+    if (E > 64) {
+        static bool lds_attr_set = false;  // the tile kernel's 128 KB of dynamic LDS
+        if (!lds_attr_set) {
+            const hipError_t aerr = hipFuncSetAttribute((const void*)router_tile_kernel,
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRtLds);
+            if (aerr != hipSuccess) return aerr;
+            lds_attr_set = true;
+        }
+        // token tiles rounded up to a multiple of 8 (one per XCD); blocks past T exit at once
+        const int tiles = (((T + kRtTok - 1) / kRtTok) + 7) / 8 * 8;
+        hipLaunchKernelGGL(router_tile_kernel, dim3((unsigned)(tiles * n_eg)), dim3(kThreads), kRtLds, s,
+                           static_cast<const uint16_t*>(X), T, d, hi, lo, bias, E, n_eg, logits);
+        return hipGetLastError();
+    }
     // token tiles rounded up to a multiple of 8 (one per XCD); blocks past T exit at once
     const int tt = 32 * router_tg(E);
     const int tiles = (((T + tt - 1) / tt) + 7) / 8 * 8;

@@ -47,9 +47,14 @@ CASES = [
     # two token tiles, one short (so tiles are claimed), each split in 32 parts
     (300, 4096, 128, "bf16", 0.5),
     # the same E with a shorter d, and too many token tiles for that path: the
-    # register-tiled kernel
+    # LDS-staged tile kernel
     (16385, 256, 128, "bf16", 0.0),
     (33000, 256, 128, "bf16", 1.0),
+    # tile kernel: a second expert group half made of zero rows; E not a
+    # multiple of 4 (element stores) with a ragged last token tile; one token
+    (1000, 512, 96, "bf16", 1.0),
+    (130, 1024, 65, "bf16", 0.5),
+    (1, 256, 200, "bf16", 0.0),
 ]
 
 
@@ -68,16 +73,18 @@ def test_router_matches_oracle(T, d, E, dt, bv):
     assert torch.equal(lg, lg2)
 
 
-@pytest.mark.parametrize("name", ["mixtral", "dsv3"])
+@pytest.mark.parametrize("name", ["mixtral", "dsv3", "fine"])
 def test_router_full_size_then_route(name):
-    """Full-size router on sampled rows, then the gate on the GPU logits matches
-    the oracle's gate on those same logits bit for bit."""
+    """Full-size router (every row on the fine-grained shape, sampled rows on the
+    other two), then the gate on the GPU logits matches the oracle's gate on
+    those same logits bit for bit."""
     cfg = synth.CONFIGS[name]
     X = synth._normal((cfg.T, cfg.d), 1.0, cfg.torch_dtype, torch.device("cuda"), synth._gen("cuda", 0, "X"))
     Wr, b = synth.make_router(cfg, "cuda", 0)
     lg = moe.moe_router(X, Wr, b)
     torch.cuda.synchronize()
-    rows = np.unique(np.r_[np.random.default_rng(1).choice(cfg.T, 48, replace=False), 0, cfg.T - 1])
+    rows = (None if name == "fine" else
+            np.unique(np.r_[np.random.default_rng(1).choice(cfg.T, 48, replace=False), 0, cfg.T - 1]))
     _check_logits(lg, to_np(X), Wr.cpu().numpy(), None if b is None else b.cpu().numpy(), rows=rows)
     idx, w, counts, offsets = moe.moe_route(lg, cfg.K)
     torch.cuda.synchronize()
