@@ -12,10 +12,12 @@
 // products of bf16 X with either term are exact in the fp32 accumulator.
 // A prep kernel writes hi and lo transposed ([E_pad, d], k-contiguous) into the
 // workspace, so that both MFMA operands are 16-byte pieces of k-contiguous rows.
-// E <= 64: the register-tiled kernel (router_mfma_kernel) loads its operands
-// straight from global memory, and the fused router-gate repeats its
-// arithmetic bit for bit.  E > 64: the tile kernel (router_tile_kernel) stages
-// 128 tokens and 64 experts' hi and lo rows through LDS by DMA, in whole lines.
+// E <= 64: router_mfma_kernel, each wave one quarter of d, the four sums added
+// in wave order; the fused router-gate repeats its arithmetic bit for bit.  For
+// E <= 32 both stage their operands through wave-private LDS by DMA in whole
+// lines (router_quarter_lds); for 32 < E <= 64 they load them straight into
+// registers.  E > 64: the tile kernel (router_tile_kernel) stages 128 tokens
+// and 64 experts' hi and lo rows through a shared LDS ring by DMA.
 //
 // For E a multiple of 128 and few enough tokens (router_gemm_ok), the same
 // split runs on the grouped GEMM's SwiGLU kernel instead: hi and lo stay in
@@ -67,6 +69,79 @@ __global__ __launch_bounds__(kThreads) void router_split_nc_kernel(const float* 
     if (blockIdx.x == 0 && (int)threadIdx.x < nz) zero[threadIdx.x] = 0;
 }
 
+// E <= 32 (one 32-expert block, 32 tokens): the K-quarter loop with its
+// operands staged through LDS by DMA, in whole 128-byte lines, instead of
+// loaded straight into registers (a fragment load touches 32 rows of 32
+// bytes).  Each wave stages its own quarter of d in a region only it uses, so
+// no barrier is needed: per 64-k block, 32 X rows and the 8 WP hi and lo rows
+// that hold experts (rows past E read as zeros; lanes past 8 WP take zero
+// fragments, as rows past E are zero), 128 bytes each, the 16-byte pieces of a
+// row XOR-swizzled by row % 8.  NS stages, NS - 1 blocks in flight.  The MFMAs
+// run in the register path's order -- k-steps of 16 ascending, the hi term
+// before the lo term -- so the sums are the same bits.
+template <int WP>
+struct RouterQ {
+    static constexpr int P = 4 + 2 * WP;                      // 1 KB pieces per stage
+    static constexpr int NS = WP == 1 ? 4 : WP == 2 ? 3 : 2;  // stages
+    static constexpr int WAVE_BYTES = NS * P * 1024;
+    static constexpr size_t LDS = 4 * (size_t)WAVE_BYTES;
+};
+
+template <int WP>
+MOE_DEV void router_quarter_lds(const uint16_t* __restrict__ X, int T, int t0, int d,
+                                const uint16_t* __restrict__ hi, const uint16_t* __restrict__ lo, int E,
+                                char* wst, uint32_t wst_lds, int wave, int lane, f32x16& acc) {
+    using C = RouterQ<WP>;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const uint32_t rb = (uint32_t)d * 2u;
+    const int ew = min(E, 8 * WP);
+    const rsrc_t xs = make_rsrc(X + (size_t)t0 * d, (uint32_t)min(T - t0, 32) * rb);
+    const rsrc_t hs = make_rsrc(hi, (uint32_t)ew * rb);
+    const rsrc_t ls = make_rsrc(lo, (uint32_t)ew * rb);
+    // lane L of a piece writes row 8p + L/8, LDS piece L % 8 = global piece (L % 8) ^ (L / 8)
+    const uint32_t lane_off = (uint32_t)(lane >> 3) * rb + (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
+    const int kq = d / 4, nb = kq / 64;
+    const uint32_t k_base = (uint32_t)(wave * kq) * 2u;
+    auto issue = [&](int b, int st) __attribute__((always_inline)) {
+        const uint32_t ko = k_base + (uint32_t)min(b, nb - 1) * 128u;  // past the end: a harmless reload
+        const uint32_t dst = wst_lds + (uint32_t)(st * C::P) * 1024u;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) dma16(xs, dst + p * 1024, lane_off + 8u * p * rb, ko);
+#pragma unroll
+        for (int p = 0; p < WP; ++p) dma16(hs, dst + (4 + p) * 1024, lane_off + 8u * p * rb, ko);
+#pragma unroll
+        for (int p = 0; p < WP; ++p) dma16(ls, dst + (4 + WP + p) * 1024, lane_off + 8u * p * rb, ko);
+    };
+    const int sw = l32 & 7;
+    const bool wrow = l32 < 8 * WP;
+    const int wr = (wrow ? l32 : 0) * 128;
+#pragma unroll
+    for (int b = 0; b < C::NS - 1; ++b) issue(b, b);
+    int st = 0;
+    for (int b = 0; b < nb; ++b) {
+        // block b has landed; the fragments of block b - 1 are all read
+        if constexpr (C::NS == 4) __asm__ volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory");
+        else if constexpr (C::NS == 3) __asm__ volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+        else __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        issue(b + C::NS - 1, st == 0 ? C::NS - 1 : st - 1);
+        const char* sb = wst + st * C::P * 1024;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const int pc = ((2 * s4 + lh) ^ sw) << 4;
+            const bf16x8 xf = *reinterpret_cast<const bf16x8*>(sb + l32 * 128 + pc);
+            bf16x8 hf = bf16x8{}, lf = bf16x8{};
+            if (wrow) {
+                hf = *reinterpret_cast<const bf16x8*>(sb + 4 * 1024 + wr + pc);
+                lf = *reinterpret_cast<const bf16x8*>(sb + (4 + WP) * 1024 + wr + pc);
+            }
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf, xf, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf, xf, acc, 0, 0, 0);
+        }
+        st = st == C::NS - 1 ? 0 : st + 1;
+    }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA outlives the loop
+}
+
 // Workgroup tile: 32*TG tokens x 32*NB experts; the four waves split d into
 // four quarters and their fp32 sums are added in wave order at the end (fixed
 // order: deterministic).  Each weight fragment a wave loads serves its TG
@@ -74,8 +149,9 @@ __global__ __launch_bounds__(kThreads) void router_split_nc_kernel(const float* 
 // b = 16 k x 32 tokens of X, both 8 consecutive k per lane; the accumulator
 // holds, in lane l, token l % 32 and experts (i/4)*8 + (l/32)*4 + i%4.
 // Workgroups of one XCD (blockIdx mod 8) take the expert groups of the same
-// token tile, so that they share its X rows in L2.
-template <int NB, int TG>
+// token tile, so that they share its X rows in L2.  WP > 0 (NB = TG = 1): the
+// operands go through LDS (router_quarter_lds) in the same MFMA order.
+template <int NB, int TG, int WP = 0>
 __global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t* __restrict__ X, int T, int d,
                                                                const uint16_t* __restrict__ hi,
                                                                const uint16_t* __restrict__ lo,
@@ -109,35 +185,43 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t* _
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[g][j][i] = 0.0f;
 
-    for (int k0 = kb; k0 < kb + kq; k0 += 16 * U) {
-        bf16x8 xf[U][TG], hf[U][NB], lf[U][NB];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = k0 + u * 16;
-#pragma unroll
-            for (int g = 0; g < TG; ++g) xf[u][g] = *reinterpret_cast<const bf16x8*>(xr[g] + k);
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                // One expert block (E <= 32): the padding rows past E are zeros, so
-                // their lanes load nothing; with E = 8 that is 3/4 of the weight reads.
-                if (NB > 1 || e0 + j * 32 + l32 < E) {
-                    hf[u][j] = *reinterpret_cast<const bf16x8*>(hi + woff + (size_t)j * 32 * d + k);
-                    lf[u][j] = *reinterpret_cast<const bf16x8*>(lo + woff + (size_t)j * 32 * d + k);
-                } else {
-                    hf[u][j] = bf16x8{};
-                    lf[u][j] = bf16x8{};
+    if constexpr (WP > 0) {
+        static_assert(NB == 1 && TG == 1, "LDS staging: one 32-expert block of 32 tokens");
+        extern __shared__ __attribute__((aligned(1024))) char rq_stage[];
+        char* wst = rq_stage + wave * RouterQ<WP>::WAVE_BYTES;
+        router_quarter_lds<WP>(X, T, t0, d, hi, lo, E, wst, (uint32_t)(uintptr_t)(lds_void*)wst, wave, lane,
+                               acc[0][0]);
+    } else {
+        for (int k0 = kb; k0 < kb + kq; k0 += 16 * U) {
+            bf16x8 xf[U][TG], hf[U][NB], lf[U][NB];
+    #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + u * 16;
+    #pragma unroll
+                for (int g = 0; g < TG; ++g) xf[u][g] = *reinterpret_cast<const bf16x8*>(xr[g] + k);
+    #pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    // One expert block (E <= 32): the padding rows past E are zeros, so
+                    // their lanes load nothing; with E = 8 that is 3/4 of the weight reads.
+                    if (NB > 1 || e0 + j * 32 + l32 < E) {
+                        hf[u][j] = *reinterpret_cast<const bf16x8*>(hi + woff + (size_t)j * 32 * d + k);
+                        lf[u][j] = *reinterpret_cast<const bf16x8*>(lo + woff + (size_t)j * 32 * d + k);
+                    } else {
+                        hf[u][j] = bf16x8{};
+                        lf[u][j] = bf16x8{};
+                    }
                 }
             }
+    #pragma unroll
+            for (int u = 0; u < U; ++u)
+    #pragma unroll
+                for (int g = 0; g < TG; ++g)
+    #pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf[u][j], xf[u][g], acc[g][j], 0, 0, 0);
+                        acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[u][j], xf[u][g], acc[g][j], 0, 0, 0);
+                    }
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int g = 0; g < TG; ++g)
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf[u][j], xf[u][g], acc[g][j], 0, 0, 0);
-                    acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[u][j], xf[u][g], acc[g][j], 0, 0, 0);
-                }
     }
 #pragma unroll
     for (int g = 0; g < TG; ++g)
@@ -293,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 1) void router_tile_kernel(const uint16_t
 // largest logit, the lower expert index among equal ones (-0.0 == +0.0), best
 // first.  Weights exp(l_k - l_0) / sum_j exp(l_j - l_0), the sum in rank
 // order.  The tile's expert counts go to blk[tile, E] (integer LDS atomics).
-template <int NB>
+template <int NB, int WP = 0>
 __global__ __launch_bounds__(kThreads) void router_gate_kernel(
     const uint16_t* __restrict__ X, int T, int d, const uint16_t* __restrict__ hi, const uint16_t* __restrict__ lo,
     const float* __restrict__ bias, int E, int K, float* __restrict__ logits, int32_t* __restrict__ topk_idx,
@@ -325,30 +409,38 @@ __global__ __launch_bounds__(kThreads) void router_gate_kernel(
     for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
-    for (int k0 = kb; k0 < kb + kq; k0 += 16 * U) {
-        bf16x8 xf[U], hf[U][NB], lf[U][NB];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = k0 + u * 16;
-            xf[u] = *reinterpret_cast<const bf16x8*>(xr + k);
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                if (NB > 1 || l32 < E) {
-                    hf[u][j] = *reinterpret_cast<const bf16x8*>(hi + woff + (size_t)j * 32 * d + k);
-                    lf[u][j] = *reinterpret_cast<const bf16x8*>(lo + woff + (size_t)j * 32 * d + k);
-                } else {
-                    hf[u][j] = bf16x8{};
-                    lf[u][j] = bf16x8{};
+    if constexpr (WP > 0) {
+        static_assert(NB == 1, "LDS staging: one 32-expert block");
+        extern __shared__ __attribute__((aligned(1024))) char rq_stage[];
+        char* wst = rq_stage + wave * RouterQ<WP>::WAVE_BYTES;
+        router_quarter_lds<WP>(X, T, t0, d, hi, lo, E, wst, (uint32_t)(uintptr_t)(lds_void*)wst, wave, lane,
+                               acc[0]);
+    } else {
+        for (int k0 = kb; k0 < kb + kq; k0 += 16 * U) {
+            bf16x8 xf[U], hf[U][NB], lf[U][NB];
+    #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + u * 16;
+                xf[u] = *reinterpret_cast<const bf16x8*>(xr + k);
+    #pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    if (NB > 1 || l32 < E) {
+                        hf[u][j] = *reinterpret_cast<const bf16x8*>(hi + woff + (size_t)j * 32 * d + k);
+                        lf[u][j] = *reinterpret_cast<const bf16x8*>(lo + woff + (size_t)j * 32 * d + k);
+                    } else {
+                        hf[u][j] = bf16x8{};
+                        lf[u][j] = bf16x8{};
+                    }
                 }
             }
+    #pragma unroll
+            for (int u = 0; u < U; ++u)
+    #pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf[u][j], xf[u], acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[u][j], xf[u], acc[j], 0, 0, 0);
+                }
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf[u][j], xf[u], acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[u][j], xf[u], acc[j], 0, 0, 0);
-            }
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) red[wave][j][lane] = acc[j];
@@ -472,6 +564,33 @@ size_t router_split_bytes(int dtype, int d, int E) {
     return std::max(transposed, router_hilo_bytes(d, E) + 256 + ffn_split_bytes(1, d, E));
 }
 
+// Weight pieces of 8 rows staged per block by the E <= 32 kernels (0: the
+// register path, for 32 < E <= 64).
+static int router_wp(int E) { return E <= 8 ? 1 : E <= 16 ? 2 : E <= 32 ? 4 : 0; }
+
+template <int WP>
+static hipError_t launch_router_q(const uint16_t* X, int T, int d, const uint16_t* hi, const uint16_t* lo,
+                                  const float* bias, int E, float* logits, dim3 grid, hipStream_t s) {
+    const hipError_t aerr = hipFuncSetAttribute((const void*)router_mfma_kernel<1, 1, WP>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)RouterQ<WP>::LDS);
+    if (aerr != hipSuccess) return aerr;
+    hipLaunchKernelGGL((router_mfma_kernel<1, 1, WP>), grid, dim3(kThreads), RouterQ<WP>::LDS, s, X, T, d, hi, lo,
+                       bias, E, 1, logits);
+    return hipGetLastError();
+}
+
+template <int WP>
+static hipError_t launch_router_gate_q(const uint16_t* X, int T, int d, const uint16_t* hi, const uint16_t* lo,
+                                       const float* bias, int E, int K, float* logits, int32_t* idx, float* w,
+                                       int32_t* blk, dim3 grid, hipStream_t s) {
+    const hipError_t aerr = hipFuncSetAttribute((const void*)router_gate_kernel<1, WP>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)RouterQ<WP>::LDS);
+    if (aerr != hipSuccess) return aerr;
+    hipLaunchKernelGGL((router_gate_kernel<1, WP>), grid, dim3(kThreads), RouterQ<WP>::LDS, s, X, T, d, hi, lo,
+                       bias, E, K, logits, idx, w, blk);
+    return hipGetLastError();
+}
+
 bool router_gate_ok(int dtype, int d, int E) { return router_mfma_ok(dtype, d) && E <= 64; }
 
 hipError_t launch_router_gate(const void* X, int T, int d, int E, int K, const float* Wr, const float* bias,
@@ -485,12 +604,16 @@ hipError_t launch_router_gate(const void* X, int T, int d, int E, int K, const f
     const unsigned sgrid = (unsigned)std::min<size_t>((n + kThreads - 1) / kThreads, 4096);
     hipLaunchKernelGGL(router_split_kernel, dim3(sgrid), dim3(kThreads), 0, s, Wr, d, E, e_pad, hi, lo);
     const dim3 grid((unsigned)((T + kRouterGateTokens - 1) / kRouterGateTokens));
-    if (nb == 1)
-        hipLaunchKernelGGL(router_gate_kernel<1>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(X), T, d,
-                           hi, lo, bias, E, K, logits, idx, w, blk);
-    else
-        hipLaunchKernelGGL(router_gate_kernel<2>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(X), T, d,
-                           hi, lo, bias, E, K, logits, idx, w, blk);
+    const uint16_t* Xb = static_cast<const uint16_t*>(X);
+    switch (router_wp(E)) {
+        case 1: return launch_router_gate_q<1>(Xb, T, d, hi, lo, bias, E, K, logits, idx, w, blk, grid, s);
+        case 2: return launch_router_gate_q<2>(Xb, T, d, hi, lo, bias, E, K, logits, idx, w, blk, grid, s);
+        case 4: return launch_router_gate_q<4>(Xb, T, d, hi, lo, bias, E, K, logits, idx, w, blk, grid, s);
+        default: break;
+    }
+    // 32 < E <= 64: two expert blocks, operands loaded straight into registers
+    hipLaunchKernelGGL(router_gate_kernel<2>, grid, dim3(kThreads), 0, s, Xb, T, d, hi, lo, bias, E, K, logits, idx,
+                       w, blk);
     return hipGetLastError();
 }
 
@@ -531,13 +654,9 @@ hipError_t launch_router(const void* X, int dtype, int T, int d, int E, const fl
     const unsigned sgrid = (unsigned)std::min<size_t>((n + kThreads - 1) / kThreads, 4096);
     hipLaunchKernelGGL(router_split_kernel, dim3(sgrid), dim3(kThreads), 0, s, Wr, d, E, e_pad, hi, lo);
     if (E > 64) {
-        static bool lds_attr_set = false;  // the tile kernel's 128 KB of dynamic LDS
-        if (!lds_attr_set) {
-            const hipError_t aerr = hipFuncSetAttribute((const void*)router_tile_kernel,
-                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRtLds);
-            if (aerr != hipSuccess) return aerr;
-            lds_attr_set = true;
-        }
+        const hipError_t aerr = hipFuncSetAttribute((const void*)router_tile_kernel,
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRtLds);
+        if (aerr != hipSuccess) return aerr;
         // token tiles rounded up to a multiple of 8 (one per XCD); blocks past T exit at once
         const int tiles = (((T + kRtTok - 1) / kRtTok) + 7) / 8 * 8;
         hipLaunchKernelGGL(router_tile_kernel, dim3((unsigned)(tiles * n_eg)), dim3(kThreads), kRtLds, s,
@@ -548,12 +667,16 @@ hipError_t launch_router(const void* X, int dtype, int T, int d, int E, const fl
     const int tt = 32 * router_tg(E);
     const int tiles = (((T + tt - 1) / tt) + 7) / 8 * 8;
     const dim3 grid((unsigned)(tiles * n_eg));
-    if (nb == 1)
-        hipLaunchKernelGGL((router_mfma_kernel<1, 1>), grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(X), T,
-                           d, hi, lo, bias, E, n_eg, logits);
-    else
-        hipLaunchKernelGGL((router_mfma_kernel<2, 4>), grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(X), T,
-                           d, hi, lo, bias, E, n_eg, logits);
+    const uint16_t* Xb = static_cast<const uint16_t*>(X);
+    switch (router_wp(E)) {
+        case 1: return launch_router_q<1>(Xb, T, d, hi, lo, bias, E, logits, grid, s);
+        case 2: return launch_router_q<2>(Xb, T, d, hi, lo, bias, E, logits, grid, s);
+        case 4: return launch_router_q<4>(Xb, T, d, hi, lo, bias, E, logits, grid, s);
+        default: break;
+    }
+    // 32 < E <= 64: two expert blocks, operands loaded straight into registers
+    hipLaunchKernelGGL((router_mfma_kernel<2, 4>), grid, dim3(kThreads), 0, s, Xb, T, d, hi, lo, bias, E, n_eg,
+                       logits);
     return hipGetLastError();
 }
 
