@@ -57,6 +57,9 @@ CASES = [
     (100, 1536, 128, 4, "bf16", 2.0),
     (33, 384, 8, 2, "bf16", 0.0),
     (256, 128, 8, 2, "f32", 0.0),
+    # staged E <= 32 with E not a multiple of 8
+    (130, 512, 12, 3, "bf16", 0.5),
+    (500, 768, 27, 5, "bf16", 1.0),
 ]
 
 

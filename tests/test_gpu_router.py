@@ -55,6 +55,13 @@ CASES = [
     (1000, 512, 96, "bf16", 1.0),
     (130, 1024, 65, "bf16", 0.5),
     (1, 256, 200, "bf16", 0.0),
+    # E <= 32, staged through LDS in pieces of 8 weight rows: E not a multiple
+    # of 8 (rows past E read as zeros), each piece count, ragged token tiles
+    (77, 512, 12, "bf16", 0.5),
+    (300, 1024, 20, "bf16", 1.0),
+    (1025, 256, 27, "bf16", 0.0),
+    (64, 4096, 32, "bf16", 0.0),
+    (33, 768, 5, "bf16", 2.0),
 ]
 
 
