@@ -239,9 +239,13 @@ ROUTER_CASES = [
     # with two token tiles (one short, claimed, 32 parts each) and with 16 tiles
     (300, 4096, 128, 0.5),
     (2000, 4096, 256, 1.5),
-    # the register-tiled kernel: E a multiple of 128 with a short d, and E padded to 64
+    # the LDS-staged tile kernel (E > 64 with a short d; a half-empty expert
+    # group), the register-tiled kernel (E padded to 64), and the staged E <= 32
+    # kernel (a ragged last token tile)
     (1000, 1536, 128, 2.0),
+    (130, 512, 96, 0.5),
     (700, 512, 40, 1.0),
+    (77, 768, 20, 0.0),
 ]
 
 
@@ -272,7 +276,8 @@ def test_router_canaries(T, d, E, bv):
     _same(bufs["logits"].view(torch.float32, (T, E)), ref, "logits")
 
 
-@pytest.mark.parametrize("T,d,E,K,bv", [(1000, 512, 40, 4, 1.0), (333, 1024, 8, 2, 0.0), (600, 4096, 256, 8, 1.5)],
+@pytest.mark.parametrize("T,d,E,K,bv", [(1000, 512, 40, 4, 1.0), (333, 1024, 8, 2, 0.0), (600, 4096, 256, 8, 1.5),
+                                          (77, 768, 20, 3, 0.5)],
                          ids=lambda v: str(v))
 def test_route_x_canaries(T, d, E, K, bv):
     """moe_route_x (fused router-gate for E <= 64, router then gate above):
